@@ -1,0 +1,40 @@
+"""CPU oracle for int4-KV attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The product path (the HIP library and its Python
+binding) never imports, links or runs anything from here, and this package
+imports nothing from the product path.  The two share only the seeded input
+generator (``qkv_inputs``), which holds none of the method's arithmetic.
+
+What the oracle computes is the plain definition of the method's result,
+written out (the fused, tiled, online-softmax kernels reach the same value in
+exact arithmetic):
+
+* ``quantize``: per-row int4 quantization with one fp16 scale per (token, KV
+  head), in fp32 as the quantizer is specified (scale = fp16(absmax / 7) with
+  IEEE fp32 division then round-to-nearest-even to fp16; code =
+  clamp(rint(x / float(scale)), -8, 7); a zero scale gives all-zero codes),
+  two's-complement nibbles packed low-nibble-first;
+* ``attention``: dequantize K/V exactly to fp64, then plain fp64
+  softmax(Q K^T * scale) V with an optional bottom-right causal mask, plus the
+  natural-log log-sum-exp of each row;
+* ``attention_partial`` / ``lse_merge``: the same attention restricted to a
+  key range, and the log-sum-exp merge of such partial results (the
+  definition the split-K decode reaches).
+
+Every function is pinned by tests in ``tests/test_oracle_*.py`` against hand
+derived examples, exact rational arithmetic, brute force on tiny inputs,
+closed forms and invariants.
+"""
+from .quantize import quantize_rows, dequantize_rows, quantize_append, dequantize_cache
+from .attention import attention, attention_partial, lse_merge
+
+__all__ = [
+    "quantize_rows",
+    "dequantize_rows",
+    "quantize_append",
+    "dequantize_cache",
+    "attention",
+    "attention_partial",
+    "lse_merge",
+]
