@@ -38,22 +38,25 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def _attend(qd, kd, vd, scale, causal, offset, chunk):
-    """Plain attention for one (batch, head): qd [Sq, D], kd/vd [L, D] fp64.
+def _attend(qd, kd, vd, scale, causal, offset, chunk, row_ids=None):
+    """Plain attention for one (batch, head): qd [n, D], kd/vd [L, D] fp64.
 
-    ``offset`` = kv_len - Sq (bottom-right causal alignment).  Returns
-    (O [Sq, D], LSE [Sq]) with LSE the natural-log log-sum-exp of the
+    ``row_ids`` are the query row indices of the rows of ``qd`` (default
+    0..n-1); ``offset`` = kv_len - Sq (bottom-right causal alignment).
+    Returns (O [n, D], LSE [n]) with LSE the natural-log log-sum-exp of the
     scaled scores over visible keys.
     """
     Sq = qd.shape[0]
     L = kd.shape[0]
+    if row_ids is None:
+        row_ids = np.arange(Sq)
     out = np.empty((Sq, qd.shape[1]), dtype=np.float64)
     lse = np.empty(Sq, dtype=np.float64)
     for r0 in range(0, Sq, chunk):
         r1 = min(Sq, r0 + chunk)
         s = (qd[r0:r1] @ kd.T) * scale
         if causal:
-            rows = np.arange(r0, r1)[:, None]
+            rows = np.asarray(row_ids[r0:r1])[:, None]
             cols = np.arange(L)[None, :]
             s = np.where(cols <= rows + offset, s, -np.inf)
         m = np.max(s, axis=1, keepdims=True)
@@ -65,13 +68,15 @@ def _attend(qd, kd, vd, scale, causal, offset, chunk):
 
 
 def attention(q_bits, k_codes, k_scales, v_codes, v_scales, kv_len, softmax_scale,
-              causal=False, heads=None, chunk=512):
+              causal=False, heads=None, rows=None, chunk=512):
     """Attention of bf16 queries over the first ``kv_len`` rows of an int4 cache.
 
     q_bits   uint16 bf16 bits ``[B, Hq, Sq, D]``
     k_codes  uint8 ``[B, Hkv, C, D/2]``, k_scales uint16 fp16 bits ``[B, Hkv, C]``
     v_codes, v_scales: same for V
     heads    optional iterable of (b, h) pairs to compute (others are NaN)
+    rows     optional sorted query row indices to compute (others are NaN);
+             each row is computed exactly as in the full result
 
     Returns ``(out, lse)``: fp64 ``[B, Hq, Sq, D]`` and ``[B, Hq, Sq]``.
     """
@@ -96,8 +101,14 @@ def attention(q_bits, k_codes, k_scales, v_codes, v_scales, kv_len, softmax_scal
             vd = dequantize_cache(v_codes[b:b + 1, g:g + 1], v_scales[b:b + 1, g:g + 1], kv_len)[0, 0]
             cache = {(b, g): (kd, vd)}     # keep one KV head resident at a time
         kd, vd = cache[(b, g)]
-        qd = bf16_bits_to_f64(q_bits[b, h])
-        out[b, h], lse[b, h] = _attend(qd, kd, vd, scale, causal, kv_len - Sq, chunk)
+        if rows is None:
+            qd = bf16_bits_to_f64(q_bits[b, h])
+            out[b, h], lse[b, h] = _attend(qd, kd, vd, scale, causal, kv_len - Sq, chunk)
+        else:
+            idx = np.asarray(rows, dtype=np.int64)
+            qd = bf16_bits_to_f64(q_bits[b, h, idx])
+            out[b, h, idx], lse[b, h, idx] = _attend(qd, kd, vd, scale, causal, kv_len - Sq, chunk,
+                                                     row_ids=idx)
     return out, lse
 
 

@@ -256,3 +256,14 @@ def test_kv_len_prefix_only():
     vc2[:, :, 10:] ^= 0xA5
     o2, _ = attention(q, kc2, ks, vc2, vs, 10, 0.3)
     assert np.array_equal(o1, o2)
+
+
+def test_row_subset_matches_full_rows():
+    q, kc, ks, vc, vs = _rand_case(17, 1, 4, 2, 40, 50, 8)
+    rows = [0, 1, 17, 39]
+    for causal in (False, True):
+        o1, l1 = attention(q, kc, ks, vc, vs, 50, 0.3, causal)
+        o2, l2 = attention(q, kc, ks, vc, vs, 50, 0.3, causal, rows=rows)
+        assert np.array_equal(o1[:, :, rows], o2[:, :, rows])
+        assert np.array_equal(l1[:, :, rows], l2[:, :, rows])
+        assert np.all(np.isnan(np.delete(o2, rows, axis=2)))
