@@ -1,0 +1,315 @@
+"""Benchmark of the int4-KV attention hot path on one MI355X.
+
+One step = one decode step of the Llama-3-8B shaped GQA decode workload
+(B=16, 32 query / 8 KV heads, D=128, 8192 cached tokens): quantize-and-append
+the new token's K and V rows, then split-K decode attention of the query over
+the whole cache (quantizer, exact int4 -> fp16 conversion, MFMA QK^T and PV,
+online softmax, LSE merge).  Inputs are resident in HBM before timing starts;
+the cache is rotated over several independent copies so that the 256 MB
+Infinity Cache cannot serve repeated reads.
+
+Printed (stdout, one JSON line): the headline decode throughput in GB/s of
+packed KV bytes (codes + scales) per step, the roofline of the decode kernel
+(achieved HBM GB/s of its algorithmic bytes over its average launch time,
+measured with HIP events on the launch stream), the CPU oracle timed on a
+bounded sample of the same workload, and secondary figures (128K-token
+decode, 16K causal prefill TFLOP/s, ViT-B prefill, bulk quantize-append).
+Everything else goes to stderr.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "int4-KV decode GB/s (% of HBM peak); prefill attention TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+MALL_BYTES = 256 * 2 ** 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter-derived traffic is valid only for these."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_flashattention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    missing or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    e = t.get("kernels", {}).get(kernel_key)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def upload_cache(torch, qkv, k, v, n_copies):
+    """Quantize fp32 K/V on the GPU into a cache, then clone it n_copies-1 times."""
+    B, H, L, D = k.shape
+    c0 = qkv.KVCache.empty(B, H, L, D)
+    kt = torch.from_numpy(k).cuda()
+    qkv.quantize_append(kt, c0.k_codes, c0.k_scales, 0)
+    del kt
+    vt = torch.from_numpy(v).cuda()
+    qkv.quantize_append(vt, c0.v_codes, c0.v_scales, 0)
+    del vt
+    caches = [c0] + [qkv.KVCache(*(t.clone() for t in c0.tensors())) for _ in range(n_copies - 1)]
+    torch.cuda.synchronize()
+    return caches
+
+
+def per_launch_ms(torch, fn, n, rotate):
+    """Average duration of fn(i) measured with events recorded around each launch."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record()
+        fn(i % rotate)
+        ends[i].record()
+    torch.cuda.synchronize()
+    t = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(t) / len(t), t[len(t) // 2]
+
+
+def decode_bytes(w):
+    codes = 2 * w.B * w.Hkv * w.L * (w.D // 2)
+    scales = 2 * w.B * w.Hkv * w.L * 2
+    q = w.B * w.Hq * w.Sq * w.D * 2
+    o = w.B * w.Hq * w.Sq * w.D * 4
+    return codes + scales, codes + scales + q + o
+
+
+def prefill_flops(w):
+    pairs = w.Sq * (w.Sq + 1) // 2 if (w.causal and w.Sq == w.L) else (
+        sum(min(w.L, i + w.L - w.Sq + 1) for i in range(w.Sq)) if w.causal else w.Sq * w.L)
+    return 4.0 * w.D * pairs * w.B * w.Hq
+
+
+def bench_decode(torch, qkv, w, steps, warmup, with_append):
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w)
+    kv_bytes, attn_bytes = decode_bytes(w)
+    n_copies = max(4, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    caches = upload_cache(torch, qkv, k, v, n_copies)
+    k_new = torch.from_numpy(k[:, :, -1:].copy()).cuda()
+    v_new = torch.from_numpy(v[:, :, -1:].copy()).cuda()
+    del k, v
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    ns = qkv.decode_auto_splits(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D)
+    ws_bytes = qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def decode_only(i):
+        qkv.decode(q, caches[i], w.L, softmax_scale=w.softmax_scale, out=out, workspace=ws)
+
+    def step(i):
+        c = caches[i]
+        if with_append:
+            qkv.quantize_append(k_new, c.k_codes, c.k_scales, w.L - 1)
+            qkv.quantize_append(v_new, c.v_codes, c.v_scales, w.L - 1)
+        decode_only(i)
+
+    for i in range(warmup):
+        step(i % n_copies)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i % n_copies)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    avg_ms, med_ms = per_launch_ms(torch, decode_only, max(steps, 20), n_copies)
+    res = {
+        "workload": w.name, "n_split": ns, "cache_copies": n_copies,
+        "ms_per_step": ms_step,
+        "packed_kv_bytes": kv_bytes, "algorithmic_bytes": attn_bytes,
+        "step_GBps_packed_kv": kv_bytes / (ms_step * 1e-3) / 1e9,
+        "decode_avg_ms": avg_ms, "decode_median_ms": med_ms,
+        "decode_GBps": attn_bytes / (avg_ms * 1e-3) / 1e9,
+    }
+    res["decode_frac_hbm"] = res["decode_GBps"] / HBM_PEAK_GBS
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(torch, qkv, w, iters):
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w)
+    cache = upload_cache(torch, qkv, k, v, 1)[0]
+    del k, v
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+
+    def run(_):
+        qkv.prefill(q, cache, w.L, w.causal, softmax_scale=w.softmax_scale, out=out)
+
+    for i in range(2):
+        run(i)
+    avg_ms, med_ms = per_launch_ms(torch, run, iters, 1)
+    fl = prefill_flops(w)
+    res = {"workload": w.name, "avg_ms": avg_ms, "median_ms": med_ms, "flops": fl,
+           "TFLOPs": fl / (avg_ms * 1e-3) / 1e12}
+    res["frac_mfma"] = res["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+    del cache, q, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_quantize(torch, qkv, w, iters):
+    from qkv_inputs import make_qkv
+    _, k, _ = make_qkv(w)
+    B, H, L, D = k.shape
+    kt = torch.from_numpy(k).cuda()
+    del k
+    codes = torch.empty((B, H, L, D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, H, L), dtype=torch.float16, device="cuda")
+
+    def run(_):
+        qkv.quantize_append(kt, codes, scales, 0)
+
+    run(0)
+    avg_ms, med_ms = per_launch_ms(torch, run, iters, 1)
+    rows = B * H * L
+    nbytes = rows * (4 * D + D // 2 + 2)
+    del kt, codes, scales
+    torch.cuda.empty_cache()
+    return {"workload": w.name + ":K", "rows": rows, "avg_ms": avg_ms, "bytes": nbytes,
+            "GBps": nbytes / (avg_ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU oracle on a bounded sample of the decode workload (whole KV groups)."""
+    import numpy as np
+    import oracle
+    from qkv_inputs import make_qkv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q_bits, k, v = make_qkv(w)
+    groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    done, t_total, nbytes = 0, 0.0, 0
+    G = w.G
+    for (b, g) in groups:
+        ks = k[b:b + 1, g:g + 1]
+        vs = v[b:b + 1, g:g + 1]
+        t0 = time.perf_counter()
+        kc, ksc = oracle.quantize_rows(ks)
+        vc, vsc = oracle.quantize_rows(vs)
+        oracle.attention(q_bits[b:b + 1, g * G:(g + 1) * G], kc, ksc, vc, vsc, w.L, w.softmax_scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        nbytes += 2 * w.L * (w.D // 2 + 2)
+        if t_total >= budget_s:
+            break
+    return {
+        "value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"{done} of {len(groups)} (batch, KV head) groups of {w.name} "
+                   f"(quantize K/V rows + fp64 attention of {G} heads x {w.L} tokens each), "
+                   f"{t_total:.1f} s; GB/s counts packed KV bytes as on the GPU"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["all", "headline", "decode", "prefill"], default="all")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_kv_flashattention_amd as qkv
+    from qkv_inputs import workload
+    torch.cuda.set_device(0)
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device: {dev.name} CUs={dev.multi_processor_count}")
+
+    w3 = workload("llama3_8b_decode")
+    head = bench_decode(torch, qkv, w3, args.steps, args.warmup, with_append=True)
+    log("headline:", json.dumps(head))
+    secondary = {}
+    if args.only in ("all", "decode"):
+        secondary["long_context_decode"] = bench_decode(torch, qkv, workload("long_context_decode"),
+                                                        max(args.steps // 2, 10), 5, with_append=True)
+        log("long:", json.dumps(secondary["long_context_decode"]))
+    if args.only in ("all", "prefill"):
+        secondary["causal_prefill_16k"] = bench_prefill(torch, qkv, workload("causal_prefill_16k"), 10)
+        log("prefill:", json.dumps(secondary["causal_prefill_16k"]))
+        secondary["vit_b_selfattn"] = bench_prefill(torch, qkv, workload("vit_b_selfattn"), 20)
+        log("vit:", json.dumps(secondary["vit_b_selfattn"]))
+    if args.only == "all":
+        secondary["quantize_append"] = bench_quantize(torch, qkv, w3, 20)
+        log("quantize:", json.dumps(secondary["quantize_append"]))
+
+    cpu = cpu_baseline(w3, args.cpu_budget)
+    log("cpu:", json.dumps(cpu))
+
+    value = head["step_GBps_packed_kv"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w3.name, "B": w3.B, "Hq": w3.Hq, "Hkv": w3.Hkv, "D": w3.D,
+                   "Sq": w3.Sq, "kv_len": w3.L, "kv_format": "int4 + fp16 scale per (token, KV head)",
+                   "step": "append 1 token (K,V) + split-K decode", "n_split": head["n_split"],
+                   "cache_copies_rotated": head["cache_copies"]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["decode_GBps"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["decode_frac_hbm"], 4),
+            "traffic": measured_traffic("decode_llama3_8b"),
+        },
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

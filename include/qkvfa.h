@@ -1,0 +1,150 @@
+/*
+ * qkvfa.h -- int4-KV FlashAttention for AMD MI355X (gfx950): the C ABI.
+ *
+ * The library computes attention directly over an int4-quantized KV cache
+ * and dequantizes inside its kernels, so no dequantized K/V ever reaches HBM
+ * ("Quantized Cross-Attention: Extending FlashAttention-3 with In-SRAM
+ * Dequantization", §3.1 and §3.2; the Open-TQ-Metal abstract on the
+ * "Attention Quantization" listing: int4 KV quantized on the fly and attended
+ * in compressed form).  Three operations follow the prefill / append / decode
+ * statement of TurboAttention (arXiv 2412.08585) §2.1: quantize-and-append,
+ * decode attention of a few query rows, prefill attention (causal or not).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * All tensors are dense, row-major, in device memory owned by the caller.
+ * The library never allocates or frees memory and keeps no pointer after a
+ * call returns.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream) and runs asynchronously: the caller keeps every buffer
+ * alive until the stream has finished it.
+ *
+ *   B    batch                     Hq   query heads     Hkv  KV heads
+ *   G    Hq / Hkv (GQA group)      D    head dim (64 or 128)
+ *   Sq   query rows per head       C    cache capacity in tokens
+ *   kv_len  number of valid cache rows the query attends
+ *
+ *   KV cache   codes  uint8  [B, Hkv, C, D/2]   packed int4, two's complement,
+ *                                               element 2i in bits 0-3 of byte i,
+ *                                               element 2i+1 in bits 4-7
+ *              scales uint16 [B, Hkv, C]        fp16 bit patterns, one per
+ *                                               (token, KV head)
+ *   value of element d of row t:  fp16(scales[t]) * code[t][d]
+ *   Q          uint16 [B, Hq, Sq, D]            bfloat16 bit patterns
+ *   out        float  [B, Hq, Sq, D]
+ *   lse        float  [B, Hq, Sq]               natural-log log-sum-exp of the
+ *                                               scaled scores, or NULL
+ *   query head h reads KV head h / G.
+ *
+ * Errors: every argument is checked before anything is enqueued; a failing
+ * call enqueues nothing, returns a nonzero qkv_status and leaves a message
+ * for qkv_last_error() (thread-local).  A HIP launch error returns
+ * QKV_ERR_HIP.  No C++ exception crosses this interface.
+ * Preconditions that are not checked (their violation gives unspecified
+ * output, never an out-of-bounds access): finite inputs; row absmax of
+ * quantized data <= 7 * 65504; |q| < 65504 for every query element.
+ */
+#ifndef QKVFA_H
+#define QKVFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QKV_OK = 0,
+  QKV_ERR_INVALID_ARG = 1, /* a size, pointer or range is invalid          */
+  QKV_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement */
+  QKV_ERR_WORKSPACE = 3,   /* workspace missing or too small               */
+  QKV_ERR_HIP = 4          /* the HIP runtime reported an error            */
+} qkv_status;
+
+/* Static text naming a status. */
+const char* qkv_status_string(qkv_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* qkv_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int qkv_version(void);
+
+/*
+ * (a) Quantize-and-append.  Quantizes T new rows of one tensor (call once for
+ * K and once for V) into cache rows [pos, pos + T); rows outside that range
+ * are not touched.  Per row of D fp32 values x:
+ *     scale = fp16_rne( max|x| / 7 )        (IEEE fp32 division)
+ *     code  = clamp( rint( x / float(scale) ), -8, 7 )   (IEEE fp32 division,
+ *             round half to even); scale == 0 gives all-zero codes.
+ * Follows: the per-(token, head) scale layout of the kernel signature in
+ * "Quantized Cross-Attention ..." §4.1 (GROUP_SIZE = D); int4 on the fly
+ * (Open-TQ-Metal abstract); append k_t, v_t to the cache (TurboAttention
+ * §2.1).
+ *   src     float [B, Hkv, T, D], device, 16-byte aligned
+ *   codes   uint8 [B, Hkv, C, D/2], device, 16-byte aligned (written)
+ *   scales  uint16 [B, Hkv, C], device, 2-byte aligned (written)
+ * Requires B, Hkv >= 1, T >= 0 (T == 0 enqueues nothing), D in {64, 128},
+ * 0 <= pos, pos + T <= C.
+ */
+qkv_status qkv_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,
+                               int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                               int64_t C, int64_t pos, void* stream);
+
+/*
+ * (b) Decode attention: each of the Sq query rows of every (batch, head)
+ * attends cache rows [0, kv_len) with no mask (append-then-attend,
+ * TurboAttention §2.1).  The KV length is split into `num_splits` ranges
+ * processed in parallel; each range yields a partial output normalized over
+ * its own keys plus its log-sum-exp, and the partials are merged with the
+ * log-sum-exp rule (the final normalization with running max and sum of
+ * FlashAttention, TurboAttention §2.2).  The K/V tile of a KV head is read
+ * once for all G query heads of its group.
+ *   q        uint16 [B, Hq, Sq, D] bf16 bits, device, 16-byte aligned
+ *   k_codes, v_codes   uint8 [B, Hkv, C, D/2], device, 16-byte aligned
+ *   k_scales, v_scales uint16 [B, Hkv, C], device, 2-byte aligned
+ *   softmax_scale      multiplies Q.K before the softmax
+ *   num_splits         0 = chosen by the library; else 1..1024 (clamped to
+ *                      the number of 32-token chunks of kv_len)
+ *   out      float [B, Hq, Sq, D], device, 16-byte aligned (written)
+ *   lse      float [B, Hq, Sq] or NULL (written)
+ *   workspace, workspace_bytes: device scratch of at least
+ *            qkv_decode_workspace_bytes(...) bytes (may be NULL when that
+ *            is 0); its contents on entry do not matter.
+ * Requires D in {64, 128}, Hq % Hkv == 0, 1 <= kv_len <= C,
+ * 1 <= G * Sq <= 64 (more rows belong to qkv_prefill).
+ */
+size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                                  int64_t kv_len, int64_t D, int num_splits);
+/* The split count the library would use for num_splits = 0 (device 0's CU
+ * count is queried once and cached per device). */
+int qkv_decode_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                           int64_t kv_len, int64_t D);
+qkv_status qkv_decode(const uint16_t* q,
+                      const uint8_t* k_codes, const uint16_t* k_scales,
+                      const uint8_t* v_codes, const uint16_t* v_scales,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                      int64_t C, int64_t D, float softmax_scale, int num_splits,
+                      float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * (c) Prefill attention, tiled with online softmax (FlashAttention tiling,
+ * TurboAttention §2.2).  causal = 0: every row sees [0, kv_len).
+ * causal = 1: query row i (0 <= i < Sq) is token kv_len - Sq + i and sees
+ * keys j <= i + kv_len - Sq (bottom-right aligned); key tiles entirely above
+ * the diagonal are never loaded.
+ *   arguments as for qkv_decode (no workspace).
+ * Requires D in {64, 128}, Hq % Hkv == 0, 1 <= kv_len <= C, Sq >= 1,
+ * causal in {0, 1}, causal ==> Sq <= kv_len.
+ */
+qkv_status qkv_prefill(const uint16_t* q,
+                       const uint8_t* k_codes, const uint16_t* k_scales,
+                       const uint8_t* v_codes, const uint16_t* v_scales,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                       int64_t C, int64_t D, float softmax_scale, int causal,
+                       float* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKVFA_H */

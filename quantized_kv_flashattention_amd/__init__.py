@@ -1,0 +1,215 @@
+"""int4-KV FlashAttention for AMD MI355X (gfx950): Python binding of libqkvfa.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libqkvfa.so`` (built in-tree by ``build.py``); PyTorch provides
+device memory and the current stream.  There is no CPU or eager fallback:
+importing this package fails if the library is missing.
+
+Tensors (all on one CUDA/HIP device, contiguous):
+
+* cache: ``k_codes``/``v_codes`` uint8 ``[B, Hkv, C, D/2]`` and
+  ``k_scales``/``v_scales`` float16 ``[B, Hkv, C]`` (one scale per token and
+  KV head); :class:`KVCache` allocates them,
+* ``q`` bfloat16 ``[B, Hq, Sq, D]``, outputs float32 ``[B, Hq, Sq, D]`` and,
+  on request, the natural-log LSE float32 ``[B, Hq, Sq]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import torch
+
+__all__ = [
+    "QKVError",
+    "KVCache",
+    "quantize_append",
+    "decode",
+    "prefill",
+    "decode_workspace_bytes",
+    "decode_auto_splits",
+    "version",
+    "library_path",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libqkvfa.so")
+
+
+class QKVError(RuntimeError):
+    """A libqkvfa call returned a nonzero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m quantized_kv_flashattention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    lib.qkv_status_string.restype = ctypes.c_char_p
+    lib.qkv_status_string.argtypes = [ci]
+    lib.qkv_last_error.restype = ctypes.c_char_p
+    lib.qkv_last_error.argtypes = []
+    lib.qkv_version.restype = ci
+    lib.qkv_version.argtypes = []
+    lib.qkv_quantize_append.restype = ci
+    lib.qkv_quantize_append.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    lib.qkv_decode_workspace_bytes.restype = sz
+    lib.qkv_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+    lib.qkv_decode_auto_splits.restype = ci
+    lib.qkv_decode_auto_splits.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.qkv_decode.restype = ci
+    lib.qkv_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
+                               vp, vp, vp, sz, vp]
+    lib.qkv_prefill.restype = ci
+    lib.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
+                                vp, vp, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def version() -> int:
+    return int(_lib.qkv_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise QKVError(status, _lib.qkv_last_error().decode(errors="replace"))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _req(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+@dataclasses.dataclass
+class KVCache:
+    """Caller-owned int4 KV cache of one layer."""
+
+    k_codes: torch.Tensor   # uint8 [B, Hkv, C, D/2]
+    k_scales: torch.Tensor  # float16 [B, Hkv, C]
+    v_codes: torch.Tensor
+    v_scales: torch.Tensor
+
+    @staticmethod
+    def empty(B: int, Hkv: int, C: int, D: int, device="cuda") -> "KVCache":
+        mk = lambda: torch.empty((B, Hkv, C, D // 2), dtype=torch.uint8, device=device)
+        ms = lambda: torch.empty((B, Hkv, C), dtype=torch.float16, device=device)
+        return KVCache(mk(), ms(), mk(), ms())
+
+    @property
+    def shape(self):
+        B, Hkv, C, half = self.k_codes.shape
+        return B, Hkv, C, 2 * half
+
+    def tensors(self):
+        return self.k_codes, self.k_scales, self.v_codes, self.v_scales
+
+
+def quantize_append(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, pos: int):
+    """Quantize fp32 rows ``src [B, Hkv, T, D]`` into cache rows ``[pos, pos+T)``."""
+    _req(src, "src", torch.float32, 4)
+    _req(codes, "codes", torch.uint8, 4)
+    _req(scales, "scales", torch.float16, 3)
+    B, Hkv, T, D = src.shape
+    if codes.shape[:2] != (B, Hkv) or codes.shape[3] * 2 != D or scales.shape != codes.shape[:3]:
+        raise ValueError("cache shape does not match src")
+    if src.device != codes.device or src.device != scales.device:
+        raise ValueError("all tensors must be on one device")
+    C = codes.shape[2]
+    _check(_lib.qkv_quantize_append(_ptr(src), _ptr(codes), _ptr(scales), B, Hkv, T, D, C, int(pos),
+                                    _stream(src)))
+
+
+def _attn_args(q, cache_tensors, kv_len):
+    _req(q, "q", torch.bfloat16, 4)
+    kc, ks, vc, vs = cache_tensors
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, C, half = kc.shape
+    if Bk != B or half * 2 != D or vc.shape != kc.shape or ks.shape != (B, Hkv, C) or vs.shape != ks.shape:
+        raise ValueError("cache shape does not match q")
+    return B, Hq, Hkv, Sq, int(kv_len), C, D
+
+
+def _scale(softmax_scale, D):
+    return float(1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+
+
+def decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits=0) -> int:
+    return int(_lib.qkv_decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits))
+
+
+def decode_auto_splits(B, Hq, Hkv, Sq, kv_len, D) -> int:
+    return int(_lib.qkv_decode_auto_splits(B, Hq, Hkv, Sq, kv_len, D))
+
+
+def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False, out=None,
+           lse=None, workspace=None):
+    """Decode attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)`` (no mask)."""
+    tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    else:
+        _req(out, "out", torch.float32, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kc, ks, vc, vs = tensors
+    _check(_lib.qkv_decode(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                           C, D, _scale(softmax_scale, D), int(num_splits), _ptr(out), _ptr(lse),
+                           _ptr(workspace), ws_bytes, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def prefill(q, cache, kv_len, causal, softmax_scale=None, return_lse=False, out=None, lse=None):
+    """Prefill attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)``."""
+    tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    else:
+        _req(out, "out", torch.float32, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    kc, ks, vc, vs = tensors
+    _check(_lib.qkv_prefill(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                            C, D, _scale(softmax_scale, D), int(bool(causal)), _ptr(out), _ptr(lse),
+                            _stream(q)))
+    return (out, lse) if return_lse else out

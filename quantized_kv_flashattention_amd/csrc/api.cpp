@@ -1,0 +1,166 @@
+// C ABI of libqkvfa: argument validation, split planning and kernel launch.
+// Every check happens before anything is enqueued; no exception leaves here.
+#include "../../include/qkvfa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "qkvfa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qkv_status fail(qkv_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Compute units of the current device, queried once per device.
+int current_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+qkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QKV_OK;
+  return fail(QKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Checks shared by decode and prefill.
+qkv_status check_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
+                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
+                           const float* out, const float* lse, const char* fn) {
+  const std::string f(fn);
+  if (!q || !kc || !ks || !vc || !vs || !out)
+    return fail(QKV_ERR_INVALID_ARG, f + ": null tensor pointer");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1)
+    return fail(QKV_ERR_INVALID_ARG, f + ": B, Hq, Hkv and Sq must be >= 1");
+  if (D != 64 && D != 128) return fail(QKV_ERR_UNSUPPORTED, f + ": head dim must be 64 or 128");
+  if (Hq % Hkv != 0) return fail(QKV_ERR_INVALID_ARG, f + ": Hq must be a multiple of Hkv");
+  if (kv_len < 1 || kv_len > C) return fail(QKV_ERR_INVALID_ARG, f + ": need 1 <= kv_len <= C");
+  if (C > 0x7FFFFFFFll || Sq > 0x7FFFFFFFll || Hq > 0xFFFF || Hkv > 0xFFFF || B > 0xFFFF)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": size beyond the supported range");
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16))
+    return fail(QKV_ERR_INVALID_ARG, f + ": q, codes and out must be 16-byte aligned");
+  if (!aligned(ks, 2) || !aligned(vs, 2) || (lse && !aligned(lse, 4)))
+    return fail(QKV_ERR_INVALID_ARG, f + ": misaligned scales or lse");
+  return QKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qkv_status_string(qkv_status s) {
+  switch (s) {
+    case QKV_OK: return "ok";
+    case QKV_ERR_INVALID_ARG: return "invalid argument";
+    case QKV_ERR_UNSUPPORTED: return "unsupported";
+    case QKV_ERR_WORKSPACE: return "workspace too small";
+    case QKV_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* qkv_last_error(void) { return g_last_error.c_str(); }
+
+int qkv_version(void) { return 100; }
+
+qkv_status qkv_quantize_append(const float* src, uint8_t* codes, uint16_t* scales, int64_t B,
+                               int64_t Hkv, int64_t T, int64_t D, int64_t C, int64_t pos,
+                               void* stream) {
+  if (B < 1 || Hkv < 1 || T < 0 || C < 1)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append: need B, Hkv, C >= 1 and T >= 0");
+  if (D != 64 && D != 128)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append: head dim must be 64 or 128");
+  if (pos < 0 || pos + T > C)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append: need 0 <= pos and pos + T <= C");
+  if (T == 0) return QKV_OK;
+  if (!src || !codes || !scales)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append: null tensor pointer");
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append: misaligned pointer");
+  if (B * Hkv > 0x7FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append: B * Hkv too large");
+  return hip_status(qkvfa::launch_quantize_append(src, codes, scales, B * Hkv, T, (int)D, C, pos,
+                                                  static_cast<hipStream_t>(stream)),
+                    "qkv_quantize_append");
+}
+
+int qkv_decode_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                           int64_t D) {
+  (void)Hq; (void)Sq; (void)D;
+  if (B < 1 || Hkv < 1 || kv_len < 1) return 1;
+  return qkvfa::plan_decode(B, Hkv, kv_len, 0, current_cus()).n_split;
+}
+
+size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                                  int64_t D, int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || kv_len < 1 || (D != 64 && D != 128)) return 0;
+  const qkvfa::DecodePlan p = qkvfa::plan_decode(B, Hkv, kv_len, num_splits, current_cus());
+  return qkvfa::decode_workspace_bytes(B * Hq * Sq, (int)D, p.n_split);
+}
+
+qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                      const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
+                      float softmax_scale, int num_splits, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
+                                  C, D, out, lse, "qkv_decode");
+  if (st != QKV_OK) return st;
+  if ((Hq / Hkv) * Sq > 64)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode: (Hq/Hkv) * Sq must be <= 64; use qkv_prefill");
+  if (num_splits < 0 || num_splits > 1024)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode: num_splits must be in [0, 1024]");
+  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, kv_len, num_splits, current_cus());
+  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, (int)D, plan.n_split);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(QKV_ERR_WORKSPACE, "qkv_decode: workspace smaller than qkv_decode_workspace_bytes()");
+    if (!aligned(workspace, 16))
+      return fail(QKV_ERR_INVALID_ARG, "qkv_decode: workspace must be 16-byte aligned");
+  }
+  return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
+                                         kv_len, C, (int)D, softmax_scale, plan, out, lse,
+                                         workspace, static_cast<hipStream_t>(stream)),
+                    "qkv_decode");
+}
+
+qkv_status qkv_prefill(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                       const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
+                       float softmax_scale, int causal, float* out, float* lse, void* stream) {
+  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
+                                  C, D, out, lse, "qkv_prefill");
+  if (st != QKV_OK) return st;
+  if (causal != 0 && causal != 1) return fail(QKV_ERR_INVALID_ARG, "qkv_prefill: causal must be 0 or 1");
+  if (causal && Sq > kv_len)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_prefill: causal attention needs Sq <= kv_len");
+  if ((Sq + 127) / 128 > 0xFFFF)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill: too many query blocks");
+  return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
+                                          kv_len, C, (int)D, softmax_scale, causal, out, lse,
+                                          static_cast<hipStream_t>(stream)),
+                    "qkv_prefill");
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side building blocks shared by the int4-KV attention kernels (gfx950).
+//
+// Exact int4 -> fp16 conversion.  The pages dequantize low-bit KV to FP16
+// ("Quantized Cross-Attention: Extending FlashAttention-3 with In-SRAM
+// Dequantization", §2.1 step 2, §3.1); here the *codes* are converted exactly
+// and the per-token scales are applied to score columns (K) and folded into
+// the softmax probabilities (V) instead of being multiplied into every element.
+//
+// Conversion: a two's-complement nibble c becomes the offset-binary value
+// n = c + 8 in [0, 15] by flipping its top bit.  OR-ing n into the mantissa of
+// an fp16 constant whose mantissa unit is 1 gives the exact value base + n:
+//   bits 0-3  of a 16-bit half, base 1024 (0x6400): value 1024 + n
+//   bits 4-7  of a 16-bit half, base   64 (0x5400): value   64 + n
+// and one packed fp16 subtraction (1032 resp. 72) leaves exactly c.  Every
+// step is exact (integers below 2048 are exact in fp16).  gfx950 fuses the
+// flip/mask/or into one v_bitop3_b32, so two codes cost two VALU ops.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkvfa {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, f);
+}
+
+// Codes held in bits 0-3 (low half) and 16-19 (high half) of x -> exact fp16 pair.
+__device__ __forceinline__ half2v nib_lo_pair(uint32_t x) {
+  const uint32_t y = ((x ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+  const half2v bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  return bitcast<half2v>(y) - bias;
+}
+
+// Codes held in bits 4-7 (low half) and 20-23 (high half) of x -> exact fp16 pair.
+__device__ __forceinline__ half2v nib_hi_pair(uint32_t x) {
+  const uint32_t y = ((x ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
+  const half2v bias = {(_Float16)72.0f, (_Float16)72.0f};
+  return bitcast<half2v>(y) - bias;
+}
+
+// Eight codes of one packed dword (element i in bits 4i..4i+3) -> 8 exact fp16
+// values in the order [c0, c4, c1, c5, c2, c6, c3, c7].  The matching query
+// operand is permuted the same way (a dot product is order-invariant).
+__device__ __forceinline__ half8v unpack8_perm(uint32_t x) {
+  const half2v a = nib_lo_pair(x);        // c0, c4
+  const half2v b = nib_hi_pair(x);        // c1, c5
+  const half2v c = nib_lo_pair(x >> 8);   // c2, c6
+  const half2v d = nib_hi_pair(x >> 8);   // c3, c7
+  half8v r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Position of packed element e (0..7) in the unpack8_perm order, and back.
+__host__ __device__ constexpr int perm8(int e) { return (e & 1) ? 4 + (e >> 1) : (e >> 1); }
+
+// Nibble `nib` (0..7) of dword a and of dword b -> exact fp16 pair (a's, b's).
+__device__ __forceinline__ half2v nib_pair2(uint32_t a, uint32_t b, int nib) {
+  const int sh = (nib >> 1) * 8;
+  const uint32_t x = ((a >> sh) & 0xFFu) | (((b >> sh) & 0xFFu) << 16);
+  return (nib & 1) ? nib_hi_pair(x) : nib_lo_pair(x);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return bitcast<float>((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float f16bits_to_f32(uint16_t b) {
+  return (float)bitcast<_Float16>(b);
+}
+
+// fp32 pair -> packed fp16, round to nearest even (v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ half2v cvt_pk_f16(float a, float b) {
+  half2v r;
+  r[0] = (_Float16)a;
+  r[1] = (_Float16)b;
+  return r;
+}
+
+__device__ __forceinline__ float4v mfma16x16x32(half8v a, half8v b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float16v mfma32x32x16(half8v a, half8v b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave64 butterfly max / sum across lanes differing in bit `mask`.
+__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+}  // namespace qkvfa

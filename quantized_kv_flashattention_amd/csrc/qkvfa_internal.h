@@ -1,0 +1,35 @@
+// Host-side launchers of the HIP kernels (internal to libqkvfa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qkvfa {
+
+hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,
+                                  int64_t BH, int64_t T, int D, int64_t C, int64_t pos,
+                                  hipStream_t stream);
+
+struct DecodePlan {
+  int n_split;     // number of KV ranges
+  int split_len;   // tokens per range (multiple of 32)
+};
+
+DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t kv_len, int num_splits, int num_cus);
+
+size_t decode_workspace_bytes(int64_t rows, int D, int n_split);
+
+hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
+                         const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
+                         float softmax_scale, const DecodePlan& plan, float* out, float* lse,
+                         void* workspace, hipStream_t stream);
+
+hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
+                          const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
+                          float softmax_scale, int causal, float* out, float* lse,
+                          hipStream_t stream);
+
+}  // namespace qkvfa

@@ -11,6 +11,11 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    lib = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")
+    if not os.path.exists(lib):
+        # nothing built yet: build once (hipcc cross-compiles without a GPU)
+        from quantized_kv_flashattention_amd.build import build
+        build()
 
 
 def _gpu_available():

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (runs on CPU; no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkvfa.h")
+LIB = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from quantized_kv_flashattention_amd.build import build
+        build()
+    L = ctypes.CDLL(LIB)
+    i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    L.qkv_quantize_append.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    L.qkv_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp, sz, vp]
+    L.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp]
+    L.qkv_last_error.restype = ctypes.c_char_p
+    L.qkv_status_string.restype = ctypes.c_char_p
+    L.qkv_decode_workspace_bytes.restype = sz
+    L.qkv_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"qkv_quantize_append", "qkv_decode", "qkv_prefill", "qkv_decode_workspace_bytes",
+                          "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.qkv_status_string(0) == b"ok"
+    assert lib.qkv_status_string(3) == b"workspace too small"
+    assert lib.qkv_version() == 100
+
+
+P = 16  # a fake, 16-byte aligned non-null address: never dereferenced on these paths
+
+
+def _qa(lib, **kw):
+    a = dict(src=P, codes=P, scales=P, B=1, Hkv=1, T=4, D=128, C=8, pos=0)
+    a.update(kw)
+    return lib.qkv_quantize_append(a["src"], a["codes"], a["scales"], a["B"], a["Hkv"], a["T"], a["D"],
+                                   a["C"], a["pos"], None)
+
+
+def test_quantize_append_argument_errors(lib):
+    assert _qa(lib, D=96) == 2
+    assert _qa(lib, pos=5) == 1                 # pos + T > C
+    assert b"pos" in lib.qkv_last_error()
+    assert _qa(lib, pos=-1) == 1
+    assert _qa(lib, B=0) == 1
+    assert _qa(lib, src=None) == 1
+    assert _qa(lib, src=P + 4) == 1             # misaligned
+    assert _qa(lib, scales=P + 1) == 1
+    assert b"misaligned" in lib.qkv_last_error()
+    assert _qa(lib, T=0, src=None) == 0         # nothing to do: ok, nothing enqueued
+
+
+def _dec(lib, **kw):
+    a = dict(q=P, kc=P, ks=P, vc=P, vs=P, B=1, Hq=4, Hkv=2, Sq=1, L=100, C=128, D=128, scale=0.1, ns=0,
+             out=P, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qkv_decode(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["L"],
+                          a["C"], a["D"], a["scale"], a["ns"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_decode_argument_errors(lib):
+    assert _dec(lib, D=80) == 2
+    assert _dec(lib, Hq=3) == 1                 # Hq % Hkv
+    assert _dec(lib, L=0) == 1
+    assert _dec(lib, L=129) == 1                # kv_len > C
+    assert _dec(lib, Sq=33) == 2                # G * Sq > 64
+    assert _dec(lib, q=None) == 1
+    assert _dec(lib, out=P + 8) == 1
+    assert _dec(lib, ns=-1) == 1
+    assert _dec(lib, ns=2000) == 1
+    assert _dec(lib, ns=2) == 3                 # needs a workspace
+    assert b"workspace" in lib.qkv_last_error()
+    assert _dec(lib, ns=2, ws=P, wsb=10) == 3
+
+
+def test_decode_workspace_size(lib):
+    assert lib.qkv_decode_workspace_bytes(1, 4, 2, 1, 100, 128, 1) == 0
+    n = lib.qkv_decode_workspace_bytes(1, 4, 2, 1, 100, 128, 2)
+    assert n >= 4 * 2 * 128 * 4 + 4 * 2 * 4
+    assert lib.qkv_decode_workspace_bytes(1, 4, 2, 1, 100, 96, 2) == 0
+
+
+def _pre(lib, **kw):
+    a = dict(q=P, kc=P, ks=P, vc=P, vs=P, B=1, Hq=4, Hkv=2, Sq=10, L=100, C=128, D=64, scale=0.1, causal=1,
+             out=P, lse=None)
+    a.update(kw)
+    return lib.qkv_prefill(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["L"],
+                           a["C"], a["D"], a["scale"], a["causal"], a["out"], a["lse"], None)
+
+
+def test_prefill_argument_errors(lib):
+    assert _pre(lib, Sq=101) == 1               # causal needs Sq <= kv_len
+    assert _pre(lib, causal=2) == 1
+    assert _pre(lib, D=32) == 2
+    assert _pre(lib, Hkv=3) == 1
+    assert _pre(lib, lse=P + 2) == 1
+    assert _pre(lib, kc=P + 8) == 1
