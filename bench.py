@@ -122,7 +122,7 @@ def bench_decode(torch, qkv, w, steps, warmup, with_append):
     out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
     ns = qkv.decode_auto_splits(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D)
     ws_bytes = qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")   # tickets start at zero
 
     def decode_only(i):
         qkv.decode(q, caches[i], w.L, softmax_scale=w.softmax_scale, out=out, workspace=ws)

@@ -108,7 +108,14 @@ qkv_status qkv_quantize_append(const float* src, uint8_t* codes, uint16_t* scale
  *   lse      float [B, Hq, Sq] or NULL (written)
  *   workspace, workspace_bytes: device scratch of at least
  *            qkv_decode_workspace_bytes(...) bytes (may be NULL when that
- *            is 0); its contents on entry do not matter.
+ *            is 0), 16-byte aligned.  Its first 4 * B * Hkv bytes (rounded
+ *            up to 256) hold one ticket counter per (batch, KV head); the
+ *            rest holds split partials.  The tickets must be zero when a
+ *            call starts and every completed call leaves them zero, so a
+ *            workspace zeroed once serves any sequence of calls with the
+ *            same B * Hkv (other sizes may change between calls).  Zero it
+ *            again before using it with a different B * Hkv.  Calls that
+ *            share a workspace must not run concurrently.
  * Requires D in {64, 128}, Hq % Hkv == 0, 1 <= kv_len <= C,
  * 1 <= G * Sq <= 64 (more rows belong to qkv_prefill).
  */

@@ -176,6 +176,25 @@ def decode_auto_splits(B, Hq, Hkv, Sq, kv_len, D) -> int:
     return int(_lib.qkv_decode_auto_splits(B, Hq, Hkv, Sq, kv_len, D))
 
 
+_WORKSPACES = {}
+
+
+def _workspace(device, units, nbytes):
+    """A zero-initialised decode workspace per (device, B*Hkv), grown on demand.
+
+    Its ticket counters sit at offset 0 and the kernels return them to zero
+    after every call, so it is reused as is by every call with the same
+    B*Hkv.  Calls on different streams must not share it: pass an explicit
+    zeroed ``workspace`` tensor for concurrent decodes.
+    """
+    key = (device.type, device.index, int(units))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False, out=None,
            lse=None, workspace=None):
     """Decode attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)`` (no mask)."""
@@ -189,7 +208,7 @@ def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False,
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(q.device, B * Hkv, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     kc, ks, vc, vs = tensors
     _check(_lib.qkv_decode(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,

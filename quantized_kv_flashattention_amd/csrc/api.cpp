@@ -1,6 +1,6 @@
 // C ABI of libqkvfa: argument validation, split planning and kernel launch.
 // Every check happens before anything is enqueued; no exception leaves here.
-#include "../../include/qkvfa.h"
+#include "qkvfa.h"
 
 #include <hip/hip_runtime.h>
 
@@ -107,16 +107,15 @@ qkv_status qkv_quantize_append(const float* src, uint8_t* codes, uint16_t* scale
 
 int qkv_decode_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
                            int64_t D) {
-  (void)Hq; (void)Sq; (void)D;
-  if (B < 1 || Hkv < 1 || kv_len < 1) return 1;
-  return qkvfa::plan_decode(B, Hkv, kv_len, 0, current_cus()).n_split;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || kv_len < 1 || (D != 64 && D != 128)) return 1;
+  return qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, 0, current_cus()).n_split;
 }
 
 size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
                                   int64_t D, int num_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || kv_len < 1 || (D != 64 && D != 128)) return 0;
-  const qkvfa::DecodePlan p = qkvfa::plan_decode(B, Hkv, kv_len, num_splits, current_cus());
-  return qkvfa::decode_workspace_bytes(B * Hq * Sq, (int)D, p.n_split);
+  const qkvfa::DecodePlan p = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus());
+  return qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, p.n_split);
 }
 
 qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
@@ -131,8 +130,8 @@ qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t*
     return fail(QKV_ERR_UNSUPPORTED, "qkv_decode: (Hq/Hkv) * Sq must be <= 64; use qkv_prefill");
   if (num_splits < 0 || num_splits > 1024)
     return fail(QKV_ERR_INVALID_ARG, "qkv_decode: num_splits must be in [0, 1024]");
-  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, kv_len, num_splits, current_cus());
-  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, (int)D, plan.n_split);
+  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus());
+  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, plan.n_split);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(QKV_ERR_WORKSPACE, "qkv_decode: workspace smaller than qkv_decode_workspace_bytes()");

@@ -26,10 +26,15 @@
 //   output O^T   : lane holds query row r, head dims 32j .. 32j+31 (D=128)
 // so a lane's eight probabilities are exactly the eight tokens of its V dwords
 // and no data moves between lanes except the row max (two butterflies).
+// Per-lane load offsets are loop-invariant; only the uniform chunk base moves.
+// The next chunk's codes are loaded before the current chunk is processed.
 //
 // After the loop the four waves of a workgroup merge their (m, l, O) through
-// LDS; a workgroup writes the normalized partial O_s and lse_s of its split,
-// and a second kernel merges splits in split order (deterministic).
+// LDS.  With one split the result goes straight to `out`.  Otherwise each
+// workgroup writes its split's normalized partial O_s and lse_s, and the last
+// workgroup of a (batch, KV head) to finish (an atomic ticket per group)
+// merges all splits in split order -- deterministic, and no second launch.
+// The ticket returns to zero after the merge, ready for the next call.
 #include <math.h>
 
 #include "qkvfa_device.hpp"
@@ -40,70 +45,103 @@ namespace qkvfa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kChunk = 32;  // tokens per wave iteration
+constexpr int kChunk = 32;     // tokens per wave iteration
+constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* kc;
+  const uint16_t* ks;
+  const uint8_t* vc;
+  const uint16_t* vs;
+  float* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  uint32_t* tickets;
+  int part_bytes;   // bytes of part_o
+  int64_t C;
+  int Hq, Hkv, G, Sq, kv_len, split_len, n_split;
+  float qk_log2;
+};
+
+template <int D>
+struct ChunkRegs {
+  uint32_t kw[2][D / 32];
+  uint32_t vw[8];
+  uint16_t sk, sv;   // K and V scale of token (lane % 32) of the chunk
+};
+
+// One wave64 per SIMD slot holds NB*32 + ~90 VGPRs; with one row block the
+// kernel is asked to fit 128 so four waves share each SIMD (16 per CU).  The
+// 64-row variant skips the one-chunk prefetch to stay within 256 VGPRs.
 template <int D, int NB>
-__global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
-    const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-    const uint16_t* __restrict__ vs, int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C,
-    float qk_log2, int split_len, int n_split, float* __restrict__ out,
-    float* __restrict__ lse_out, float* __restrict__ part_o, float* __restrict__ part_lse) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
+void decode_kernel(const DecodeArgs a) {
+  constexpr bool kPrefetch = (NB <= 2);
   constexpr int KK = D / 32;    // QK MFMAs per 16-token block
   constexpr int DW = D / 8;     // dwords per packed row
   constexpr int NPB = D / 16;   // PV MFMAs (16 head dims each)
   constexpr int ROWB = D / 2;   // bytes per packed row
   constexpr int OSTR = D + 4;   // padded LDS row stride of the merge buffer (floats)
 
-  __shared__ __align__(16) uint16_t s_scale[kWaves][64];
+  __shared__ __align__(16) _Float16 s_q[NB * 16 * D];
+  __shared__ __align__(16) float s_sc[kWaves][64];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ __align__(16) float s_o[kWaves][16 * OSTR];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int j = lane >> 4;
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
+  const int G = a.G, Sq = a.Sq, kv_len = a.kv_len;
   const int R = G * Sq;
-  const int t_begin = split * split_len;
-  const int t_end = min(kv_len, t_begin + split_len);
+  const int t_begin = split * a.split_len;
+  const int t_end = min(kv_len, t_begin + a.split_len);
 
-  const int64_t kvrow0 = ((int64_t)b * Hkv + g) * C;
-  const uint8_t* kbase = kc + kvrow0 * ROWB;
-  const uint8_t* vbase = vc + kvrow0 * ROWB;
-  const uint16_t* ksb = ks + kvrow0;
-  const uint16_t* vsb = vs + kvrow0;
+  const int64_t kvrow0 = ((int64_t)b * a.Hkv + g) * a.C;
+  const uint8_t* kbase = a.kc + kvrow0 * ROWB;
+  const uint8_t* vbase = a.vc + kvrow0 * ROWB;
+  const uint16_t* ksb = a.ks + kvrow0;
+  const uint16_t* vsb = a.vs + kvrow0;
+  const float sc_mul = (lane < 32) ? a.qk_log2 : 1.0f;
+
+  // Loop-invariant per-lane byte offsets inside a chunk.
+  const uint32_t offk = (uint32_t)((8 * (r >> 2) + (r & 3)) * ROWB + 4 * KK * j);  // +4 rows for kb = 1
+  const uint32_t offv = (uint32_t)(8 * j * ROWB + 4 * (r % DW));
+  const uint32_t offs = (uint32_t)(2 * (lane & 31));
 
   // Query operand (B of S^T = K Q^T): query row nb*16 + r, k = 8j + e <->
   // head dim 8*(KK*j + kk) + perm8(e), matching the K lane's dword order.
-  half8v qop[NB][KK];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = nb * 16 + r;
+  // Converted once into LDS (shared by the four waves): 16-byte chunk c of
+  // row x sits at chunk c ^ (x % 16), so the 16 rows a wave reads together
+  // fall in different banks.
+  for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 256) {
+    const int row = idx / DW;
+    const int c = idx - row * DW;
+    half8v h = half8v{};
     if (row < R) {
       const int hg = row / Sq;
       const int sq = row - hg * Sq;
-      const uint16_t* qr = q + (((int64_t)b * Hq + g * G + hg) * Sq + sq) * D;
+      const uint16_t* qr = a.q + (((int64_t)b * a.Hq + g * G + hg) * Sq + sq) * D + 8 * c;
+      const uint4v w = *reinterpret_cast<const uint4v*>(qr);
+      uint16_t e16[8];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4v w = *reinterpret_cast<const uint4v*>(qr + 8 * (KK * j + kk));
-        uint16_t e16[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
-          e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qop[nb][kk][e] = (_Float16)bf16_to_f32(e16[perm8(e)]);
+      for (int t = 0; t < 4; ++t) {
+        e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
+        e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
       }
-    } else {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qop[nb][kk] = half8v{};
+      for (int e = 0; e < 8; ++e) h[e] = (_Float16)bf16_to_f32(e16[perm8(e)]);
     }
+    *reinterpret_cast<half8v*>(&s_q[(row * DW + (c ^ (row & 15 & (DW - 1)))) * 8]) = h;
   }
+  __syncthreads();
 
   float m_run[NB], l_run[NB];
   float4v o_acc[NB][NPB];
@@ -115,80 +153,93 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int p = 0; p < NPB; ++p) o_acc[nb][p] = float4v{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
-  for (int c = wave; c < n_chunks; c += kWaves) {
-    const int c0 = t_begin + c * kChunk;
-
-    // ---- loads (token indices clamped into [0, kv_len) for memory safety;
-    //      tokens >= t_end are masked below)
-    uint32_t kw[2][KK];
+  // Codes of the chunk starting at token c0, through buffer descriptors whose
+  // range ends at row kv_len: the hardware returns zero for any row at or
+  // past kv_len (those tokens are masked), so the sequence's last chunk needs
+  // no clamping and no load can leave the valid rows.
+  auto load_chunk = [&](int c0, ChunkRegs<D>& cr) {
+    const int rows_left = kv_len - c0;
+    const rsrc_t rk = make_rsrc(kbase + (int64_t)c0 * ROWB, rows_left * ROWB);
+    const rsrc_t rv = make_rsrc(vbase + (int64_t)c0 * ROWB, rows_left * ROWB);
+    const rsrc_t rks = make_rsrc(ksb + c0, rows_left * 2);
+    const rsrc_t rvs = make_rsrc(vsb + c0, rows_left * 2);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int tok = min(c0 + 8 * (r >> 2) + 4 * kb + (r & 3), kv_len - 1);
-      const uint8_t* p = kbase + (int64_t)tok * ROWB + (4 * KK) * j;
       if constexpr (KK == 4) {
-        const uint4v w = *reinterpret_cast<const uint4v*>(p);
+        const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kw[kb][kk] = w[kk];
+        for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
       } else {
-        const uint2v w = *reinterpret_cast<const uint2v*>(p);
-        kw[kb][0] = w[0];
-        kw[kb][1] = w[1];
+        const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
+        cr.kw[kb][0] = w[0];
+        cr.kw[kb][1] = w[1];
       }
     }
-    uint32_t vw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = min(c0 + 8 * j + e, kv_len - 1);
-      vw[e] = *reinterpret_cast<const uint32_t*>(vbase + (int64_t)tok * ROWB + 4 * (r % DW));
-      if constexpr (D == 64) vw[e] = (r >= 8) ? (vw[e] >> 16) : vw[e];
+    for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
+    cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
+    cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
+  };
+
+  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
+  ChunkRegs<D> cur;
+  if (wave < n_chunks) load_chunk(t_begin + wave * kChunk, cur);
+
+  for (int c = wave; c < n_chunks; c += kWaves) {
+    const int c0 = t_begin + c * kChunk;
+    // Compiler-only barrier: keeps the query-operand LDS reads inside the loop
+    // instead of hoisted into (NB * D / 8) live registers per lane.
+    asm volatile("" ::: "memory");
+    ChunkRegs<D> nxt;
+    if constexpr (kPrefetch) {
+      if (c + kWaves < n_chunks) load_chunk(c0 + kWaves * kChunk, nxt);
     }
-    {
-      const int tok = min(c0 + (lane & 31), kv_len - 1);
-      s_scale[wave][lane] = (lane < 32) ? ksb[tok] : vsb[tok];
-    }
-    // The LDS write above and the reads below are issued by the same wave and
-    // execute in order; no barrier is needed.
-    const uint4v ksc = *reinterpret_cast<const uint4v*>(&s_scale[wave][8 * j]);
-    const uint4v vsc = *reinterpret_cast<const uint4v*>(&s_scale[wave][32 + 8 * j]);
-    float csk[8], sv[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      csk[2 * t] = f16bits_to_f32((uint16_t)(ksc[t] & 0xFFFFu)) * qk_log2;
-      csk[2 * t + 1] = f16bits_to_f32((uint16_t)(ksc[t] >> 16)) * qk_log2;
-      sv[2 * t] = f16bits_to_f32((uint16_t)(vsc[t] & 0xFFFFu));
-      sv[2 * t + 1] = f16bits_to_f32((uint16_t)(vsc[t] >> 16));
-    }
+
+    // ---- scales: each lane converts one, the wave reads its eight back
+    s_sc[wave][lane] = f16bits_to_f32(lane < 32 ? cur.sk : cur.sv) * sc_mul;
+    const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
+    const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
+    const float4v sv0 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j]);
+    const float4v sv1 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j + 4]);
+    const float csk[8] = {ck0[0], ck0[1], ck0[2], ck0[3], ck1[0], ck1[1], ck1[2], ck1[3]};
+    const float sv[8] = {sv0[0], sv0[1], sv0[2], sv0[3], sv1[0], sv1[1], sv1[2], sv1[3]};
     const bool full = (c0 + kChunk <= t_end);
 
-    // ---- V operand: nibble p of the eight token dwords -> exact fp16 (token e = k index)
-    half8v vop[NPB];
+    if constexpr (D == 64) {
+      // lanes 8..15 own nibbles 4..7 of their dword: move them down
 #pragma unroll
-    for (int p = 0; p < NPB; ++p) {
+      for (int e = 0; e < 8; ++e) cur.vw[e] = (r >= 8) ? (cur.vw[e] >> 16) : cur.vw[e];
+    }
+
+    // ---- scores S^T for 2 x 16 tokens and every 16-row block; each K operand
+    //      is converted once and used for all row blocks
+    float4v s_t[NB][2];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const half2v pr = nib_pair2(vw[2 * hh], vw[2 * hh + 1], p);
-        vop[p][2 * hh] = pr[0];
-        vop[p][2 * hh + 1] = pr[1];
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const half8v kop = unpack8_perm(cur.kw[kb][kk]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int qrow = nb * 16 + r;
+          const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
+          const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+          s_t[nb][kb] = mfma16x16x32(kop, qop, s_t[nb][kb]);
+        }
       }
     }
 
+    // ---- online softmax per row block -> P^T operand (V scale folded in)
+    half8v pop[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      // ---- scores S^T for 2 x 16 tokens
-      float4v s_t[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) acc = mfma16x16x32(unpack8_perm(kw[kb][kk]), qop[nb][kk], acc);
-        s_t[kb] = acc;
-      }
       float x[8];
       float mloc = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float v = s_t[e >> 2][e & 3] * csk[e];
+        float v = s_t[nb][e >> 2][e & 3] * csk[e];
         if (!full) v = (c0 + 8 * j + e < t_end) ? v : -INFINITY;
         x[e] = v;
         mloc = fmaxf(mloc, v);
@@ -198,15 +249,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
       const float alpha = fast_exp2(m_run[nb] - m_new);
       float lsum = 0.0f;
-      half8v pop;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float p0 = fast_exp2(x[e] - m_new);
         const float p1 = fast_exp2(x[e + 1] - m_new);
         lsum += p0 + p1;
         const half2v pr = cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]);
-        pop[e] = pr[0];
-        pop[e + 1] = pr[1];
+        pop[nb][e] = pr[0];
+        pop[nb][e + 1] = pr[1];
       }
       l_run[nb] = l_run[nb] * alpha + lsum;
       m_run[nb] = m_new;
@@ -214,13 +264,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
         for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
       }
-      // ---- O^T += V^T P^T
+    }
+
+    // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
+    //      token dwords, low and high nibble -> exact fp16 (token e = k index)
 #pragma unroll
-      for (int p = 0; p < NPB; ++p) o_acc[nb][p] = mfma16x16x32(vop[p], pop, o_acc[nb][p]);
+    for (int k = 0; k < NPB / 2; ++k) {
+      half8v vlo, vhi;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const uint32_t xb = pair_bytes(cur.vw[2 * hh], cur.vw[2 * hh + 1], k);
+        const half2v lo = nib_lo_pair(xb);
+        const half2v hi = nib_hi_pair(xb);
+        vlo[2 * hh] = lo[0];
+        vlo[2 * hh + 1] = lo[1];
+        vhi[2 * hh] = hi[0];
+        vhi[2 * hh + 1] = hi[1];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
+        o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
+      }
+    }
+    if constexpr (kPrefetch) {
+      cur = nxt;
+    } else if (c + kWaves < n_chunks) {
+      load_chunk(c0 + kWaves * kChunk, cur);
     }
   }
 
   // ---- merge the four waves through LDS, one 16-row block at a time
+  const bool direct = (a.n_split == 1);
+  // one descriptor over all partial outputs (the planner keeps them < 2 GiB)
+  const rsrc_t rpart = make_rsrc(a.part_o, direct ? 0 : a.part_bytes);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float l = xor_sum(l_run[nb], 16);
@@ -247,98 +324,101 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
     __syncthreads();
     const int rows_here = min(16, R - nb * 16);
-    for (int idx = threadIdx.x; idx < rows_here * D; idx += 256) {
-      const int rr = idx / D;
-      const int d = idx - rr * D;
+    for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += 256) {
+      const int rr = idx / (D / 4);
+      const int d = 4 * (idx - rr * (D / 4));
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
-      float acc = 0.0f, den = 0.0f;
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wt = fast_exp2(s_m[w][rr] - M);   // empty waves: exp2(-inf) = 0
-        acc += wt * s_o[w][rr * OSTR + d];
+        acc += wt * *reinterpret_cast<const float4v*>(&s_o[w][rr * OSTR + d]);
         den += wt * s_l[w][rr];
       }
       const int row = nb * 16 + rr;
       const int hg = row / Sq;
       const int sq = row - hg * Sq;
-      const int64_t grow = ((int64_t)b * Hq + g * G + hg) * Sq + sq;
-      const float o = acc / den;
-      const float lse2 = M + __log2f(den);
-      if (n_split == 1) {
-        out[grow * D + d] = o;
-        if (d == 0 && lse_out) lse_out[grow] = lse2 * kLn2;
+      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + sq;
+      const float inv = 1.0f / den;
+      const float lse2 = M + log2f(den);
+      if (direct) {
+        *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * inv;
+        if (d == 0 && a.lse) a.lse[grow] = lse2 * kLn2;
       } else {
-        part_o[(grow * n_split + split) * D + d] = o;
-        if (d == 0) part_lse[grow * n_split + split] = lse2;   // log2 units
+        // device-coherent stores (sc1): visible to every XCD without an L2 writeback
+        __builtin_amdgcn_raw_buffer_store_b128(
+            acc * inv, rpart, (uint32_t)(((grow * a.n_split + split) * D + d) * 4), 0, kCoherent);
+        if (d == 0)   // log2 units
+          __hip_atomic_store(a.part_lse + grow * a.n_split + split, lse2, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
   }
-}
+  if (direct) return;
 
-// Merge split partials: O = sum_s w_s O_s / sum_s w_s, w_s = 2^(lse_s - max).
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_lse,
-                                                         int n_split, float* __restrict__ out,
-                                                         float* __restrict__ lse_out) {
-  const int64_t row = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* pl = part_lse + row * n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[s]);
-  float acc = 0.0f, den = 0.0f;
-  const float* po = part_o + row * n_split * D + d;
-  for (int s = 0; s < n_split; ++s) {
-    const float w = fast_exp2(pl[s] - M);
-    acc += w * po[(int64_t)s * D];
-    den += w;
+  // ---- split merge by the last workgroup of this (batch, KV head) to finish.
+  // Partials were written with device-coherent stores; waiting for their
+  // completion before the barrier orders them before the ticket increment.
+  // The merging workgroup reads them back with device-coherent loads, so no
+  // L2 writeback or invalidation (an expensive whole-cache operation) is needed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint32_t* ticket = a.tickets + (int64_t)b * a.Hkv + g;
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (uint32_t)(a.n_split - 1));
   }
-  out[row * D + d] = acc / den;
-  if (d == 0 && lse_out) lse_out[row] = (M + __log2f(den)) * kLn2;
+  __syncthreads();
+  if (!s_last) return;
+  const int n_split = a.n_split;
+  for (int idx = threadIdx.x; idx < R * (D / 4); idx += 256) {
+    const int row = idx / (D / 4);
+    const int d = 4 * (idx - row * (D / 4));
+    const int hg = row / Sq;
+    const int sq = row - hg * Sq;
+    const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + sq;
+    const float* pl = a.part_lse + grow * n_split;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s)
+      M = fmaxf(M, __hip_atomic_load(pl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+      const float w = fast_exp2(__hip_atomic_load(pl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
+      const float4v o = __builtin_amdgcn_raw_buffer_load_b128(
+          rpart, (uint32_t)(((grow * n_split + s) * D + d) * 4), 0, kCoherent);
+      acc += w * o;
+      den += w;
+    }
+    *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (1.0f / den);
+    if (d == 0 && a.lse) a.lse[grow] = (M + log2f(den)) * kLn2;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int NB>
-hipError_t launch_split(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
-                        const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
-                        int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, float qk_log2,
-                        const DecodePlan& plan, float* out, float* lse, float* part_o,
-                        float* part_lse, hipStream_t stream) {
-  dim3 grid((uint32_t)plan.n_split, (uint32_t)Hkv, (uint32_t)B);
-  decode_split_kernel<D, NB><<<grid, dim3(256), 0, stream>>>(
-      q, kc, ks, vc, vs, (int)Hq, (int)Hkv, (int)(Hq / Hkv), (int)Sq, (int)kv_len, C, qk_log2,
-      plan.split_len, plan.n_split, out, lse, part_o, part_lse);
+hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
+  dim3 grid((uint32_t)n_split, (uint32_t)Hkv, (uint32_t)B);
+  decode_kernel<D, NB><<<grid, dim3(256), 0, stream>>>(args);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
-                    const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
-                    int64_t kv_len, int64_t C, float qk_log2, const DecodePlan& plan, float* out,
-                    float* lse, float* part_o, float* part_lse, hipStream_t stream) {
-  const int64_t R = (Hq / Hkv) * Sq;
-  hipError_t err;
-  if (R <= 16)
-    err = launch_split<D, 1>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, plan, out, lse,
-                             part_o, part_lse, stream);
-  else if (R <= 32)
-    err = launch_split<D, 2>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, plan, out, lse,
-                             part_o, part_lse, stream);
-  else
-    err = launch_split<D, 4>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, plan, out, lse,
-                             part_o, part_lse, stream);
-  if (err != hipSuccess || plan.n_split == 1) return err;
-  const int64_t rows = B * Hq * Sq;
-  decode_merge_kernel<D><<<dim3((uint32_t)rows), dim3(D), 0, stream>>>(part_o, part_lse,
-                                                                        plan.n_split, out, lse);
-  return hipGetLastError();
+hipError_t launch_d(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
+  const int R = args.G * args.Sq;
+  if (R <= 16) return launch_nb<D, 1>(args, B, Hkv, n_split, stream);
+  if (R <= 32) return launch_nb<D, 2>(args, B, Hkv, n_split, stream);
+  return launch_nb<D, 4>(args, B, Hkv, n_split, stream);
 }
 
 }  // namespace
 
-DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t kv_len, int num_splits, int num_cus) {
+DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int D, int num_splits,
+                       int num_cus) {
   const int64_t chunks = (kv_len + kChunk - 1) / kChunk;
   const int64_t units = B * Hkv;
   int64_t ns;
@@ -352,6 +432,9 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t kv_len, int num_splits, i
   }
   if (ns > chunks) ns = chunks;
   if (ns > 1024) ns = 1024;
+  // partial outputs (rows * ns * D fp32) are addressed with 32-bit offsets
+  const int64_t max_ns_bytes = ((int64_t)1 << 31) / ((int64_t)rows * D * 4 + 1);
+  if (ns > max_ns_bytes) ns = max_ns_bytes;
   if (ns < 1) ns = 1;
   const int64_t cps = (chunks + ns - 1) / ns;   // chunks per split
   DecodePlan p;
@@ -360,11 +443,15 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t kv_len, int num_splits, i
   return p;
 }
 
-size_t decode_workspace_bytes(int64_t rows, int D, int n_split) {
+// Workspace: one uint32 ticket per (batch, KV head) at offset 0 (a fixed place
+// for a given B*Hkv, whatever the other sizes), then partial outputs
+// [rows][n_split][D] fp32, then partial LSE [rows][n_split] fp32 (log2 units).
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t decode_workspace_bytes(int64_t rows, int64_t units, int D, int n_split) {
   if (n_split <= 1) return 0;
-  const size_t o = (size_t)rows * n_split * D * sizeof(float);
-  const size_t l = (size_t)rows * n_split * sizeof(float);
-  return ((o + 255) / 256) * 256 + l;
+  return align256((size_t)units * sizeof(uint32_t)) +
+         align256((size_t)rows * n_split * D * sizeof(float)) + (size_t)rows * n_split * sizeof(float);
 }
 
 hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
@@ -372,20 +459,26 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, hipStream_t stream) {
-  const float qk_log2 = softmax_scale * kLog2e;
-  float* part_o = nullptr;
-  float* part_lse = nullptr;
+  DecodeArgs a;
+  a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
+  a.out = out; a.lse = lse;
+  a.part_o = nullptr; a.part_lse = nullptr; a.tickets = nullptr; a.part_bytes = 0;
   if (plan.n_split > 1) {
     const int64_t rows = B * Hq * Sq;
-    const size_t o = (size_t)rows * plan.n_split * D * sizeof(float);
-    part_o = static_cast<float*>(workspace);
-    part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o + 255) / 256) * 256);
+    char* w = static_cast<char*>(workspace);
+    const size_t t = align256((size_t)B * Hkv * sizeof(uint32_t));
+    const size_t o = align256((size_t)rows * plan.n_split * D * sizeof(float));
+    a.tickets = reinterpret_cast<uint32_t*>(w);
+    a.part_o = reinterpret_cast<float*>(w + t);
+    a.part_lse = reinterpret_cast<float*>(w + t + o);
+    a.part_bytes = (int)((size_t)rows * plan.n_split * D * sizeof(float));
   }
-  if (D == 128)
-    return launch_d<128>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, plan, out, lse,
-                         part_o, part_lse, stream);
-  return launch_d<64>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, plan, out, lse, part_o,
-                      part_lse, stream);
+  a.C = C;
+  a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv); a.Sq = (int)Sq; a.kv_len = (int)kv_len;
+  a.split_len = plan.split_len; a.n_split = plan.n_split;
+  a.qk_log2 = softmax_scale * kLog2e;
+  if (D == 128) return launch_d<128>(a, (int)B, (int)Hkv, plan.n_split, stream);
+  return launch_d<64>(a, (int)B, (int)Hkv, plan.n_split, stream);
 }
 
 }  // namespace qkvfa

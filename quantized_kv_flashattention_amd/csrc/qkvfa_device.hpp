@@ -68,11 +68,26 @@ __device__ __forceinline__ half8v unpack8_perm(uint32_t x) {
 // Position of packed element e (0..7) in the unpack8_perm order, and back.
 __host__ __device__ constexpr int perm8(int e) { return (e & 1) ? 4 + (e >> 1) : (e >> 1); }
 
+// Byte k of dword a into bits 0-7 and byte k of dword b into bits 16-23
+// (other bits zero): one v_perm_b32.  Selector bytes 0-3 pick bytes of the
+// second operand, 4-7 bytes of the first, 12 gives 0x00.
+__device__ __forceinline__ uint32_t pair_bytes(uint32_t a, uint32_t b, int k) {
+  const uint32_t sel = (uint32_t)k | (12u << 8) | ((uint32_t)(4 + k) << 16) | (12u << 24);
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
 // Nibble `nib` (0..7) of dword a and of dword b -> exact fp16 pair (a's, b's).
 __device__ __forceinline__ half2v nib_pair2(uint32_t a, uint32_t b, int nib) {
-  const int sh = (nib >> 1) * 8;
-  const uint32_t x = ((a >> sh) & 0xFFu) | (((b >> sh) & 0xFFu) << 16);
+  const uint32_t x = pair_bytes(a, b, nib >> 1);
   return (nib & 1) ? nib_hi_pair(x) : nib_lo_pair(x);
+}
+
+// Raw buffer descriptor over [base, base + num_bytes): loads at offsets past
+// num_bytes return zero instead of touching memory (gfx9-family raw buffer
+// range check; the fourth descriptor word selects 32-bit data format).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes, 0x00020000);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

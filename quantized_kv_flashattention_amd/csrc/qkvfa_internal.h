@@ -16,9 +16,12 @@ struct DecodePlan {
   int split_len;   // tokens per range (multiple of 32)
 };
 
-DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t kv_len, int num_splits, int num_cus);
+// Split plan for rows = B*Hq*Sq query rows; num_splits = 0 picks the count.
+DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int D, int num_splits,
+                       int num_cus);
 
-size_t decode_workspace_bytes(int64_t rows, int D, int n_split);
+// Bytes of decode workspace: split partials plus one ticket per (batch, KV head).
+size_t decode_workspace_bytes(int64_t rows, int64_t units, int D, int n_split);
 
 hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
                          const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,

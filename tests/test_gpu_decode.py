@@ -99,3 +99,42 @@ def test_full_size_decode_workloads(index):
     mx, mn = assert_close(out, ro, w.name)
     print(f"{w.name}: max {mx:.3e} mean {mn:.3e}")
     assert compare(lse, rl)[0] < 1e-3
+
+
+def test_workspace_reuse_across_shapes():
+    """One zeroed workspace serves a sequence of calls with the same B*Hkv whose
+    split counts and sizes change: the tickets sit at a fixed offset and each
+    call leaves them at zero."""
+    ws = torch.zeros(4 << 20, dtype=torch.uint8, device=DEV)
+    for Sq, L, ns in [(4, 3000, 20), (1, 500, 2), (16, 999, 7), (2, 64, 2), (1, 4000, 0), (3, 3000, 20)]:
+        q, kc, ks, vc, vs = random_case(L + Sq, 1, 8, 2, Sq, L, 128)
+        out = qkv.decode(q_to_dev(q), cache_to_dev(kc, ks, vc, vs), L, softmax_scale=0.1, num_splits=ns,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        ro, _ = oracle.attention(q, kc, ks, vc, vs, L, 0.1)
+        assert_close(out, ro, f"Sq={Sq} L={L} ns={ns}")
+        assert int((ws[:8] != 0).sum()) == 0, "tickets not returned to zero"
+
+
+@pytest.mark.parametrize("case", [(16, 32, 8, 1, 8192, 128, 0), (1, 64, 8, 1, 20000, 128, 0), (2, 8, 2, 4, 3000, 64, 11)])
+def test_split_merge_sees_fresh_partials(case):
+    """The last workgroup of a group merges partials written by workgroups on
+    other XCDs.  Alternate two caches of the same shape many times: every
+    output must equal the first output of its own inputs bit for bit (a stale
+    partial from the other input set would show up as a difference)."""
+    B, Hq, Hkv, Sq, L, D, ns = case
+    inputs = [random_case(100 + t, B, Hq, Hkv, Sq, L, D) for t in range(2)]
+    dev = [(q_to_dev(q), cache_to_dev(kc, ks, vc, vs)) for q, kc, ks, vc, vs in inputs]
+    first = [None, None]
+    for it in range(24):
+        t = it % 2
+        out = qkv.decode(dev[t][0], dev[t][1], L, softmax_scale=0.09, num_splits=ns)
+        torch.cuda.synchronize()
+        if first[t] is None:
+            first[t] = out.clone()
+            q, kc, ks, vc, vs = inputs[t]
+            heads = [(b, h) for b in range(min(B, 2)) for h in range(Hq)]
+            ro, _ = oracle.attention(q, kc, ks, vc, vs, L, 0.09, heads=heads)
+            assert_close(out, ro, f"{case} input {t}")
+        else:
+            assert torch.equal(out, first[t]), f"{case}: iteration {it} differs"
