@@ -47,6 +47,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
+constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (fits s_o at D = 64)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -86,7 +87,7 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int OSTR = D + 4;   // padded LDS row stride of the merge buffer (floats)
 
   __shared__ __align__(16) _Float16 s_q[NB * 16 * D];
-  __shared__ __align__(16) float s_sc[kWaves][64];
+  __shared__ __align__(16) float s_sc[kWaves][96];   // K column scale, V scale, mask bias
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ __align__(16) float s_o[kWaves][16 * OSTR];
@@ -154,11 +155,14 @@ void decode_kernel(const DecodeArgs a) {
   }
 
   // Codes of the chunk starting at token c0, through buffer descriptors whose
-  // range ends at row kv_len: the hardware returns zero for any row at or
-  // past kv_len (those tokens are masked), so the sequence's last chunk needs
-  // no clamping and no load can leave the valid rows.
+  // range ends at the split end t_end <= kv_len: the hardware returns zero for
+  // any row at or past it (those tokens are masked) without touching memory.
+  // So no load leaves the valid rows, the last chunk needs no clamping, and a
+  // chunk past the split can be "loaded" unconditionally (all zeros, no
+  // traffic), which keeps the prefetch branch-free: a conditional prefetch
+  // makes the compiler wait for every outstanding load where the paths join.
   auto load_chunk = [&](int c0, ChunkRegs<D>& cr) {
-    const int rows_left = kv_len - c0;
+    const int rows_left = max(t_end - c0, 0);
     const rsrc_t rk = make_rsrc(kbase + (int64_t)c0 * ROWB, rows_left * ROWB);
     const rsrc_t rv = make_rsrc(vbase + (int64_t)c0 * ROWB, rows_left * ROWB);
     const rsrc_t rks = make_rsrc(ksb + c0, rows_left * 2);
@@ -183,113 +187,117 @@ void decode_kernel(const DecodeArgs a) {
 
   const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
   ChunkRegs<D> cur;
-  if (wave < n_chunks) load_chunk(t_begin + wave * kChunk, cur);
+  load_chunk(t_begin + wave * kChunk, cur);
+
+  // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
+  auto process_chunk = [&](int c0, ChunkRegs<D>& cr) {
+      // ---- scales: each lane converts one, the wave reads its eight back.  A
+      //      token at or past the split end gets bias -inf (score masked), so
+      //      the score is one FMA on every chunk, full or not.
+      s_sc[wave][lane] = f16bits_to_f32(lane < 32 ? cr.sk : cr.sv) * sc_mul;
+      if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < t_end) ? 0.0f : -INFINITY;
+      const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
+      const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
+      const float4v sv0 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j]);
+      const float4v sv1 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j + 4]);
+      const float4v mb0 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j]);
+      const float4v mb1 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j + 4]);
+      const float csk[8] = {ck0[0], ck0[1], ck0[2], ck0[3], ck1[0], ck1[1], ck1[2], ck1[3]};
+      const float sv[8] = {sv0[0], sv0[1], sv0[2], sv0[3], sv1[0], sv1[1], sv1[2], sv1[3]};
+      const float mbias[8] = {mb0[0], mb0[1], mb0[2], mb0[3], mb1[0], mb1[1], mb1[2], mb1[3]};
+
+      if constexpr (D == 64) {
+        // lanes 8..15 own nibbles 4..7 of their dword: move them down
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cr.vw[e] = (r >= 8) ? (cr.vw[e] >> 16) : cr.vw[e];
+      }
+
+      // ---- scores S^T for 2 x 16 tokens and every 16-row block; each K operand
+      //      is converted once and used for all row blocks
+      float4v s_t[NB][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const half8v kop = unpack8_perm(cr.kw[kb][kk]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int qrow = nb * 16 + r;
+            const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
+            const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+            s_t[nb][kb] = mfma16x16x32(kop, qop, s_t[nb][kb]);
+          }
+        }
+      }
+
+      // ---- online softmax per row block -> P^T operand (V scale folded in)
+      half8v pop[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float x[8];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = fmaf(s_t[nb][e >> 2][e & 3], csk[e], mbias[e]);
+          mloc = fmaxf(mloc, x[e]);
+        }
+        mloc = xor_max(mloc, 16);
+        mloc = xor_max(mloc, 32);
+        const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
+        const float alpha = fast_exp2(m_run[nb] - m_new);
+        float lsum = 0.0f;
+        uint4v pw;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = fast_exp2(x[e] - m_new);
+          const float p1 = fast_exp2(x[e + 1] - m_new);
+          lsum += p0 + p1;
+          pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
+        }
+        pop[nb] = bitcast<half8v>(pw);
+        l_run[nb] = l_run[nb] * alpha + lsum;
+        m_run[nb] = m_new;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
+        }
+      }
+
+      // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
+      //      token dwords, low and high nibble -> exact fp16 (token e = k index)
+#pragma unroll
+      for (int k = 0; k < NPB / 2; ++k) {
+        uint4v wlo, whi;
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
+          wlo[hh] = bitcast<uint32_t>(nib_lo_pair(xb));
+          whi[hh] = bitcast<uint32_t>(nib_hi_pair(xb));
+        }
+        const half8v vlo = bitcast<half8v>(wlo);
+        const half8v vhi = bitcast<half8v>(whi);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
+          o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
+        }
+      }
+  };
 
   for (int c = wave; c < n_chunks; c += kWaves) {
     const int c0 = t_begin + c * kChunk;
     // Compiler-only barrier: keeps the query-operand LDS reads inside the loop
     // instead of hoisted into (NB * D / 8) live registers per lane.
     asm volatile("" ::: "memory");
-    ChunkRegs<D> nxt;
     if constexpr (kPrefetch) {
-      if (c + kWaves < n_chunks) load_chunk(c0 + kWaves * kChunk, nxt);
-    }
-
-    // ---- scales: each lane converts one, the wave reads its eight back
-    s_sc[wave][lane] = f16bits_to_f32(lane < 32 ? cur.sk : cur.sv) * sc_mul;
-    const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
-    const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
-    const float4v sv0 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j]);
-    const float4v sv1 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j + 4]);
-    const float csk[8] = {ck0[0], ck0[1], ck0[2], ck0[3], ck1[0], ck1[1], ck1[2], ck1[3]};
-    const float sv[8] = {sv0[0], sv0[1], sv0[2], sv0[3], sv1[0], sv1[1], sv1[2], sv1[3]};
-    const bool full = (c0 + kChunk <= t_end);
-
-    if constexpr (D == 64) {
-      // lanes 8..15 own nibbles 4..7 of their dword: move them down
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cur.vw[e] = (r >= 8) ? (cur.vw[e] >> 16) : cur.vw[e];
-    }
-
-    // ---- scores S^T for 2 x 16 tokens and every 16-row block; each K operand
-    //      is converted once and used for all row blocks
-    float4v s_t[NB][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const half8v kop = unpack8_perm(cur.kw[kb][kk]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int qrow = nb * 16 + r;
-          const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
-          const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
-          s_t[nb][kb] = mfma16x16x32(kop, qop, s_t[nb][kb]);
-        }
-      }
-    }
-
-    // ---- online softmax per row block -> P^T operand (V scale folded in)
-    half8v pop[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float x[8];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = s_t[nb][e >> 2][e & 3] * csk[e];
-        if (!full) v = (c0 + 8 * j + e < t_end) ? v : -INFINITY;
-        x[e] = v;
-        mloc = fmaxf(mloc, v);
-      }
-      mloc = xor_max(mloc, 16);
-      mloc = xor_max(mloc, 32);
-      const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
-      const float alpha = fast_exp2(m_run[nb] - m_new);
-      float lsum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = fast_exp2(x[e] - m_new);
-        const float p1 = fast_exp2(x[e + 1] - m_new);
-        lsum += p0 + p1;
-        const half2v pr = cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]);
-        pop[nb][e] = pr[0];
-        pop[nb][e + 1] = pr[1];
-      }
-      l_run[nb] = l_run[nb] * alpha + lsum;
-      m_run[nb] = m_new;
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
-      }
-    }
-
-    // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
-    //      token dwords, low and high nibble -> exact fp16 (token e = k index)
-#pragma unroll
-    for (int k = 0; k < NPB / 2; ++k) {
-      half8v vlo, vhi;
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const uint32_t xb = pair_bytes(cur.vw[2 * hh], cur.vw[2 * hh + 1], k);
-        const half2v lo = nib_lo_pair(xb);
-        const half2v hi = nib_hi_pair(xb);
-        vlo[2 * hh] = lo[0];
-        vlo[2 * hh + 1] = lo[1];
-        vhi[2 * hh] = hi[0];
-        vhi[2 * hh + 1] = hi[1];
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
-        o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
-      }
-    }
-    if constexpr (kPrefetch) {
+      ChunkRegs<D> nxt;
+      load_chunk(c0 + kWaves * kChunk, nxt);
+      process_chunk(c0, cur);
       cur = nxt;
-    } else if (c + kWaves < n_chunks) {
+    } else {
+      process_chunk(c0, cur);
       load_chunk(c0 + kWaves * kChunk, cur);
     }
   }
@@ -375,27 +383,76 @@ void decode_kernel(const DecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
   const int n_split = a.n_split;
+  // (1) every split's LSE of this group -> LDS (the wave-merge buffer is free
+  //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
+  float* s_w = &s_o[0][0];
+  __shared__ float s_den[64];
+  {
+    const int total = R * n_split;
+    for (int base = threadIdx.x; base < total; base += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 256;
+        v[u] = -INFINITY;
+        if (idx < total) {
+          const int row = idx / n_split;
+          const int hg = row / Sq;
+          const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+          v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_split), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (base + u * 256 < total) s_w[base + u * 256] = v[u];
+    }
+  }
+  __syncthreads();
+  // (2) per row: max, weights 2^(lse_s - max) (in place), their sum -- one wave per row
+  for (int row = wave; row < R; row += kWaves) {
+    float* wr = s_w + row * n_split;
+    float M = -INFINITY;
+    for (int s = lane; s < n_split; s += 64) M = fmaxf(M, wr[s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
+    float den = 0.0f;
+    for (int s = lane; s < n_split; s += 64) {
+      const float w = fast_exp2(wr[s] - M);
+      wr[s] = w;
+      den += w;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
+    if (lane == 0) {
+      s_den[row] = den;
+      const int hg = row / Sq;
+      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+      if (a.lse) a.lse[grow] = (M + log2f(den)) * kLn2;
+    }
+  }
+  __syncthreads();
+  // (3) O = sum_s w_s O_s / sum_s w_s, eight partial loads in flight per thread
   for (int idx = threadIdx.x; idx < R * (D / 4); idx += 256) {
     const int row = idx / (D / 4);
     const int d = 4 * (idx - row * (D / 4));
     const int hg = row / Sq;
-    const int sq = row - hg * Sq;
-    const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + sq;
-    const float* pl = a.part_lse + grow * n_split;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s)
-      M = fmaxf(M, __hip_atomic_load(pl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+    const float* wr = s_w + row * n_split;
+    const uint32_t off0 = (uint32_t)((grow * n_split * D + d) * 4);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-      const float w = fast_exp2(__hip_atomic_load(pl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-      const float4v o = __builtin_amdgcn_raw_buffer_load_b128(
-          rpart, (uint32_t)(((grow * n_split + s) * D + d) * 4), 0, kCoherent);
-      acc += w * o;
-      den += w;
+    for (int s0 = 0; s0 < n_split; s0 += 8) {
+      float4v o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        o[u] = (s0 + u < n_split)
+                   ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
+                   : float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < n_split) acc += wr[s0 + u] * o[u];
     }
-    *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (1.0f / den);
-    if (d == 0 && a.lse) a.lse[grow] = (M + log2f(den)) * kLn2;
+    *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (1.0f / s_den[row]);
   }
   if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -432,6 +489,9 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
   }
   if (ns > chunks) ns = chunks;
   if (ns > 1024) ns = 1024;
+  // the merging workgroup keeps (rows per group) * ns weights in LDS
+  const int64_t rpg = rows / units;
+  if (ns > kMaxMergeLse / rpg) ns = kMaxMergeLse / rpg;
   // partial outputs (rows * ns * D fp32) are addressed with 32-bit offsets
   const int64_t max_ns_bytes = ((int64_t)1 << 31) / ((int64_t)rows * D * 4 + 1);
   if (ns > max_ns_bytes) ns = max_ns_bytes;

@@ -55,14 +55,12 @@ __device__ __forceinline__ half2v nib_hi_pair(uint32_t x) {
 // values in the order [c0, c4, c1, c5, c2, c6, c3, c7].  The matching query
 // operand is permuted the same way (a dot product is order-invariant).
 __device__ __forceinline__ half8v unpack8_perm(uint32_t x) {
-  const half2v a = nib_lo_pair(x);        // c0, c4
-  const half2v b = nib_hi_pair(x);        // c1, c5
-  const half2v c = nib_lo_pair(x >> 8);   // c2, c6
-  const half2v d = nib_hi_pair(x >> 8);   // c3, c7
-  half8v r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
+  uint4v w;
+  w[0] = bitcast<uint32_t>(nib_lo_pair(x));        // c0, c4
+  w[1] = bitcast<uint32_t>(nib_hi_pair(x));        // c1, c5
+  w[2] = bitcast<uint32_t>(nib_lo_pair(x >> 8));   // c2, c6
+  w[3] = bitcast<uint32_t>(nib_hi_pair(x >> 8));   // c3, c7
+  return bitcast<half8v>(w);
 }
 
 // Position of packed element e (0..7) in the unpack8_perm order, and back.
