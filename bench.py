@@ -2,11 +2,14 @@
 
 One step = one decode step of the Llama-3-8B shaped GQA decode workload
 (B=16, 32 query / 8 KV heads, D=128, 8192 cached tokens): quantize-and-append
-the new token's K and V rows, then split-K decode attention of the query over
-the whole cache (quantizer, exact int4 -> fp16 conversion, MFMA QK^T and PV,
-online softmax, LSE merge).  Inputs are resident in HBM before timing starts;
-the cache is rotated over several independent copies so that the 256 MB
-Infinity Cache cannot serve repeated reads.
+the new token's K and V rows (one launch), then split-K decode attention of
+the query over the whole cache (exact int4 -> fp16 conversion, MFMA QK^T and
+PV, online softmax, LSE merge; one launch).  Inputs are resident in HBM
+before timing starts; the cache is rotated over several independent copies
+so that the 256 MB Infinity Cache cannot serve repeated reads.  Timed
+launches are queued behind a GPU hold so that host-side Python launch
+overhead is excluded (the GPU runs them back to back, as a captured graph
+would).
 
 Printed (stdout, one JSON line): the headline decode throughput in GB/s of
 packed KV bytes (codes + scales) per step, the roofline of the decode kernel
@@ -44,12 +47,14 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter-derived traffic is valid only for these."""
+    """Hash of what the decode kernel is built from (its source, the shared
+    device header, the split planner's inputs and the compiler flags):
+    counter-derived traffic is valid only for exactly these."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "quantized_kv_flashattention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    pkg = os.path.join(ROOT, "quantized_kv_flashattention_amd")
+    for rel in ("csrc/decode.hip", "csrc/qkvfa_device.hpp", "csrc/qkvfa_internal.h", "csrc/api.cpp", "build.py"):
+        with open(os.path.join(pkg, rel), "rb") as f:
+            h.update(rel.encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -82,10 +87,44 @@ def upload_cache(torch, qkv, k, v, n_copies):
     return caches
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_gpu(torch, ms):
+    """Queue a GPU spin of about `ms` milliseconds on the current stream.
+
+    Launches enqueued behind it pile up while it runs, so the timed kernels
+    run back to back and the host's per-launch Python overhead (tens of us,
+    comparable to a decode kernel) is not measured -- as with a captured
+    graph.  The spin's rate is calibrated once with events."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
+
+
+def host_enqueue_ms(fn, n):
+    """Host time to enqueue n calls of fn (no synchronization)."""
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    return (time.perf_counter() - t0) * 1e3
+
+
 def per_launch_ms(torch, fn, n, rotate):
-    """Average duration of fn(i) measured with events recorded around each launch."""
+    """Average duration of fn(i) measured with HIP events recorded around each
+    launch on the launch stream, with the launches queued behind a GPU hold."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    enq = host_enqueue_ms(lambda i: fn(i % rotate), 4)
+    torch.cuda.synchronize()
+    hold_gpu(torch, 2.0 * enq / 4 * n + 1.0)
     for i in range(n):
         starts[i].record()
         fn(i % rotate)
@@ -130,15 +169,17 @@ def bench_decode(torch, qkv, w, steps, warmup, with_append):
     def step(i):
         c = caches[i]
         if with_append:
-            qkv.quantize_append(k_new, c.k_codes, c.k_scales, w.L - 1)
-            qkv.quantize_append(v_new, c.v_codes, c.v_scales, w.L - 1)
+            qkv.quantize_append_kv(k_new, v_new, c, w.L - 1)   # the new token's K and V rows
         decode_only(i)
 
     for i in range(warmup):
         step(i % n_copies)
     torch.cuda.synchronize()
+    enq = host_enqueue_ms(lambda i: step(i % n_copies), 4) / 4
+    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    hold_gpu(torch, 2.0 * enq * steps + 1.0)
     e0.record()
     for i in range(steps):
         step(i % n_copies)
@@ -239,6 +280,85 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def profile_target(target: str, iters: int):
+    """Run one kernel `iters` times (for rocprofv3 counter passes) and exit."""
+    import torch
+    import quantized_kv_flashattention_amd as qkv
+    from qkv_inputs import make_qkv, workload
+    torch.cuda.set_device(0)
+    if target == "copy":
+        # plain device copy of known size: calibrates FETCH_SIZE / WRITE_SIZE
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(iters):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
+    w = workload({"decode": "llama3_8b_decode", "long": "long_context_decode"}[target])
+    q_bits, k, v = make_qkv(w)
+    caches = upload_cache(torch, qkv, k, v, max(4, math.ceil(2.5 * MALL_BYTES / decode_bytes(w)[0])))
+    del k, v
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    for i in range(iters):
+        qkv.decode(q, caches[i % len(caches)], w.L, softmax_scale=w.softmax_scale, out=out)
+    torch.cuda.synchronize()
+
+
+COPY_BYTES = 1 << 30
+
+
+def _counter_per_dispatch(path_dir: str, counter: str, name_re: str):
+    """Average value of `counter` per dispatch of kernels matching name_re (KiB)."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(path_dir, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter or not re.search(name_re, r["Kernel_Name"]):
+                    continue
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    vals = [per[k] for k in sorted(per, key=int)]
+    if len(vals) > 4:
+        vals = vals[2:]          # skip first dispatches (cold caches, page mapping)
+    return (sum(vals) / len(vals)) if vals else None, len(vals)
+
+
+def summarize_profiles(root: str):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes into HBM bytes per
+    decode launch.  Expects <root>/{fetch,write}_{decode,copy}/ outputs."""
+    fc, nfc = _counter_per_dispatch(os.path.join(root, "fetch_copy"), "FETCH_SIZE", "copyBuffer|copy")
+    wc, nwc = _counter_per_dispatch(os.path.join(root, "write_copy"), "WRITE_SIZE", "copyBuffer|copy")
+    fd, nfd = _counter_per_dispatch(os.path.join(root, "fetch_decode"), "FETCH_SIZE", "decode_kernel")
+    wd, nwd = _counter_per_dispatch(os.path.join(root, "write_decode"), "WRITE_SIZE", "decode_kernel")
+    if None in (fc, wc, fd, wd):
+        raise SystemExit(f"missing counter data: {fc} {wc} {fd} {wd}")
+    f_scale = fc * 1024 / COPY_BYTES     # counter bytes per true byte, reads
+    w_scale = wc * 1024 / COPY_BYTES     # same, writes
+    from qkv_inputs import workload
+    w = workload("llama3_8b_decode")
+    alg = decode_bytes(w)[1]
+    read_b = fd * 1024 / f_scale
+    write_b = wd * 1024 / w_scale
+    result = {
+        "source_hash": kernel_source_hash(),
+        "copy_calibration": {"bytes_copied": COPY_BYTES, "fetch_kib": fc, "write_kib": wc,
+                             "fetch_scale": f_scale, "write_scale": w_scale, "dispatches": [nfc, nwc]},
+        "kernels": {"decode_llama3_8b": {
+            "fetch_kib_raw": fd, "write_kib_raw": wd, "dispatches": [nfd, nwd],
+            "read_bytes": read_b, "write_bytes": write_b,
+            "bytes_per_launch": read_b + write_b, "algorithmic_bytes": alg,
+            "traffic_over_algorithmic": (read_b + write_b) / alg}},
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(result, f, indent=1)
+    print(json.dumps(result, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +366,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "headline", "decode", "prefill"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--profile-target", choices=["decode", "long", "copy"], default=None,
+                    help="run one kernel repeatedly for rocprofv3 counter passes, print nothing")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
+    if args.profile_target:
+        profile_target(args.profile_target, 20)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(use --gpus 1).", file=sys.stderr)

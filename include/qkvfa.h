@@ -90,6 +90,21 @@ qkv_status qkv_quantize_append(const float* src, uint8_t* codes, uint16_t* scale
                                int64_t C, int64_t pos, void* stream);
 
 /*
+ * (a') The same quantize-and-append for K and V of the same T tokens in one
+ * launch (a decode step appends k_t and v_t together, TurboAttention §2.1).
+ * Results are identical to two qkv_quantize_append calls.
+ *   k_src, v_src      float [B, Hkv, T, D], device, 16-byte aligned
+ *   k_codes, v_codes  uint8 [B, Hkv, C, D/2], device, 16-byte aligned (written)
+ *   k_scales, v_scales uint16 [B, Hkv, C], device, 2-byte aligned (written)
+ * Same requirements as qkv_quantize_append.
+ */
+qkv_status qkv_quantize_append_kv(const float* k_src, const float* v_src,
+                                  uint8_t* k_codes, uint16_t* k_scales,
+                                  uint8_t* v_codes, uint16_t* v_scales,
+                                  int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                                  int64_t C, int64_t pos, void* stream);
+
+/*
  * (b) Decode attention: each of the Sq query rows of every (batch, head)
  * attends cache rows [0, kv_len) with no mask (append-then-attend,
  * TurboAttention §2.1).  The KV length is split into `num_splits` ranges

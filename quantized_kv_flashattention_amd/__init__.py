@@ -26,6 +26,7 @@ __all__ = [
     "QKVError",
     "KVCache",
     "quantize_append",
+    "quantize_append_kv",
     "decode",
     "prefill",
     "decode_workspace_bytes",
@@ -49,7 +50,7 @@ class QKVError(RuntimeError):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m quantized_kv_flashattention_amd.build`")
+            f"{_LIB_PATH} is missing: build it with `python quantized_kv_flashattention_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     lib.qkv_status_string.restype = ctypes.c_char_p
@@ -60,6 +61,8 @@ def _load():
     lib.qkv_version.argtypes = []
     lib.qkv_quantize_append.restype = ci
     lib.qkv_quantize_append.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    lib.qkv_quantize_append_kv.restype = ci
+    lib.qkv_quantize_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
     lib.qkv_decode_workspace_bytes.restype = sz
     lib.qkv_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
     lib.qkv_decode_auto_splits.restype = ci
@@ -147,6 +150,26 @@ def quantize_append(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
     C = codes.shape[2]
     _check(_lib.qkv_quantize_append(_ptr(src), _ptr(codes), _ptr(scales), B, Hkv, T, D, C, int(pos),
                                     _stream(src)))
+
+
+def quantize_append_kv(k_src: torch.Tensor, v_src: torch.Tensor, cache: "KVCache", pos: int):
+    """Quantize new K and V rows ``[B, Hkv, T, D]`` into cache rows ``[pos, pos+T)`` in one launch."""
+    _req(k_src, "k_src", torch.float32, 4)
+    _req(v_src, "v_src", torch.float32, 4)
+    if k_src.shape != v_src.shape or k_src.device != v_src.device:
+        raise ValueError("k_src and v_src must have one shape and device")
+    kc, ks, vc, vs = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+        if t.device != k_src.device:
+            raise ValueError("all tensors must be on one device")
+    B, Hkv, T, D = k_src.shape
+    if kc.shape[:2] != (B, Hkv) or kc.shape[3] * 2 != D or vc.shape != kc.shape or \
+            ks.shape != kc.shape[:3] or vs.shape != ks.shape:
+        raise ValueError("cache shape does not match src")
+    _check(_lib.qkv_quantize_append_kv(_ptr(k_src), _ptr(v_src), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                       B, Hkv, T, D, kc.shape[2], int(pos), _stream(k_src)))
 
 
 def _attn_args(q, cache_tensors, kv_len):

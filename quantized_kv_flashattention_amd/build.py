@@ -1,6 +1,7 @@
 """Build libqkvfa.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
 
-Usage: ``python -m quantized_kv_flashattention_amd.build`` (or call ``build()``).
+Usage: ``python quantized_kv_flashattention_amd/build.py`` (or call ``build()``).
+Run it by path: importing the package loads the library it builds.
 """
 from __future__ import annotations
 

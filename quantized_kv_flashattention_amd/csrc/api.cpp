@@ -100,9 +100,34 @@ qkv_status qkv_quantize_append(const float* src, uint8_t* codes, uint16_t* scale
     return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append: misaligned pointer");
   if (B * Hkv > 0x7FFFFFFFll)
     return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append: B * Hkv too large");
-  return hip_status(qkvfa::launch_quantize_append(src, codes, scales, B * Hkv, T, (int)D, C, pos,
+  return hip_status(qkvfa::launch_quantize_append(src, codes, scales, nullptr, nullptr, nullptr,
+                                                  B * Hkv, T, (int)D, C, pos,
                                                   static_cast<hipStream_t>(stream)),
                     "qkv_quantize_append");
+}
+
+qkv_status qkv_quantize_append_kv(const float* k_src, const float* v_src, uint8_t* k_codes,
+                                  uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                                  int64_t B, int64_t Hkv, int64_t T, int64_t D, int64_t C,
+                                  int64_t pos, void* stream) {
+  if (B < 1 || Hkv < 1 || T < 0 || C < 1)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv: need B, Hkv, C >= 1 and T >= 0");
+  if (D != 64 && D != 128)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append_kv: head dim must be 64 or 128");
+  if (pos < 0 || pos + T > C)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv: need 0 <= pos and pos + T <= C");
+  if (T == 0) return QKV_OK;
+  if (!k_src || !v_src || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv: null tensor pointer");
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 2) || !aligned(v_scales, 2))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv: misaligned pointer");
+  if (B * Hkv > 0x3FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append_kv: B * Hkv too large");
+  return hip_status(qkvfa::launch_quantize_append(k_src, k_codes, k_scales, v_src, v_codes, v_scales,
+                                                  B * Hkv, T, (int)D, C, pos,
+                                                  static_cast<hipStream_t>(stream)),
+                    "qkv_quantize_append_kv");
 }
 
 int qkv_decode_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,

@@ -432,7 +432,7 @@ void decode_kernel(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  // (3) O = sum_s w_s O_s / sum_s w_s, eight partial loads in flight per thread
+  // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per thread
   for (int idx = threadIdx.x; idx < R * (D / 4); idx += 256) {
     const int row = idx / (D / 4);
     const int d = 4 * (idx - row * (D / 4));
@@ -441,15 +441,15 @@ void decode_kernel(const DecodeArgs a) {
     const float* wr = s_w + row * n_split;
     const uint32_t off0 = (uint32_t)((grow * n_split * D + d) * 4);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_split; s0 += 8) {
-      float4v o[8];
+    for (int s0 = 0; s0 < n_split; s0 += 16) {
+      float4v o[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         o[u] = (s0 + u < n_split)
                    ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
                    : float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (s0 + u < n_split) acc += wr[s0 + u] * o[u];
     }
     *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (1.0f / s_den[row]);
@@ -480,7 +480,10 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
   const int64_t units = B * Hkv;
   int64_t ns;
   if (num_splits <= 0) {
-    const int64_t target_wgs = 4 * (int64_t)(num_cus > 0 ? num_cus : 256);
+    // about two workgroups (eight waves) per CU: measured best on MI355X for
+    // both a 128-group 8K-token and an 8-group 128K-token decode; more splits
+    // add per-split epilogue and merge work without adding bandwidth
+    const int64_t target_wgs = 2 * (int64_t)(num_cus > 0 ? num_cus : 256);
     ns = (target_wgs + units - 1) / units;
     const int64_t max_ns = chunks / kWaves > 0 ? chunks / kWaves : 1;   // >= one chunk per wave
     if (ns > max_ns) ns = max_ns;

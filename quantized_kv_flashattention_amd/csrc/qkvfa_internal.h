@@ -7,7 +7,9 @@
 
 namespace qkvfa {
 
+// Quantize one tensor (src2 == nullptr) or two tensors of the same shape in one launch.
 hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,
+                                  const float* src2, uint8_t* codes2, uint16_t* scales2,
                                   int64_t BH, int64_t T, int D, int64_t C, int64_t pos,
                                   hipStream_t stream);
 

@@ -22,14 +22,27 @@
 
 namespace qkvfa {
 
+// One launch may quantize two tensors (K and V of the same tokens): blocks
+// [0, nblk) take the first, blocks [nblk, 2 nblk) the second.
+struct QuantTarget {
+  const float* src;
+  uint8_t* codes;
+  uint16_t* scales;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void quantize_append_kernel(
-    const float* __restrict__ src, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-    int64_t T, int64_t C, int64_t pos, uint32_t tblocks) {
+__global__ __launch_bounds__(256) void quantize_append_kernel(QuantTarget t0, QuantTarget t1,
+                                                              uint32_t nblk, int64_t T, int64_t C,
+                                                              int64_t pos, uint32_t tblocks) {
   constexpr int TPR = D / 8;          // threads per row
   constexpr int RPB = 256 / TPR;      // rows per block
-  const uint32_t bh = blockIdx.x / tblocks;
-  const uint32_t tb = blockIdx.x - bh * tblocks;
+  const bool second = blockIdx.x >= nblk;
+  const uint32_t blk = second ? blockIdx.x - nblk : blockIdx.x;
+  const float* __restrict__ src = second ? t1.src : t0.src;
+  uint8_t* __restrict__ codes = second ? t1.codes : t0.codes;
+  uint16_t* __restrict__ scales = second ? t1.scales : t0.scales;
+  const uint32_t bh = blk / tblocks;
+  const uint32_t tb = blk - bh * tblocks;
   const int sub = threadIdx.x % TPR;
   const int64_t t = (int64_t)tb * RPB + threadIdx.x / TPR;
   if (t >= T) return;  // whole TPR-lane groups leave together
@@ -62,19 +75,24 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
 }
 
 hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,
+                                  const float* src2, uint8_t* codes2, uint16_t* scales2,
                                   int64_t BH, int64_t T, int D, int64_t C, int64_t pos,
                                   hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int rpb = 256 / (D / 8);
   const int64_t tblocks = (T + rpb - 1) / rpb;
-  const int64_t grid = BH * tblocks;
-  if (grid > 0x7FFFFFFF || tblocks > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  const int64_t nblk = BH * tblocks;
+  const int ntensors = src2 ? 2 : 1;
+  if (nblk * ntensors > 0x7FFFFFFF || tblocks > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  const QuantTarget t0 = {src, codes, scales};
+  const QuantTarget t1 = src2 ? QuantTarget{src2, codes2, scales2} : t0;
+  const dim3 grid((uint32_t)(nblk * ntensors));
   if (D == 128) {
-    quantize_append_kernel<128><<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
-        src, codes, scales, T, C, pos, (uint32_t)tblocks);
+    quantize_append_kernel<128><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, C, pos,
+                                                                (uint32_t)tblocks);
   } else {
-    quantize_append_kernel<64><<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
-        src, codes, scales, T, C, pos, (uint32_t)tblocks);
+    quantize_append_kernel<64><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, C, pos,
+                                                               (uint32_t)tblocks);
   }
   return hipGetLastError();
 }

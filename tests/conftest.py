@@ -14,8 +14,12 @@ def pytest_configure(config):
     lib = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")
     if not os.path.exists(lib):
         # nothing built yet: build once (hipcc cross-compiles without a GPU)
-        from quantized_kv_flashattention_amd.build import build
-        build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "qkvfa_build", os.path.join(ROOT, "quantized_kv_flashattention_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 def _gpu_available():

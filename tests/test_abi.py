@@ -13,12 +13,11 @@ LIB = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(LIB):
-        from quantized_kv_flashattention_amd.build import build
-        build()
+    assert os.path.exists(LIB), "libqkvfa.so is not built (conftest builds it when missing)"
     L = ctypes.CDLL(LIB)
     i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     L.qkv_quantize_append.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    L.qkv_quantize_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
     L.qkv_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp, sz, vp]
     L.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp]
     L.qkv_last_error.restype = ctypes.c_char_p
@@ -116,3 +115,15 @@ def test_prefill_argument_errors(lib):
     assert _pre(lib, Hkv=3) == 1
     assert _pre(lib, lse=P + 2) == 1
     assert _pre(lib, kc=P + 8) == 1
+
+
+def test_quantize_append_kv_argument_errors(lib):
+    f = lambda **kw: lib.qkv_quantize_append_kv(*(kw.get(n, P) for n in ("ks_", "vs_", "kc", "kss", "vc", "vss")),
+                                                kw.get("B", 1), 1, kw.get("T", 4), kw.get("D", 64), 8,
+                                                kw.get("pos", 0), None)
+    assert f(D=32) == 2
+    assert f(pos=6) == 1
+    assert f(vs_=None) == 1
+    assert f(kc=P + 2) == 1
+    assert f(B=0) == 1
+    assert f(T=0, vs_=None) == 0

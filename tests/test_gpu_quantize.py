@@ -108,3 +108,25 @@ def test_full_size_workloads(index):
         torch.cuda.synchronize()
         assert np.array_equal(codes.cpu().numpy(), rc)
         assert np.array_equal(scales.view(torch.int16).cpu().numpy().view(np.uint16), rs)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T,C,pos", [(1, 9, 8), (300, 310, 5)])
+def test_append_kv_matches_two_appends(D, T, C, pos):
+    rng = np.random.default_rng(T * D)
+    k = rng.standard_normal((3, 2, T, D)).astype(np.float32)
+    v = (rng.standard_normal((3, 2, T, D)) * 3).astype(np.float32)
+    cache = qkv.KVCache(*(torch.full(s, f, dtype=dt, device=DEV) for s, f, dt in (
+        ((3, 2, C, D // 2), 0xA5, torch.uint8), ((3, 2, C), 1.5, torch.float16),
+        ((3, 2, C, D // 2), 0x5A, torch.uint8), ((3, 2, C), -2.5, torch.float16))))
+    qkv.quantize_append_kv(torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV), cache, pos)
+    torch.cuda.synchronize()
+    for src, codes, scales, fill_c, fill_s in ((k, cache.k_codes, cache.k_scales, 0xA5, 1.5),
+                                               (v, cache.v_codes, cache.v_scales, 0x5A, -2.5)):
+        rc, rs = oracle.quantize_rows(src)
+        c = codes.cpu().numpy()
+        s = scales.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(c[:, :, pos:pos + T], rc) and np.array_equal(s[:, :, pos:pos + T], rs)
+        assert np.all(c[:, :, :pos] == fill_c) and np.all(c[:, :, pos + T:] == fill_c)
+        fs = np.float16(fill_s).view(np.uint16)
+        assert np.all(s[:, :, :pos] == fs) and np.all(s[:, :, pos + T:] == fs)
