@@ -294,6 +294,17 @@ def profile_target(target: str, iters: int):
             dst.copy_(src)
         torch.cuda.synchronize()
         return
+    if target == "prefill":
+        w = workload("causal_prefill_16k")
+        q_bits, k, v = make_qkv(w)
+        cache = upload_cache(torch, qkv, k, v, 1)[0]
+        del k, v
+        q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+        out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+        for _ in range(max(iters // 4, 3)):
+            qkv.prefill(q, cache, w.L, True, softmax_scale=w.softmax_scale, out=out)
+        torch.cuda.synchronize()
+        return
     w = workload({"decode": "llama3_8b_decode", "long": "long_context_decode"}[target])
     q_bits, k, v = make_qkv(w)
     caches = upload_cache(torch, qkv, k, v, max(4, math.ceil(2.5 * MALL_BYTES / decode_bytes(w)[0])))
@@ -366,7 +377,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "headline", "decode", "prefill"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--profile-target", choices=["decode", "long", "copy"], default=None,
+    ap.add_argument("--profile-target", choices=["decode", "long", "prefill", "copy"], default=None,
                     help="run one kernel repeatedly for rocprofv3 counter passes, print nothing")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")
