@@ -181,6 +181,8 @@ qkv_status qkv_prefill(const uint16_t* q, const uint8_t* k_codes, const uint16_t
     return fail(QKV_ERR_INVALID_ARG, "qkv_prefill: causal attention needs Sq <= kv_len");
   if ((Sq + 127) / 128 > 0xFFFF)
     return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill: too many query blocks");
+  if (kv_len * (D / 2) > 0x7FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill: kv_len * D / 2 must stay below 2^31 bytes");
   return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
                                           kv_len, C, (int)D, softmax_scale, causal, out, lse,
                                           static_cast<hipStream_t>(stream)),

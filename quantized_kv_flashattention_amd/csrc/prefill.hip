@@ -1,27 +1,64 @@
 // Tiled prefill attention over an int4 KV cache, causal or not.
 //
 // FlashAttention tiling with online softmax (TurboAttention arXiv 2412.08585
-// §2.2): a workgroup owns 128 query rows of one head (4 waves x 32 rows) and
-// walks the key axis in tiles of 64 tokens.  For each tile the workgroup
+// §2.2): a workgroup owns 32 NW query rows of one head (NW waves x 32 rows)
+// and walks the key axis in tiles of 64 tokens.  For each tile the workgroup
 // loads the packed int4 K/V codes (8 KB at D = 128, the "quantized KV 8 KB +
-// 256 B scales" tile of "Quantized Cross-Attention ..." §3.2) and converts
-// them exactly to fp16 into LDS, where all four waves share them; the codes
-// are never dequantized to HBM (same page §3.1).  Scales stay per token: the
-// K scale multiplies score columns, the V scale is folded into P (§3.4 in
-// the reading that keeps the result exact).
+// 256 B scales" tile of "Quantized Cross-Attention: Extending
+// FlashAttention-3 with In-SRAM Dequantization" §3.2) and converts them
+// exactly to fp16 in LDS, where all NW waves share them; codes are never
+// dequantized to HBM (same page §3.1).  Scales stay per token: the K scale
+// times softmax_scale * log2(e) multiplies score columns in fp32, the V scale
+// is folded into P before its one fp16 rounding (§3.4 in the reading that
+// keeps the result exact).  Folding either scale into fp16 K/V values instead
+// would add one fp16 rounding per element, which large-magnitude channels
+// turn into score errors above the attention tolerance.
 //
 // Contractions use v_mfma_f32_32x32x16_f16 in transposed form:
 //   S^T = K Q^T   (M = 32 tokens, N = 32 query rows, K = 16 head dims)
 //   O^T += V^T P^T (M = 32 head dims, N = 32 query rows, K = 16 tokens)
-// so every lane owns one query row: its 32 scores of a tile need a single
-// cross-lane step for the row max, and its probabilities are already in the
-// B-operand position of the PV product.
+// so every lane owns one query row: its 32 scores of a tile are already in
+// the B-operand position of the PV product.  Q (bf16) converts exactly to
+// fp16; scores are kept in log2 units.
+//
+// The matrix work hides behind the vector work here (dequantization,
+// exponentials, scale products), so the kernel is organised to issue as few
+// VALU instructions per tile as it can:
+//  * the conversion of a tile is shared by all NW waves;
+//  * online softmax keeps a per-row reference m_ref and rescales only when a
+//    tile may exceed it by more than kTau (base-2 exponent).  On full tiles the
+//    test uses an upper bound, max|s| x max|csk| of the tile, so the common
+//    tile needs no per-score product before the exponent: p = exp2(s csk -
+//    m_ref) is one fma.  Probabilities stay below 2^kTau, far inside fp16
+//    range, and the final normalisation by l = sum(p) is unaffected;
+//  * P~ = fp16(p x s_V) is one v_fma_mix per value with s_V read as fp16.
+//
+// Pipeline: LDS is double buffered.  While a wave computes on tile kt it
+// converts tile kt+1 (loaded into registers one iteration earlier) into the
+// other buffer and issues the loads of tile kt+2; one barrier per tile.
+// Loads go through buffer descriptors whose range ends at kv_len, so the
+// ragged last tile and the look-ahead past the last tile read zeros.
 //
 // Causal (bottom-right aligned, row i sees keys <= i + kv_len - Sq): key tiles
-// beyond the last visible key of a workgroup are never loaded; only tiles
+// beyond the last visible key of a workgroup are never used; only tiles
 // crossing the diagonal (or the ragged end of the keys) evaluate the mask;
 // waves whose rows see nothing of a tile skip its math.  Workgroups are
 // dispatched longest-first (highest query block first).
+//
+// LDS layouts (one buffer):
+//   K: fp16 16-byte chunk planes: chunk c (head dims 8c..8c+7 in
+//      unpack8_perm order) of token t at [c][t][8].  The QK reads of 16
+//      consecutive tokens and the conversion writes of 64 consecutive tokens
+//      both cover whole 256-byte bank rows.
+//   V: fp16 transposed, 8-token planes: plane P holds tokens 4u..4u+3 (h = 0)
+//      and 4(u+2)..4(u+2)+3 (h = 1) with u = 8 tb + 4 kp + j,
+//      P = 4 tb + 2 kp + j, i.e. exactly the 8 keys one lane feeds to one PV
+//      MFMA; head dim d sits at row d ^ ((d >> 4) & 7) of its plane.  The
+//      swizzle makes both the PV reads (16 consecutive d) and the conversion
+//      writes (d = 8 i + n) hit distinct banks.
+//   scales: fp32 K scale x softmax_scale x log2(e) per token; fp16 V scale
+//      ordered [j][tb][vq][i] for token 32 tb + 8 vq + 4 j + i, so a lane
+//      reads the 32 V scales of its tokens as four 16-byte loads.
 #include <math.h>
 
 #include "qkvfa_device.hpp"
@@ -31,34 +68,56 @@ namespace qkvfa {
 
 namespace {
 
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per tile
+constexpr int BN = 64;        // keys per tile
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void prefill_kernel(
+// Maximum over the 64 lanes of a wave of a non-negative float (the integer
+// order of the bit patterns is the float order for non-negative values),
+// returned uniformly.  Prefix maxima inside each 16-lane row, then the row
+// broadcasts carry them across rows; lane 63 ends with the wave maximum.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  int v = bitcast<int>(x);
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
+}
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
     const uint16_t* __restrict__ vs, int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C,
     float qk_log2, int nqb, float* __restrict__ out, float* __restrict__ lse_out) {
+  constexpr int BM = 32 * NW;  // query rows per workgroup
   constexpr int KS = D / 16;   // QK k-steps
   constexpr int NDB = D / 32;  // PV output blocks
-  constexpr int NCH = D / 8;   // 16-byte chunks per LDS K row
+  constexpr int NCH = D / 8;   // K chunk planes
   constexpr int ROWB = D / 2;  // bytes per packed row
+  constexpr int KPL = BN * 8;  // halves per K chunk plane
+  constexpr int VPL = D * 8;   // halves per V 8-token plane
+  constexpr int KBUF = NCH * KPL;
+  constexpr int VBUF = 8 * VPL;
+  constexpr int KDW = ROWB / (4 * NW);   // K code dwords per thread and tile
+  constexpr int VT = D / (8 * NW);       // V tokens (x one code dword) per thread
+  static_assert(KDW >= 1 && KDW <= 4 && (VT == 2 || VT == 4), "unsupported D / NW");
 
-  // K tile: [token][D] fp16, chunk c of token t stored at chunk c ^ (t % NCH).
-  // V tile: transposed [D][BN] fp16, 4-token unit u of row d stored at u ^ (d % 16).
-  __shared__ __align__(16) _Float16 s_k[BN * D];
-  __shared__ __align__(16) _Float16 s_v[D * BN];
-  __shared__ __align__(16) float s_csk[BN];
-  __shared__ __align__(16) float s_sv[BN];
+  __shared__ __align__(16) _Float16 s_k[2 * KBUF];
+  __shared__ __align__(16) _Float16 s_v[2 * VBUF];
+  __shared__ __align__(16) float s_csk[2][BN];     // K scale x qk_log2
+  __shared__ __align__(16) _Float16 s_svh[2][BN];  // V scale, [j][tb][vq][i]
+  __shared__ float s_cmax[2];                      // max |csk| of the tile
+  __shared__ __align__(16) float s_ones[BN];
 
   const int h = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / G;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31;
   const int j = lane >> 5;
   const int q0 = qb * BM;
@@ -75,7 +134,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const bool wave_active = wrow_lo < Sq;
 
   // Query operand (B of S^T = K Q^T): row qrow, k = 8j + e <-> head dim
-  // 8 * (2 ks + j) + perm8(e), matching the LDS K chunk 2 ks + j.
+  // 8 (2 s + j) + perm8(e), matching K chunk plane 2 s + j.
   half8v qop[KS];
   if (qrow < Sq) {
     const uint16_t* qr = q + (((int64_t)b * Hq + h) * Sq + qrow) * D;
@@ -99,176 +158,248 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   float16v o_acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o_acc[db] = float16v{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  float m_ref = -INFINITY;  // row reference (log2 units), shared by lanes r and r + 32
+  float m_use = 0.0f;       // m_ref, or 0 while the row has seen no key
+  float l_run = 0.0f;       // this lane's share of sum(p), relative to m_ref
 
   const int64_t kvrow0 = ((int64_t)b * Hkv + g) * C;
-  const uint8_t* kbase = kc + kvrow0 * ROWB;
-  const uint8_t* vbase = vc + kvrow0 * ROWB;
+  const rsrc_t rk = make_rsrc(kc + kvrow0 * ROWB, kv_len * ROWB);
+  const rsrc_t rv = make_rsrc(vc + kvrow0 * ROWB, kv_len * ROWB);
+  const rsrc_t rsc = make_rsrc((wave == 0 ? ks : vs) + kvrow0, kv_len * 2);
 
-  // Loader roles.  K: thread -> token tid/4, bytes [part*D/8, +D/8).
-  // V (D=128): thread -> dword dp = tid%16 of tokens 4*(tid/16) .. +3.
-  // V (D=64):  thread -> dword dp = tid%8  of tokens 2*(tid/8), +1.
-  constexpr int VTOK = (D == 128) ? 4 : 2;
-  const int k_tok = tid >> 2;
-  const int k_part = tid & 3;
-  const int v_dp = tid % (D / 8);
-  const int v_tg = tid / (D / 8);
-  uint32_t kreg[D / 32];
-  uint32_t vreg[VTOK];
-  uint16_t sreg = 0;
+  // Loader roles.  K: lane = token, wave = which ROWB / NW bytes of the row
+  // (chunk planes KDW wave ..).  V: VT consecutive tokens x one dword (8 head
+  // dims) per thread, mapped so that every conversion write instruction of a
+  // wave covers distinct banks.  Scales: wave 0 lane t loads the K scale of
+  // token t, wave 1 the V scale.
+  const uint32_t k_voff = (uint32_t)(lane * ROWB + wave * (ROWB / NW));
+  int v_dp, v_tok0;
+  if constexpr (D == 128 && NW == 4) {
+    const int t = lane >> 4;
+    v_dp = lane & 15;
+    v_tok0 = 4 * (8 * (wave >> 1) + 4 * (wave & 1) + 2 * (t & 1) + (t >> 1));
+  } else if constexpr (D == 128 && NW == 8) {
+    const int t = lane >> 4;
+    v_dp = lane & 15;
+    v_tok0 = 4 * (8 * (wave >> 2) + 4 * ((wave >> 1) & 1) + 2 * (t & 1) + (wave & 1)) + 2 * (t >> 1);
+  } else {
+    static_assert(D == 64 && NW == 4, "unsupported D / NW");
+    v_dp = lane & 7;
+    v_tok0 = 2 * (8 * wave + (lane >> 3));
+  }
+  const uint32_t v_voff = (uint32_t)(v_tok0 * ROWB + 4 * v_dp);
+  // V store position: plane P and half h of the token unit, row slot base.
+  int v_st;
+  {
+    const int u = v_tok0 >> 2;
+    const int P = 4 * (u >> 3) + 2 * ((u >> 2) & 1) + (u & 1);
+    const int hh = (u >> 1) & 1;
+    const int sig = (v_dp >> 1) & 7;  // (d >> 4) & 7 for d = 8 v_dp + n
+    v_st = P * VPL + (8 * v_dp + sig) * 8 + hh * 4 + (v_tok0 & 3);
+  }
+  // V-scale table slot of token `lane`: [j][tb][vq][i]
+  const int sv_slot = ((lane >> 2) & 1) * 32 + (lane >> 5) * 16 + ((lane >> 3) & 3) * 4 + (lane & 3);
+
+  uint32_t kw[KDW];
+  uint32_t vw[VT];
+  uint16_t sc = 0;
 
   auto load_tile = [&](int t0) {
-    {
-      const int tok = min(t0 + k_tok, kv_len - 1);
-      const uint8_t* p = kbase + (int64_t)tok * ROWB + k_part * (D / 8);
-      if constexpr (D == 128) {
-        const uint4v w = *reinterpret_cast<const uint4v*>(p);
+    const int so = t0 * ROWB;
+    if constexpr (KDW == 4) {
+      const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff, so, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[i] = w[i];
+      for (int i = 0; i < 4; ++i) kw[i] = w[i];
+    } else if constexpr (KDW == 2) {
+      const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, k_voff, so, 0);
+      kw[0] = w[0];
+      kw[1] = w[1];
+    } else {
+      kw[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, k_voff, so, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VT; ++i)
+      vw[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_voff + i * ROWB, so, 0);
+    if (wave < 2) sc = __builtin_amdgcn_raw_buffer_load_b16(rsc, (uint32_t)(lane * 2), t0 * 2, 0);
+  };
+
+  // Exact codes to LDS (no scale applied), scales to their tables.
+  auto store_tile = [&](int buf) {
+    _Float16* sk_ = s_k + buf * KBUF;
+    _Float16* sv_ = s_v + buf * VBUF;
+#pragma unroll
+    for (int i = 0; i < KDW; ++i) {
+      const int c = KDW * wave + i;
+      *reinterpret_cast<half8v*>(sk_ + c * KPL + lane * 8) = unpack8_perm(kw[i]);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      // row slot (8 v_dp + n) ^ sig = v_st's slot with n xor-ed into bits 0-2
+      _Float16* dst = sv_ + (v_st ^ (n * 8));
+      const half2v a = nib_pair2(vw[0], vw[1], n);
+      if constexpr (VT == 4) {
+        const half2v c = nib_pair2(vw[2], vw[3], n);
+        const uint2v w = {bitcast<uint32_t>(a), bitcast<uint32_t>(c)};
+        *reinterpret_cast<uint2v*>(dst) = w;
       } else {
-        const uint2v w = *reinterpret_cast<const uint2v*>(p);
-        kreg[0] = w[0];
-        kreg[1] = w[1];
+        *reinterpret_cast<uint32_t*>(dst) = bitcast<uint32_t>(a);
       }
     }
-#pragma unroll
-    for (int i = 0; i < VTOK; ++i) {
-      const int tok = min(t0 + VTOK * v_tg + i, kv_len - 1);
-      vreg[i] = *reinterpret_cast<const uint32_t*>(vbase + (int64_t)tok * ROWB + 4 * v_dp);
-    }
-    if (tid < 2 * BN) {
-      const int tok = min(t0 + (tid & (BN - 1)), kv_len - 1);
-      sreg = (tid < BN) ? ks[kvrow0 + tok] : vs[kvrow0 + tok];
+    if (wave == 0) {
+      const float f = f16bits_to_f32(sc) * qk_log2;
+      s_csk[buf][lane] = f;
+      const float m = wave_max_nonneg(fabsf(f));
+      if (lane == 0) s_cmax[buf] = m;
+    } else if (wave == 1) {
+      s_svh[buf][sv_slot] = bitcast<_Float16>(sc);
     }
   };
 
+  // Reader bases (halves, buffer 0).  K: plane j, token r.  V: plane j,
+  // row (32 db + r) ^ sigma for each output block db.
+  const int k_rd = j * KPL + r * 8;
+  int v_rd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = 32 * db + r;
+    v_rd[db] = j * VPL + (d ^ ((d >> 4) & 7)) * 8;
+  }
+
+  if (threadIdx.x < BN) s_ones[threadIdx.x] = 1.0f;
   load_tile(0);
+  store_tile(0);
+  load_tile(BN);
+  __syncthreads();
+
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int t0 = kt * BN;
-    __syncthreads();  // the previous tile's LDS reads are done
-    // ---- codes -> exact fp16 in LDS
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const int c = k_part * (D / 32) + i;
-      const int pc = c ^ (k_tok & (NCH - 1));
-      *reinterpret_cast<half8v*>(&s_k[k_tok * D + pc * 8]) = unpack8_perm(kreg[i]);
-    }
-#pragma unroll
-    for (int nib = 0; nib < 8; ++nib) {
-      const int d = 8 * v_dp + nib;
-      if constexpr (D == 128) {
-        const half2v a = nib_pair2(vreg[0], vreg[1], nib);
-        const half2v bb = nib_pair2(vreg[2], vreg[3], nib);
-        const int pu = v_tg ^ (d & 15);
-        uint2v w = {bitcast<uint32_t>(a), bitcast<uint32_t>(bb)};
-        *reinterpret_cast<uint2v*>(&s_v[d * BN + pu * 4]) = w;
-      } else {
-        const half2v a = nib_pair2(vreg[0], vreg[1], nib);
-        const int pu = (v_tg >> 1) ^ (d & 15);
-        *reinterpret_cast<uint32_t*>(&s_v[d * BN + pu * 4 + (v_tg & 1) * 2]) = bitcast<uint32_t>(a);
-      }
-    }
-    if (tid < BN)
-      s_csk[tid] = f16bits_to_f32(sreg) * qk_log2;
-    else if (tid < 2 * BN)
-      s_sv[tid - BN] = f16bits_to_f32(sreg);
-    __syncthreads();
-    if (kt + 1 < n_tiles) load_tile(t0 + BN);  // prefetch the next tile's codes
-
+    const int buf = kt & 1;
+    const _Float16* sk_ = s_k + buf * KBUF;
+    const _Float16* sv_ = s_v + buf * VBUF;
+    const float* csk_ = s_csk[buf];
     const bool need = wave_active && (!CAUSAL || t0 <= wrow_hi + off);
-    if (!need) continue;
 
-    // ---- S^T = K Q^T for two 32-token blocks
+    // Convert the next tile into the other buffer and fetch the one after.
+    // On the last tiles this converts and fetches past the end (zeros, or
+    // keys this workgroup never uses): harmless, and branch-free.
     float16v st[2];
+    if (need) {
+      // ---- S^T = K Q^T for two 32-token blocks
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      float16v acc = float16v{};
-      const int tok = 32 * tb + r;
+      for (int tb = 0; tb < 2; ++tb) {
+        float16v acc = float16v{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int pc = (2 * s + j) ^ (tok & (NCH - 1));
-        const half8v a = *reinterpret_cast<const half8v*>(&s_k[tok * D + pc * 8]);
-        acc = mfma32x32x16(a, qop[s], acc);
+        for (int s = 0; s < KS; ++s) {
+          const half8v a = *reinterpret_cast<const half8v*>(sk_ + k_rd + 2 * s * KPL + tb * 256);
+          acc = mfma32x32x16(a, qop[s], acc);
+        }
+        st[tb] = acc;
       }
-      st[tb] = acc;
+      store_tile(buf ^ 1);
+      load_tile(t0 + 2 * BN);
+    } else {
+      store_tile(buf ^ 1);
+      load_tile(t0 + 2 * BN);
     }
 
-    // ---- online softmax; lane's tokens: 32 tb + 8 (v/4) + 4 j + v%4
-    const bool full = (t0 + BN <= kv_len) && (!CAUSAL || t0 + BN - 1 <= wrow_lo + off);
-    float x[2][16];
-    float mloc = -INFINITY;
+    if (need) {
+      // ---- online softmax; lane's tokens: 32 tb + 8 (v/4) + 4 j + v%4
+      const bool full = (t0 + BN <= kv_len) && (!CAUSAL || t0 + BN - 1 <= wrow_lo + off);
+      auto csk4 = [&](int tb, int vq) {
+        return *reinterpret_cast<const float4v*>(csk_ + 32 * tb + 8 * vq + 4 * j);
+      };
+      // Exponent p = exp2(st * c - m_use): with c = csk and raw scores st on
+      // full tiles, with c = 1 and exact masked scores st on the others.
+      const float* ctab = s_ones;
+      float mx;
+      if (!full) {
+        mx = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int tok0 = 32 * tb + 8 * vq + 4 * j;
-        const float4v cs = *reinterpret_cast<const float4v*>(&s_csk[tok0]);
+          for (int vq = 0; vq < 4; ++vq) {
+            const float4v c = csk4(tb, vq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = st[tb][4 * vq + i] * cs[i];
-          if (!full) {
-            const int key = t0 + tok0 + i;
-            const bool ok = (key < kv_len) && (!CAUSAL || key <= qrow + off);
-            v = ok ? v : -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+              const int key = t0 + 32 * tb + 8 * vq + 4 * j + i;
+              const bool ok = (key < kv_len) && (!CAUSAL || key <= qrow + off);
+              const float x = ok ? st[tb][4 * vq + i] * c[i] : -INFINITY;
+              st[tb][4 * vq + i] = x;
+              mx = fmaxf(mx, x);
+            }
           }
-          x[tb][4 * vq + i] = v;
-          mloc = fmaxf(mloc, v);
+        }
+      } else {
+        // upper bound of the lane's max score: max |s| x max |csk| of the tile
+        mx = 0.0f;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fabsf(st[tb][v]));
+        }
+        mx *= s_cmax[buf];
+        ctab = csk_;
+      }
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kTau)) {
+        // some row of the wave may rise above its reference: move the
+        // reference of those rows to their new maximum, rescale their state
+        if (full) {
+          mx = -INFINITY;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int vq = 0; vq < 4; ++vq) {
+              const float4v c = csk4(tb, vq);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[tb][4 * vq + i] * c[i]);
+            }
+          }
+        }
+        mx = xor_max(mx, 32);
+        const bool up = mx > m_ref + kTau;
+        const float alpha = up ? fast_exp2(m_ref - mx) : 1.0f;
+        m_ref = up ? mx : m_ref;
+        m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o_acc[db] *= alpha;
+      }
+      half8v pop[2][2];
+      const half8v* svh = reinterpret_cast<const half8v*>(&s_svh[buf][32 * j]);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const half8v sv = svh[2 * tb + kp];  // tokens 32 tb + 8 (2 kp + e/4) + 4 j + e%4
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // v = 4 vq + i = 8 kp + e  ->  vq = 2 kp + e/4, i = e%4
+            const int vq = 2 * kp + (e >> 2);
+            const int i = e & 3;
+            const float c = ctab[32 * tb + 8 * vq + 4 * j + i];
+            const float p = fast_exp2(fmaf(st[tb][8 * kp + e], c, -m_use));
+            l_run += p;
+            // P~ = fp16(p x s_V): one rounding of the exact product
+            pop[tb][kp][e] = (_Float16)fmaf(p, (float)sv[e], 0.0f);
+          }
         }
       }
-    }
-    mloc = xor_max(mloc, 32);
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float lsum = 0.0f;
-    half8v pop[2][2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int tok0 = 32 * tb + 8 * vq + 4 * j;
-        const float4v sv = *reinterpret_cast<const float4v*>(&s_sv[tok0]);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = fast_exp2(x[tb][4 * vq + i] - m_use);
-          lsum += p[i];
-        }
-        const half2v p01 = cvt_pk_f16(p[0] * sv[0], p[1] * sv[1]);
-        const half2v p23 = cvt_pk_f16(p[2] * sv[2], p[3] * sv[3]);
-        // v = 4 vq + i = 8 kp + e  ->  kp = vq / 2, e = 4 (vq % 2) + i
-        const int kp = vq >> 1;
-        const int e0 = 4 * (vq & 1);
-        pop[tb][kp][e0 + 0] = p01[0];
-        pop[tb][kp][e0 + 1] = p01[1];
-        pop[tb][kp][e0 + 2] = p23[0];
-        pop[tb][kp][e0 + 3] = p23[1];
-      }
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o_acc[db] *= alpha;
-    }
 
-    // ---- O^T += V^T P^T; k = 8j + e <-> token 32 tb + 16 kp + 8 (e/4) + 4 j + e%4
+      // ---- O^T += V^T P^T; k = 8 j + e <-> token 32 tb + 16 kp + 8 (e/4) + 4 j + e%4
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const int u0 = 8 * tb + 4 * kp + j;
+        for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + r;
-          const uint2v lo = *reinterpret_cast<const uint2v*>(&s_v[d * BN + ((u0 ^ (d & 15)) * 4)]);
-          const uint2v hi = *reinterpret_cast<const uint2v*>(&s_v[d * BN + (((u0 + 2) ^ (d & 15)) * 4)]);
-          const uint4v w = {lo[0], lo[1], hi[0], hi[1]};
-          o_acc[db] = mfma32x32x16(bitcast<half8v>(w), pop[tb][kp], o_acc[db]);
+          for (int db = 0; db < NDB; ++db) {
+            const half8v a =
+                *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
+            o_acc[db] = mfma32x32x16(a, pop[tb][kp], o_acc[db]);
+          }
         }
       }
     }
+    __syncthreads();  // tile kt+1 is in LDS; nobody still reads buffer `buf`
   }
 
   // ---- epilogue: O = O^T / l; lane owns row qrow, head dims 32 db + 8 vq + 4 j + i
@@ -286,18 +417,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       }
     }
     if (j == 0 && lse_out)
-      lse_out[((int64_t)b * Hq + h) * Sq + qrow] = (m_run + log2f(l)) * kLn2;
+      lse_out[((int64_t)b * Hq + h) * Sq + qrow] = (m_ref + log2f(l)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int NW, bool CAUSAL>
 hipError_t launch(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
                   const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                   int64_t kv_len, int64_t C, float qk_log2, float* out, float* lse,
                   hipStream_t stream) {
+  constexpr int BM = 32 * NW;
   const int nqb = (int)((Sq + BM - 1) / BM);
   dim3 grid((uint32_t)Hq, (uint32_t)nqb, (uint32_t)B);
-  prefill_kernel<D, CAUSAL><<<grid, dim3(256), 0, stream>>>(
+  prefill_kernel<D, NW, CAUSAL><<<grid, dim3(64 * NW), 0, stream>>>(
       q, kc, ks, vc, vs, (int)Hq, (int)Hkv, (int)(Hq / Hkv), (int)Sq, (int)kv_len, C, qk_log2, nqb,
       out, lse);
   return hipGetLastError();
@@ -313,14 +445,16 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
   const float qk_log2 = softmax_scale * kLog2e;
   if (D == 128) {
     if (causal)
-      return launch<128, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
-                               stream);
-    return launch<128, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
-                              stream);
+      return launch<128, 8, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2,
+                                         out, lse, stream);
+    return launch<128, 8, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2,
+                                        out, lse, stream);
   }
   if (causal)
-    return launch<64, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
-  return launch<64, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
+    return launch<64, 4, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
+                               stream);
+  return launch<64, 4, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
+                              stream);
 }
 
 }  // namespace qkvfa

@@ -5,7 +5,9 @@ import torch
 
 import oracle
 import quantized_kv_flashattention_amd as qkv
-from gpu_helpers import DEV, assert_close, cache_to_dev, compare, full_workload, q_to_dev, random_case
+from gpu_helpers import (DEV, assert_close, cache_to_dev, compare, full_workload, oracle_cache, q_to_dev,
+                         random_case)
+from qkv_inputs import f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +74,27 @@ def test_full_size_causal_prefill_sampled():
     ro, rl = oracle.attention(q, kc, ks, vc, vs, w.L, w.softmax_scale, True, heads=heads, rows=rows)
     mx, mn = assert_close(out, ro, w.name)
     print(f"{w.name}: sampled max {mx:.3e} mean {mn:.3e}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("trend", ["rising", "falling"])
+def test_prefill_score_trends(D, causal, trend):
+    """K rows scaled by a factor that grows (or shrinks) 40x along the keys,
+    so a row's running maximum keeps moving by far more than 2^8 between
+    tiles: every rescale decision of the online softmax is exercised (a missed
+    one overflows fp16 probabilities into inf/NaN)."""
+    rng = np.random.default_rng(D + 2 * causal + (trend == "rising"))
+    B, Hq, Hkv, Sq, L = 1, 4, 2, 700, 900
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, Sq, D)).astype(np.float32))
+    k = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    f = np.linspace(1.0, 40.0, L, dtype=np.float32)
+    k *= (f if trend == "rising" else f[::-1])[None, None, :, None]
+    kc, ks, vc, vs = oracle_cache(k, v, L + 3, seed=D)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, lse = _run(q, (kc, ks, vc, vs), L, causal, scale)
+    assert not bool(torch.isnan(out).any()) and not bool(torch.isinf(out).any())
+    ro, rl = oracle.attention(q, kc, ks, vc, vs, L, scale, causal)
+    assert_close(out, ro, f"{trend} D={D} causal={causal}")
+    assert compare(lse, rl)[0] < 1e-3
