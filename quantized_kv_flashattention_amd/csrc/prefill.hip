@@ -313,6 +313,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const float* ctab = s_ones;
       float mx;
       if (!full) {
+        const int lim = (CAUSAL ? min(kv_len - 1, qrow + off) : kv_len - 1) - t0 - 4 * j;
         mx = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
@@ -321,8 +322,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const float4v c = csk4(tb, vq);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = t0 + 32 * tb + 8 * vq + 4 * j + i;
-              const bool ok = (key < kv_len) && (!CAUSAL || key <= qrow + off);
+              // key t0 + 32 tb + 8 vq + 4 j + i is visible iff its offset
+              // 32 tb + 8 vq + i is at most lim
+              const bool ok = 32 * tb + 8 * vq + i <= lim;
               const float x = ok ? st[tb][4 * vq + i] * c[i] : -INFINITY;
               st[tb][4 * vq + i] = x;
               mx = fmaxf(mx, x);
