@@ -52,7 +52,7 @@ def kernel_source_hash() -> str:
     counter-derived traffic is valid only for exactly these."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "quantized_kv_flashattention_amd")
-    for rel in ("csrc/decode.hip", "csrc/qkvfa_device.hpp", "csrc/qkvfa_internal.h", "csrc/api.cpp", "build.py"):
+    for rel in ("csrc/decode.hip", "csrc/qkvfa_device.hpp", "csrc/qkvfa_internal.h", "build.py"):
         with open(os.path.join(pkg, rel), "rb") as f:
             h.update(rel.encode() + f.read())
     return h.hexdigest()[:16]

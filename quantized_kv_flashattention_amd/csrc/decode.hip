@@ -29,8 +29,8 @@
 // Per-lane load offsets are loop-invariant; only the uniform chunk base moves.
 // The next chunk's codes are loaded before the current chunk is processed.
 //
-// After the loop the four waves of a workgroup merge their (m, l, O) through
-// LDS.  With one split the result goes straight to `out`.  Otherwise each
+// A workgroup is eight waves; wave w takes chunks w, w + 8, w + 16, ... of the
+// split.  After the loop the eight waves merge their (m, l, O) through LDS.  With one split the result goes straight to `out`.  Otherwise each
 // workgroup writes its split's normalized partial O_s and lse_s, and the last
 // workgroup of a (batch, KV head) to finish (an atomic ticket per group)
 // merges all splits in split order -- deterministic, and no second launch.
@@ -44,7 +44,7 @@ namespace qkvfa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (fits s_o at D = 64)
@@ -73,11 +73,12 @@ struct ChunkRegs {
   uint16_t sk, sv;   // K and V scale of token (lane % 32) of the chunk
 };
 
-// One wave64 per SIMD slot holds NB*32 + ~90 VGPRs; with one row block the
-// kernel is asked to fit 128 so four waves share each SIMD (16 per CU).  The
-// 64-row variant skips the one-chunk prefetch to stay within 256 VGPRs.
+// One wave64 holds NB*32 + ~90 VGPRs.  The planner launches about one
+// workgroup (two waves per SIMD) per CU; the one-row-block kernel still fits
+// 128 VGPRs so that concurrent launches can share a CU.  The 64-row variant
+// skips the one-chunk prefetch to stay within 256 VGPRs.
 template <int D, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
   constexpr bool kPrefetch = (NB <= 2);
   constexpr int KK = D / 32;    // QK MFMAs per 16-token block
@@ -119,10 +120,10 @@ void decode_kernel(const DecodeArgs a) {
 
   // Query operand (B of S^T = K Q^T): query row nb*16 + r, k = 8j + e <->
   // head dim 8*(KK*j + kk) + perm8(e), matching the K lane's dword order.
-  // Converted once into LDS (shared by the four waves): 16-byte chunk c of
+  // Converted once into LDS (shared by the eight waves): 16-byte chunk c of
   // row x sits at chunk c ^ (x % 16), so the 16 rows a wave reads together
   // fall in different banks.
-  for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 256) {
+  for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 64 * kWaves) {
     const int row = idx / DW;
     const int c = idx - row * DW;
     half8v h = half8v{};
@@ -302,7 +303,7 @@ void decode_kernel(const DecodeArgs a) {
     }
   }
 
-  // ---- merge the four waves through LDS, one 16-row block at a time
+  // ---- merge the eight waves through LDS, one 16-row block at a time
   const bool direct = (a.n_split == 1);
   // one descriptor over all partial outputs (the planner keeps them < 2 GiB)
   const rsrc_t rpart = make_rsrc(a.part_o, direct ? 0 : a.part_bytes);
@@ -332,7 +333,7 @@ void decode_kernel(const DecodeArgs a) {
     }
     __syncthreads();
     const int rows_here = min(16, R - nb * 16);
-    for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += 256) {
+    for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += 64 * kWaves) {
       const int rr = idx / (D / 4);
       const int d = 4 * (idx - rr * (D / 4));
       float M = -INFINITY;
@@ -389,11 +390,11 @@ void decode_kernel(const DecodeArgs a) {
   __shared__ float s_den[64];
   {
     const int total = R * n_split;
-    for (int base = threadIdx.x; base < total; base += 256 * 8) {
+    for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 256;
+        const int idx = base + u * 64 * kWaves;
         v[u] = -INFINITY;
         if (idx < total) {
           const int row = idx / n_split;
@@ -405,7 +406,7 @@ void decode_kernel(const DecodeArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (base + u * 256 < total) s_w[base + u * 256] = v[u];
+        if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
     }
   }
   __syncthreads();
@@ -433,7 +434,7 @@ void decode_kernel(const DecodeArgs a) {
   }
   __syncthreads();
   // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per thread
-  for (int idx = threadIdx.x; idx < R * (D / 4); idx += 256) {
+  for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
     const int row = idx / (D / 4);
     const int d = 4 * (idx - row * (D / 4));
     const int hg = row / Sq;
@@ -460,7 +461,7 @@ void decode_kernel(const DecodeArgs a) {
 template <int D, int NB>
 hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
   dim3 grid((uint32_t)n_split, (uint32_t)Hkv, (uint32_t)B);
-  decode_kernel<D, NB><<<grid, dim3(256), 0, stream>>>(args);
+  decode_kernel<D, NB><<<grid, dim3(64 * kWaves), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -480,10 +481,11 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
   const int64_t units = B * Hkv;
   int64_t ns;
   if (num_splits <= 0) {
-    // about two workgroups (eight waves) per CU: measured best on MI355X for
-    // both a 128-group 8K-token and an 8-group 128K-token decode; more splits
-    // add per-split epilogue and merge work without adding bandwidth
-    const int64_t target_wgs = 2 * (int64_t)(num_cus > 0 ? num_cus : 256);
+    // one workgroup (eight waves) per CU: measured best on MI355X for both a
+    // 128-group 8K-token and an 8-group 128K-token decode.  Every workgroup
+    // starts at once and streams its range at the shared HBM rate; more
+    // splits add per-split epilogue and merge latency without adding bandwidth
+    const int64_t target_wgs = (int64_t)(num_cus > 0 ? num_cus : 256);
     ns = (target_wgs + units - 1) / units;
     const int64_t max_ns = chunks / kWaves > 0 ? chunks / kWaves : 1;   // >= one chunk per wave
     if (ns > max_ns) ns = max_ns;

@@ -88,6 +88,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes, 0x00020000);
 }
 
+// Row quantization, one fp16 scale per row of D values x (the arithmetic of
+// every kernel that writes cache rows, so all of them agree bit for bit):
+//   scale = fp16_rne(max|x| / 7)    (IEEE fp32 division, then one rounding)
+//   code  = clamp(rint(x / float(scale)), -8, 7) as a 4-bit two's complement
+//           nibble (IEEE fp32 division, round half to even); a zero scale
+//           gives zero codes.  These files are built without fast-math.
+__device__ __forceinline__ _Float16 quant_scale(float amax) { return (_Float16)(amax / 7.0f); }
+__device__ __forceinline__ uint32_t quant_code(float x, float scale) {
+  const float c = fminf(fmaxf(rintf(x / scale), -8.0f), 7.0f);
+  return (uint32_t)(int)c & 0xFu;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return bitcast<float>((uint32_t)b << 16);
 }

@@ -58,16 +58,12 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantTarget t0, Qu
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, TPR));
 
-  const _Float16 s16 = (_Float16)(m / 7.0f);   // IEEE divide, then RNE to fp16
+  const _Float16 s16 = quant_scale(m);
   const float s = (float)s16;
   uint32_t packed = 0;
   if (s != 0.0f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float c = rintf(x[i] / s);                 // IEEE divide, round half to even
-      c = fminf(fmaxf(c, -8.0f), 7.0f);
-      packed |= ((uint32_t)(int)c & 0xFu) << (4 * i);
-    }
+    for (int i = 0; i < 8; ++i) packed |= quant_code(x[i], s) << (4 * i);
   }
   const int64_t row = (int64_t)bh * C + pos + t;
   reinterpret_cast<uint32_t*>(codes + row * (D / 2))[sub] = packed;
