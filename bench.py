@@ -2,9 +2,9 @@
 
 One step = one decode step of the Llama-3-8B shaped GQA decode workload
 (B=16, 32 query / 8 KV heads, D=128, 8192 cached tokens): quantize-and-append
-the new token's K and V rows (one launch), then split-K decode attention of
-the query over the whole cache (exact int4 -> fp16 conversion, MFMA QK^T and
-PV, online softmax, LSE merge; one launch).  Inputs are resident in HBM
+the new token's K and V rows, then split-K decode attention of the query over
+the whole cache (exact int4 -> fp16 conversion, MFMA QK^T and PV, online
+softmax, LSE merge) -- both in one launch (qkv_decode_append).  Inputs are resident in HBM
 before timing starts; the cache is rotated over several independent copies
 so that the 256 MB Infinity Cache cannot serve repeated reads.  Timed
 launches are queued behind a GPU hold so that host-side Python launch
@@ -167,10 +167,11 @@ def bench_decode(torch, qkv, w, steps, warmup, with_append):
         qkv.decode(q, caches[i], w.L, softmax_scale=w.softmax_scale, out=out, workspace=ws)
 
     def step(i):
-        c = caches[i]
-        if with_append:
-            qkv.quantize_append_kv(k_new, v_new, c, w.L - 1)   # the new token's K and V rows
-        decode_only(i)
+        if with_append:   # the new token's K and V rows go to row L-1, then decode: one launch
+            qkv.decode_append(q, k_new, v_new, caches[i], w.L - 1, softmax_scale=w.softmax_scale, out=out,
+                              workspace=ws)
+        else:
+            decode_only(i)
 
     for i in range(warmup):
         step(i % n_copies)
@@ -186,7 +187,11 @@ def bench_decode(torch, qkv, w, steps, warmup, with_append):
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
-    avg_ms, med_ms = per_launch_ms(torch, decode_only, max(steps, 20), n_copies)
+    # the step's kernel, one launch at a time (events on the launch stream)
+    avg_ms, med_ms = per_launch_ms(torch, step, max(steps, 20), n_copies)
+    plain_avg, _ = per_launch_ms(torch, decode_only, max(steps, 20), n_copies)
+    if with_append:   # + the new rows' fp32 K and V read by the kernel
+        attn_bytes += 2 * w.B * w.Hkv * w.D * 4
     res = {
         "workload": w.name, "n_split": ns, "cache_copies": n_copies,
         "ms_per_step": ms_step,
@@ -194,6 +199,7 @@ def bench_decode(torch, qkv, w, steps, warmup, with_append):
         "step_GBps_packed_kv": kv_bytes / (ms_step * 1e-3) / 1e9,
         "decode_avg_ms": avg_ms, "decode_median_ms": med_ms,
         "decode_GBps": attn_bytes / (avg_ms * 1e-3) / 1e9,
+        "decode_only_avg_ms": plain_avg,
     }
     res["decode_frac_hbm"] = res["decode_GBps"] / HBM_PEAK_GBS
     del caches
@@ -308,11 +314,13 @@ def profile_target(target: str, iters: int):
     w = workload({"decode": "llama3_8b_decode", "long": "long_context_decode"}[target])
     q_bits, k, v = make_qkv(w)
     caches = upload_cache(torch, qkv, k, v, max(4, math.ceil(2.5 * MALL_BYTES / decode_bytes(w)[0])))
-    del k, v
     q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
     out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
-    for i in range(iters):
-        qkv.decode(q, caches[i % len(caches)], w.L, softmax_scale=w.softmax_scale, out=out)
+    k_new = torch.from_numpy(k[:, :, -1:].copy()).cuda()
+    v_new = torch.from_numpy(v[:, :, -1:].copy()).cuda()
+    for i in range(iters):   # the benchmark's step: append the new token + decode, one launch
+        qkv.decode_append(q, k_new, v_new, caches[i % len(caches)], w.L - 1, softmax_scale=w.softmax_scale,
+                          out=out)
     torch.cuda.synchronize()
 
 
@@ -436,7 +444,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w3.name, "B": w3.B, "Hq": w3.Hq, "Hkv": w3.Hkv, "D": w3.D,
                    "Sq": w3.Sq, "kv_len": w3.L, "kv_format": "int4 + fp16 scale per (token, KV head)",
-                   "step": "append 1 token (K,V) + split-K decode", "n_split": head["n_split"],
+                   "step": "append 1 token (K,V) + split-K decode, one launch", "n_split": head["n_split"],
                    "cache_copies_rotated": head["cache_copies"]},
         "roofline": {
             "bound": "hbm",

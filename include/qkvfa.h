@@ -149,6 +149,32 @@ qkv_status qkv_decode(const uint16_t* q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * (a)+(b) One decode step in one launch: append, then attend.  Quantizes
+ * n_new new K and V rows into cache rows [pos, pos + n_new), exactly as
+ * qkv_quantize_append_kv does, then computes qkv_decode over cache rows
+ * [0, pos + n_new) (TurboAttention §2.1: a decode step appends k_t and v_t
+ * to the cache and its query attends the updated cache).  The rows written,
+ * out and lse are bit-identical to qkv_quantize_append_kv followed by
+ * qkv_decode with kv_len = pos + n_new and the same num_splits; the single
+ * launch saves the second kernel's start and drain.
+ *   k_new, v_new   float [B, Hkv, n_new, D], device, 16-byte aligned
+ *   k_codes, v_codes, k_scales, v_scales: the cache as for qkv_decode; rows
+ *                  [pos, pos + n_new) are written, no other row is touched
+ *   workspace      as for qkv_decode with kv_len = pos + n_new (same tickets
+ *                  contract; qkv_decode_workspace_bytes gives the size)
+ *   other arguments as for qkv_decode.
+ * Requires 0 <= pos, 1 <= n_new <= 64, pos + n_new <= C, and the
+ * qkv_decode requirements.  The new rows must not alias the cache.
+ */
+qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float* v_new,
+                             uint8_t* k_codes, uint16_t* k_scales,
+                             uint8_t* v_codes, uint16_t* v_scales,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                             int64_t pos, int64_t n_new, int64_t C, int64_t D,
+                             float softmax_scale, int num_splits, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * (c) Prefill attention, tiled with online softmax (FlashAttention tiling,
  * TurboAttention §2.2).  causal = 0: every row sees [0, kv_len).
  * causal = 1: query row i (0 <= i < Sq) is token kv_len - Sq + i and sees

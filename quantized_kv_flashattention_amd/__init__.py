@@ -28,6 +28,7 @@ __all__ = [
     "quantize_append",
     "quantize_append_kv",
     "decode",
+    "decode_append",
     "prefill",
     "decode_workspace_bytes",
     "decode_auto_splits",
@@ -70,6 +71,9 @@ def _load():
     lib.qkv_decode.restype = ci
     lib.qkv_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                vp, vp, vp, sz, vp]
+    lib.qkv_decode_append.restype = ci
+    lib.qkv_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                      f32, ci, vp, vp, vp, sz, vp]
     lib.qkv_prefill.restype = ci
     lib.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                 vp, vp, vp]
@@ -237,6 +241,38 @@ def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False,
     _check(_lib.qkv_decode(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
                            C, D, _scale(softmax_scale, D), int(num_splits), _ptr(out), _ptr(lse),
                            _ptr(workspace), ws_bytes, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def decode_append(q, k_new, v_new, cache, pos, softmax_scale=None, num_splits=0, return_lse=False,
+                  out=None, lse=None, workspace=None):
+    """One decode step in one launch: quantize ``k_new``/``v_new [B, Hkv, n_new, D]``
+    into cache rows ``[pos, pos+n_new)``, then decode ``q`` over rows ``[0, pos+n_new)``.
+    Same results as ``quantize_append_kv`` followed by ``decode``."""
+    tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    _req(k_new, "k_new", torch.float32, 4)
+    _req(v_new, "v_new", torch.float32, 4)
+    if k_new.shape != v_new.shape or k_new.device != q.device or v_new.device != q.device:
+        raise ValueError("k_new and v_new must have one shape and q's device")
+    n_new = k_new.shape[2]
+    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, int(pos) + n_new)
+    if k_new.shape != (B, Hkv, n_new, D):
+        raise ValueError("k_new shape does not match the cache")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    else:
+        _req(out, "out", torch.float32, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, B * Hkv, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kc, ks, vc, vs = tensors
+    _check(_lib.qkv_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                  B, Hq, Hkv, Sq, int(pos), n_new, C, D, _scale(softmax_scale, D),
+                                  int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                  _stream(q)))
     return (out, lse) if return_lse else out
 
 

@@ -143,30 +143,71 @@ size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq
   return qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, p.n_split);
 }
 
+}  // extern "C"
+
+namespace {
+
+// qkv_decode and qkv_decode_append after their own argument checks.
+qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                         const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
+                         float softmax_scale, int num_splits, float* out, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         const qkvfa::DecodeAppend* append, void* stream, const char* fn) {
+  const std::string f(fn);
+  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
+                                  C, D, out, lse, fn);
+  if (st != QKV_OK) return st;
+  if ((Hq / Hkv) * Sq > 64)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": (Hq/Hkv) * Sq must be <= 64; use qkv_prefill");
+  if (num_splits < 0 || num_splits > 1024)
+    return fail(QKV_ERR_INVALID_ARG, f + ": num_splits must be in [0, 1024]");
+  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus());
+  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, plan.n_split);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(QKV_ERR_WORKSPACE, f + ": workspace smaller than qkv_decode_workspace_bytes()");
+    if (!aligned(workspace, 16))
+      return fail(QKV_ERR_INVALID_ARG, f + ": workspace must be 16-byte aligned");
+  }
+  return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
+                                         kv_len, C, (int)D, softmax_scale, plan, out, lse,
+                                         workspace, append, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
 qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
                       const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
                       int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
                       float softmax_scale, int num_splits, float* out, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
-                                  C, D, out, lse, "qkv_decode");
-  if (st != QKV_OK) return st;
-  if ((Hq / Hkv) * Sq > 64)
-    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode: (Hq/Hkv) * Sq must be <= 64; use qkv_prefill");
-  if (num_splits < 0 || num_splits > 1024)
-    return fail(QKV_ERR_INVALID_ARG, "qkv_decode: num_splits must be in [0, 1024]");
-  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus());
-  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, plan.n_split);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(QKV_ERR_WORKSPACE, "qkv_decode: workspace smaller than qkv_decode_workspace_bytes()");
-    if (!aligned(workspace, 16))
-      return fail(QKV_ERR_INVALID_ARG, "qkv_decode: workspace must be 16-byte aligned");
-  }
-  return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
-                                         kv_len, C, (int)D, softmax_scale, plan, out, lse,
-                                         workspace, static_cast<hipStream_t>(stream)),
-                    "qkv_decode");
+  return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D,
+                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr,
+                       stream, "qkv_decode");
+}
+
+qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float* v_new,
+                             uint8_t* k_codes, uint16_t* k_scales, uint8_t* v_codes,
+                             uint16_t* v_scales, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                             int64_t pos, int64_t n_new, int64_t C, int64_t D,
+                             float softmax_scale, int num_splits, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_append: null new-row pointer");
+  if (n_new < 1 || n_new > 64)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_append: n_new must be in [1, 64]");
+  if (pos < 0 || pos + n_new > C)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_append: need 0 <= pos and pos + n_new <= C");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_append: k_new and v_new must be 16-byte aligned");
+  const qkvfa::DecodeAppend app = {k_new, v_new, n_new};
+  return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, pos + n_new, C, D,
+                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes, &app,
+                       stream, "qkv_decode_append");
 }
 
 qkv_status qkv_prefill(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,

@@ -35,6 +35,16 @@
 // workgroup of a (batch, KV head) to finish (an atomic ticket per group)
 // merges all splits in split order -- deterministic, and no second launch.
 // The ticket returns to zero after the merge, ready for the next call.
+//
+// Append mode (a decode step that first appends its new K/V rows): before
+// streaming, the workgroup whose split holds new rows quantizes them with the
+// shared row quantizer, writes codes and scales to the cache (for later steps)
+// and keeps a copy in LDS.  The new rows are the last rows of the attended
+// range, so the chunk loop streams only the older rows of the split and at
+// most two tail chunks then take the new rows from the LDS copy: the kernel
+// never reads the rows it wrote and needs no memory ordering between those
+// stores and its own loads.  Outputs and the written rows are bit-identical
+// to a separate append followed by decode.
 #include <math.h>
 
 #include "qkvfa_device.hpp"
@@ -44,10 +54,14 @@ namespace qkvfa {
 
 namespace {
 
-constexpr int kWaves = 8;
+// Waves per workgroup: eight, except for the 64-row variant, whose registers
+// (256 per lane with eight waves) do not fit; it keeps four waves and gets
+// the whole register file of its SIMD slot.
+__host__ __device__ constexpr int waves_for(int NB) { return NB >= 4 ? 4 : 8; }
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (fits s_o at D = 64)
+constexpr int kMaxNew = 64;                 // rows one append-mode call may add
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -61,10 +75,49 @@ struct DecodeArgs {
   float* part_lse;
   uint32_t* tickets;
   int part_bytes;   // bytes of part_o
+  // append mode (k_new != nullptr): n_new rows [B, Hkv, n_new, D] go to cache
+  // rows [pos, pos + n_new) through the writable cache pointers
+  const float* k_new;
+  const float* v_new;
+  uint8_t* kc_w;
+  uint16_t* ks_w;
+  uint8_t* vc_w;
+  uint16_t* vs_w;
+  int pos, n_new;
   int64_t C;
   int Hq, Hkv, G, Sq, kv_len, split_len, n_split;
   float qk_log2;
 };
+
+// One row of D fp32 values quantized by one wave: lane l < D/2 owns elements
+// 2l and 2l+1 (= byte l of the packed row).  Codes and scale go to the cache
+// row in global memory and to an LDS copy.
+template <int D>
+__device__ __forceinline__ void quantize_row_wave(const float* __restrict__ src, int lane,
+                                                  uint8_t* gcodes, uint16_t* gscale,
+                                                  uint8_t* lcodes, uint16_t* lscale) {
+  float x0 = 0.0f, x1 = 0.0f;
+  if (lane < D / 2) {
+    const float2 v = *reinterpret_cast<const float2*>(src + 2 * lane);
+    x0 = v.x;
+    x1 = v.y;
+  }
+  float m = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = xor_max(m, o);
+  const _Float16 s16 = quant_scale(m);
+  const float s = (float)s16;
+  uint32_t byte = 0;
+  if (s != 0.0f) byte = quant_code(x0, s) | (quant_code(x1, s) << 4);
+  if (lane < D / 2) {
+    gcodes[lane] = (uint8_t)byte;
+    lcodes[lane] = (uint8_t)byte;
+  }
+  if (lane == 0) {
+    *gscale = bitcast<uint16_t>(s16);
+    *lscale = bitcast<uint16_t>(s16);
+  }
+}
 
 template <int D>
 struct ChunkRegs {
@@ -78,8 +131,9 @@ struct ChunkRegs {
 // 128 VGPRs so that concurrent launches can share a CU.  The 64-row variant
 // skips the one-chunk prefetch to stay within 256 VGPRs.
 template <int D, int NB>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
+__global__ __launch_bounds__(64 * waves_for(NB)) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
+  constexpr int kWaves = waves_for(NB);
   constexpr bool kPrefetch = (NB <= 2);
   constexpr int KK = D / 32;    // QK MFMAs per 16-token block
   constexpr int DW = D / 8;     // dwords per packed row
@@ -93,6 +147,11 @@ void decode_kernel(const DecodeArgs a) {
   __shared__ float s_l[kWaves][16];
   __shared__ __align__(16) float s_o[kWaves][16 * OSTR];
   __shared__ int s_last;
+  // append mode: this split's new rows, indexed by row - pos
+  __shared__ __align__(16) uint32_t s_nk[kMaxNew * DW];
+  __shared__ __align__(16) uint32_t s_nv[kMaxNew * DW];
+  __shared__ uint16_t s_nks[kMaxNew];
+  __shared__ uint16_t s_nvs[kMaxNew];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -117,6 +176,70 @@ void decode_kernel(const DecodeArgs a) {
   const uint32_t offk = (uint32_t)((8 * (r >> 2) + (r & 3)) * ROWB + 4 * KK * j);  // +4 rows for kb = 1
   const uint32_t offv = (uint32_t)(8 * j * ROWB + 4 * (r % DW));
   const uint32_t offs = (uint32_t)(2 * (lane & 31));
+
+  // ---- append mode: this split's new rows [new_lo, new_hi)
+  const bool append = a.k_new != nullptr;
+  const int new_lo = append ? max(a.pos, t_begin) : 0;
+  const int new_hi = append ? min(a.pos + a.n_new, t_end) : 0;
+  // The chunk loop covers the split up to the first chunk that holds a new
+  // row; the remaining (tail) chunks are handled after it, each by the wave
+  // the plain decode gives it, so the arithmetic is the plain decode's.
+  const int t_main =
+      append ? min(t_end, t_begin + (max(a.pos, t_begin) - t_begin) / kChunk * kChunk) : t_end;
+
+  // Codes of the chunk starting at token c0, through buffer descriptors whose
+  // range ends at t_main <= kv_len (the split end, before any new rows): the
+  // hardware returns zero for
+  // any row at or past it (those tokens are masked) without touching memory.
+  // So no load leaves the valid rows, the last chunk needs no clamping, and a
+  // chunk past the split can be "loaded" unconditionally (all zeros, no
+  // traffic), which keeps the prefetch branch-free: a conditional prefetch
+  // makes the compiler wait for every outstanding load where the paths join.
+  auto load_chunk = [&](int c0, ChunkRegs<D>& cr, int lim) {
+    const int rows_left = max(lim - c0, 0);
+    const rsrc_t rk = make_rsrc(kbase + (int64_t)c0 * ROWB, rows_left * ROWB);
+    const rsrc_t rv = make_rsrc(vbase + (int64_t)c0 * ROWB, rows_left * ROWB);
+    const rsrc_t rks = make_rsrc(ksb + c0, rows_left * 2);
+    const rsrc_t rvs = make_rsrc(vsb + c0, rows_left * 2);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (KK == 4) {
+        const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
+      } else {
+        const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
+        cr.kw[kb][0] = w[0];
+        cr.kw[kb][1] = w[1];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
+    cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
+    cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
+  };
+
+  const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
+  ChunkRegs<D> cur;
+  load_chunk(t_begin + wave * kChunk, cur, t_main);
+
+  // ---- append mode: quantize the new rows (one wave per row and tensor,
+  //      from the last wave down: with one row block the first half of the
+  //      waves converts the query meanwhile), while the first chunk loads
+  if (append) {
+    const int ntask = 2 * max(new_hi - new_lo, 0);
+    for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
+      const int t = new_lo + (task >> 1);
+      const bool isv = (task & 1) != 0;
+      const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - a.pos)) * D;
+      uint8_t* gcodes = (isv ? a.vc_w : a.kc_w) + (kvrow0 + t) * ROWB;
+      uint16_t* gscale = (isv ? a.vs_w : a.ks_w) + kvrow0 + t;
+      uint8_t* lcodes = reinterpret_cast<uint8_t*>(isv ? s_nv : s_nk) + (t - a.pos) * ROWB;
+      uint16_t* lscale = (isv ? s_nvs : s_nks) + (t - a.pos);
+      quantize_row_wave<D>(src, lane, gcodes, gscale, lcodes, lscale);
+    }
+  }
+
 
   // Query operand (B of S^T = K Q^T): query row nb*16 + r, k = 8j + e <->
   // head dim 8*(KK*j + kk) + perm8(e), matching the K lane's dword order.
@@ -155,48 +278,13 @@ void decode_kernel(const DecodeArgs a) {
     for (int p = 0; p < NPB; ++p) o_acc[nb][p] = float4v{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Codes of the chunk starting at token c0, through buffer descriptors whose
-  // range ends at the split end t_end <= kv_len: the hardware returns zero for
-  // any row at or past it (those tokens are masked) without touching memory.
-  // So no load leaves the valid rows, the last chunk needs no clamping, and a
-  // chunk past the split can be "loaded" unconditionally (all zeros, no
-  // traffic), which keeps the prefetch branch-free: a conditional prefetch
-  // makes the compiler wait for every outstanding load where the paths join.
-  auto load_chunk = [&](int c0, ChunkRegs<D>& cr) {
-    const int rows_left = max(t_end - c0, 0);
-    const rsrc_t rk = make_rsrc(kbase + (int64_t)c0 * ROWB, rows_left * ROWB);
-    const rsrc_t rv = make_rsrc(vbase + (int64_t)c0 * ROWB, rows_left * ROWB);
-    const rsrc_t rks = make_rsrc(ksb + c0, rows_left * 2);
-    const rsrc_t rvs = make_rsrc(vsb + c0, rows_left * 2);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (KK == 4) {
-        const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
-      } else {
-        const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
-        cr.kw[kb][0] = w[0];
-        cr.kw[kb][1] = w[1];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
-    cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
-    cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
-  };
-
-  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
-  ChunkRegs<D> cur;
-  load_chunk(t_begin + wave * kChunk, cur);
-
   // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
-  auto process_chunk = [&](int c0, ChunkRegs<D>& cr) {
+  auto process_chunk = [&](int c0, ChunkRegs<D>& cr, int lim) {
       // ---- scales: each lane converts one, the wave reads its eight back.  A
       //      token at or past the split end gets bias -inf (score masked), so
       //      the score is one FMA on every chunk, full or not.
       s_sc[wave][lane] = f16bits_to_f32(lane < 32 ? cr.sk : cr.sv) * sc_mul;
-      if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < t_end) ? 0.0f : -INFINITY;
+      if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < lim) ? 0.0f : -INFINITY;
       const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
       const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
       const float4v sv0 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j]);
@@ -294,12 +382,42 @@ void decode_kernel(const DecodeArgs a) {
     asm volatile("" ::: "memory");
     if constexpr (kPrefetch) {
       ChunkRegs<D> nxt;
-      load_chunk(c0 + kWaves * kChunk, nxt);
-      process_chunk(c0, cur);
+      load_chunk(c0 + kWaves * kChunk, nxt, t_main);
+      process_chunk(c0, cur, t_main);
       cur = nxt;
     } else {
-      process_chunk(c0, cur);
-      load_chunk(c0 + kWaves * kChunk, cur);
+      process_chunk(c0, cur, t_main);
+      load_chunk(c0 + kWaves * kChunk, cur, t_main);
+    }
+  }
+
+  // ---- append mode: tail chunks [t_main, t_end).  Rows before pos come from
+  //      the cache (the load range ends at pos, so no row at or past it is
+  //      read), rows from pos on from the LDS copy of the new rows.
+  if (append) {
+    for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
+      if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
+      ChunkRegs<D> cr;
+      load_chunk(c0, cr, max(a.pos, c0));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
+        if (tk >= a.pos && tk < new_hi) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) cr.kw[kb][kk] = s_nk[(tk - a.pos) * DW + KK * j + kk];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tv = c0 + 8 * j + e;
+        if (tv >= a.pos && tv < new_hi) cr.vw[e] = s_nv[(tv - a.pos) * DW + (r % DW)];
+      }
+      const int ts = c0 + (lane & 31);
+      if (ts >= a.pos && ts < new_hi) {
+        cr.sk = s_nks[ts - a.pos];
+        cr.sv = s_nvs[ts - a.pos];
+      }
+      process_chunk(c0, cr, t_end);
     }
   }
 
@@ -461,7 +579,7 @@ void decode_kernel(const DecodeArgs a) {
 template <int D, int NB>
 hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
   dim3 grid((uint32_t)n_split, (uint32_t)Hkv, (uint32_t)B);
-  decode_kernel<D, NB><<<grid, dim3(64 * kWaves), 0, stream>>>(args);
+  decode_kernel<D, NB><<<grid, dim3(64 * waves_for(NB)), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -479,15 +597,18 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
                        int num_cus) {
   const int64_t chunks = (kv_len + kChunk - 1) / kChunk;
   const int64_t units = B * Hkv;
+  const int64_t rows_per_group = rows / units;
+  const int waves = waves_for(rows_per_group <= 16 ? 1 : rows_per_group <= 32 ? 2 : 4);
   int64_t ns;
   if (num_splits <= 0) {
-    // one workgroup (eight waves) per CU: measured best on MI355X for both a
-    // 128-group 8K-token and an 8-group 128K-token decode.  Every workgroup
-    // starts at once and streams its range at the shared HBM rate; more
-    // splits add per-split epilogue and merge latency without adding bandwidth
-    const int64_t target_wgs = (int64_t)(num_cus > 0 ? num_cus : 256);
+    // eight waves per CU (one 8-wave or two 4-wave workgroups): measured best
+    // on MI355X for both a 128-group 8K-token and an 8-group 128K-token
+    // decode.  Every workgroup starts at once and streams its range at the
+    // shared HBM rate; more splits add per-split epilogue and merge latency
+    // without adding bandwidth
+    const int64_t target_wgs = (int64_t)(num_cus > 0 ? num_cus : 256) * 8 / waves;
     ns = (target_wgs + units - 1) / units;
-    const int64_t max_ns = chunks / kWaves > 0 ? chunks / kWaves : 1;   // >= one chunk per wave
+    const int64_t max_ns = chunks / waves > 0 ? chunks / waves : 1;   // >= one chunk per wave
     if (ns > max_ns) ns = max_ns;
   } else {
     ns = num_splits;
@@ -523,10 +644,23 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
-                         void* workspace, hipStream_t stream) {
+                         void* workspace, const DecodeAppend* append, hipStream_t stream) {
   DecodeArgs a;
   a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.out = out; a.lse = lse;
+  a.k_new = nullptr; a.v_new = nullptr;
+  a.kc_w = nullptr; a.ks_w = nullptr; a.vc_w = nullptr; a.vs_w = nullptr;
+  a.pos = 0; a.n_new = 0;
+  if (append) {
+    a.k_new = append->k_new;
+    a.v_new = append->v_new;
+    a.kc_w = const_cast<uint8_t*>(kc);
+    a.ks_w = const_cast<uint16_t*>(ks);
+    a.vc_w = const_cast<uint8_t*>(vc);
+    a.vs_w = const_cast<uint16_t*>(vs);
+    a.n_new = (int)append->n_new;
+    a.pos = (int)(kv_len - append->n_new);
+  }
   a.part_o = nullptr; a.part_lse = nullptr; a.tickets = nullptr; a.part_bytes = 0;
   if (plan.n_split > 1) {
     const int64_t rows = B * Hq * Sq;

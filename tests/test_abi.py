@@ -20,6 +20,8 @@ def lib():
     L.qkv_quantize_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
     L.qkv_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp, sz, vp]
     L.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp]
+    L.qkv_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, f32, ci,
+                                    vp, vp, vp, sz, vp]
     L.qkv_last_error.restype = ctypes.c_char_p
     L.qkv_status_string.restype = ctypes.c_char_p
     L.qkv_decode_workspace_bytes.restype = sz
@@ -35,7 +37,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) >= {"qkv_quantize_append", "qkv_decode", "qkv_prefill", "qkv_decode_workspace_bytes",
+    assert set(names) >= {"qkv_quantize_append", "qkv_decode", "qkv_decode_append", "qkv_prefill",
+                          "qkv_quantize_append_kv", "qkv_decode_workspace_bytes",
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -127,3 +130,27 @@ def test_quantize_append_kv_argument_errors(lib):
     assert f(kc=P + 2) == 1
     assert f(B=0) == 1
     assert f(T=0, vs_=None) == 0
+
+
+def _dapp(lib, **kw):
+    a = dict(q=P, kn=P, vn=P, kc=P, ks=P, vc=P, vs=P, B=1, Hq=4, Hkv=2, Sq=1, pos=99, n=1, C=128, D=128,
+             scale=0.1, ns=0, out=P, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qkv_decode_append(a["q"], a["kn"], a["vn"], a["kc"], a["ks"], a["vc"], a["vs"], a["B"], a["Hq"],
+                                 a["Hkv"], a["Sq"], a["pos"], a["n"], a["C"], a["D"], a["scale"], a["ns"],
+                                 a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_decode_append_argument_errors(lib):
+    assert _dapp(lib, kn=None) == 1
+    assert b"new-row" in lib.qkv_last_error()
+    assert _dapp(lib, vn=P + 4) == 1            # misaligned new rows
+    assert _dapp(lib, n=0) == 2
+    assert _dapp(lib, n=65) == 2
+    assert _dapp(lib, pos=-1) == 1
+    assert _dapp(lib, pos=128) == 1             # pos + n_new > C
+    assert _dapp(lib, D=80) == 2
+    assert _dapp(lib, Sq=33) == 2               # G * Sq > 64
+    assert _dapp(lib, ns=2) == 3                # needs a workspace
+    assert b"qkv_decode_append" in lib.qkv_last_error()
+    assert _dapp(lib, q=None) == 1

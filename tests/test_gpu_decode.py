@@ -138,3 +138,79 @@ def test_split_merge_sees_fresh_partials(case):
             assert_close(out, ro, f"{case} input {t}")
         else:
             assert torch.equal(out, first[t]), f"{case}: iteration {it} differs"
+
+
+APPEND_CASES = [
+    # B, Hq, Hkv, Sq, pos, n_new, C, D, num_splits
+    (2, 8, 2, 1, 999, 1, 1024, 128, 0),
+    (1, 64, 8, 1, 4096, 1, 4100, 128, 0),
+    (2, 32, 8, 2, 777, 2, 800, 128, 3),
+    (1, 8, 2, 5, 124, 5, 129, 64, 0),
+    (1, 4, 1, 16, 300, 16, 320, 128, 0),    # 64 rows per group: the four-wave variant
+    (1, 8, 2, 4, 1534, 4, 2048, 128, 4),    # new rows straddle the split boundary at 1536
+    (1, 4, 2, 3, 0, 3, 8, 64, 0),           # the whole cache is new
+    (1, 2, 2, 64, 100, 64, 200, 64, 0),     # the most new rows one call takes
+    (3, 12, 4, 1, 2049, 2, 2100, 128, 0),   # two new rows, one query row
+]
+
+
+def _new_rows(seed, B, Hkv, n, D):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+    v = (rng.standard_normal((B, Hkv, n, D)) * 2).astype(np.float32)
+    k[0, 0, 0, :3] = 0.0      # exact zeros and a row with a large channel
+    v[-1, -1, -1, 5] *= 9.0
+    return k, v
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[str(c) for c in APPEND_CASES])
+def test_decode_append_equals_append_then_decode(case):
+    """The one-launch step writes the same cache rows and gives bit-identical
+    out and lse as quantize_append_kv followed by decode; both match the oracle."""
+    B, Hq, Hkv, Sq, pos, n_new, C, D, ns = case
+    q, kc, ks, vc, vs = random_case(sum(case), B, Hq, Hkv, Sq, max(pos, 1), D, C)
+    k_new, v_new = _new_rows(sum(case) + 1, B, Hkv, n_new, D)
+    kn, vn = torch.from_numpy(k_new).to(DEV), torch.from_numpy(v_new).to(DEV)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    sep = cache_to_dev(kc, ks, vc, vs)
+    fused = cache_to_dev(kc, ks, vc, vs)
+    qkv.quantize_append_kv(kn, vn, sep, pos)
+    o1, l1 = qkv.decode(q_to_dev(q), sep, pos + n_new, softmax_scale=scale, num_splits=ns, return_lse=True)
+    o2, l2 = qkv.decode_append(q_to_dev(q), kn, vn, fused, pos, softmax_scale=scale, num_splits=ns,
+                               return_lse=True)
+    torch.cuda.synchronize()
+    for a, b in zip(sep.tensors(), fused.tensors()):
+        assert torch.equal(a, b), "cache rows differ"
+    assert torch.equal(o1, o2), f"out differs: {float((o1 - o2).abs().max())}"
+    assert torch.equal(l1, l2)
+    rkc, rks = oracle.quantize_rows(k_new)
+    rvc, rvs = oracle.quantize_rows(v_new)
+    kc2, ks2, vc2, vs2 = kc.copy(), ks.copy(), vc.copy(), vs.copy()
+    kc2[:, :, pos:pos + n_new], ks2[:, :, pos:pos + n_new] = rkc, rks
+    vc2[:, :, pos:pos + n_new], vs2[:, :, pos:pos + n_new] = rvc, rvs
+    assert np.array_equal(fused.k_codes.cpu().numpy(), kc2)
+    assert np.array_equal(fused.v_scales.view(torch.int16).cpu().numpy().view(np.uint16), vs2)
+    ro, rl = oracle.attention(q, kc2, ks2, vc2, vs2, pos + n_new, scale)
+    assert_close(o2, ro, f"decode_append {case}")
+    assert compare(l2, rl)[0] < 1e-3
+
+
+def test_decode_append_steps_reuse_workspace():
+    """Ten consecutive one-token steps on one cache and one workspace, each
+    checked bit for bit against the two-launch step on a twin cache."""
+    B, Hq, Hkv, D, C, L0 = 2, 16, 4, 128, 3100, 3000
+    q, kc, ks, vc, vs = random_case(11, B, Hq, Hkv, 1, L0, D, C)
+    qd = q_to_dev(q)
+    sep, fused = cache_to_dev(kc, ks, vc, vs), cache_to_dev(kc, ks, vc, vs)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    for step in range(10):
+        kn, vn = (torch.from_numpy(t).to(DEV) for t in _new_rows(100 + step, B, Hkv, 1, D))
+        pos = L0 + step
+        qkv.quantize_append_kv(kn, vn, sep, pos)
+        o1 = qkv.decode(qd, sep, pos + 1, softmax_scale=0.09, num_splits=7)
+        o2 = qkv.decode_append(qd, kn, vn, fused, pos, softmax_scale=0.09, num_splits=7, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"step {step}"
+        assert int((ws[:64] != 0).sum()) == 0, "tickets not returned to zero"
+    for a, b in zip(sep.tensors(), fused.tensors()):
+        assert torch.equal(a, b)
