@@ -175,6 +175,53 @@ qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * (a)+(b) over a ragged and optionally paged cache: the serving form of the
+ * decode step (TurboAttention §2.1: during decoding every sequence of the
+ * batch appends its new token's K and V to its own cache and attends it;
+ * sequences differ in length).  Sequence b attends its own rows
+ * [0, L_b), L_b = kv_lens[b] + n_new, after first quantizing its n_new new
+ * rows into rows [kv_lens[b], L_b) exactly as qkv_quantize_append_kv does.
+ * Per sequence, out, lse and the rows written are the same as qkv_decode_append
+ * (n_new > 0) or qkv_decode (n_new = 0) on that sequence's rows alone.
+ *   k_codes, v_codes   uint8 [num_pages, Hkv, page_size, D/2] page pool,
+ *                      device, 16-byte aligned
+ *   k_scales, v_scales uint16 [num_pages, Hkv, page_size], device
+ *   block_table  int32 [B, max_pages], device, or NULL.  Token t of sequence
+ *                b is row t % page_size of page block_table[b, t / page_size]
+ *                (ids outside [0, num_pages) are clamped into it, so no access
+ *                leaves the pool).  Needs page_size % 32 == 0.
+ *                NULL: sequence b owns page b (a contiguous cache
+ *                [B, Hkv, C, D/2] is the pool with page_size = C); needs
+ *                max_pages == 1 and num_pages >= B, any page_size.
+ *   kv_lens      int32 [B], device: rows already cached per sequence (before
+ *                this call's new rows), or NULL: every sequence holds
+ *                max_kv_len - n_new.  Values are clamped to
+ *                [0, max_kv_len - n_new].  A sequence with L_b = 0 gets
+ *                out = 0 and lse = -inf.
+ *   k_new, v_new float [B, Hkv, n_new, D], device, 16-byte aligned, read
+ *                only when n_new > 0 (NULL allowed otherwise); must not alias
+ *                the cache.  The pages they land in must belong to one
+ *                sequence each.
+ *   n_new        0..64 rows appended per sequence (0: attend only)
+ *   max_kv_len   upper bound of every L_b, 1 <= max_kv_len <= max_pages *
+ *                page_size, >= n_new.  The split plan and the workspace size
+ *                follow it (qkv_decode_workspace_bytes with kv_len =
+ *                max_kv_len); splits past a sequence's length do no work.
+ *   other arguments as for qkv_decode (same workspace and tickets contract).
+ * Requires the qkv_decode requirements with kv_len = max_kv_len and
+ * C = max_pages * page_size.
+ */
+qkv_status qkv_decode_paged(const uint16_t* q, const float* k_new, const float* v_new,
+                            uint8_t* k_codes, uint16_t* k_scales,
+                            uint8_t* v_codes, uint16_t* v_scales,
+                            const int32_t* block_table, const int32_t* kv_lens,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t n_new,
+                            int64_t max_kv_len, int64_t page_size, int64_t max_pages,
+                            int64_t num_pages, int64_t D, float softmax_scale, int num_splits,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * (c) Prefill attention, tiled with online softmax (FlashAttention tiling,
  * TurboAttention §2.2).  causal = 0: every row sees [0, kv_len).
  * causal = 1: query row i (0 <= i < Sq) is token kv_len - Sq + i and sees

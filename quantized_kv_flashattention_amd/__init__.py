@@ -29,6 +29,7 @@ __all__ = [
     "quantize_append_kv",
     "decode",
     "decode_append",
+    "decode_paged",
     "prefill",
     "decode_workspace_bytes",
     "decode_auto_splits",
@@ -75,6 +76,9 @@ def _load():
     lib.qkv_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                       f32, ci, vp, vp, vp, sz, vp]
     lib.qkv_prefill.restype = ci
+    lib.qkv_decode_paged.restype = ci
+    lib.qkv_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                     i64, i64, i64, f32, ci, vp, vp, vp, sz, vp]
     lib.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                 vp, vp, vp]
     return lib
@@ -191,6 +195,24 @@ def _attn_args(q, cache_tensors, kv_len):
     return B, Hq, Hkv, Sq, int(kv_len), C, D
 
 
+def _outputs(q, out, lse, return_lse):
+    """Allocate or check ``out [B, Hq, Sq, D]`` fp32 and (on request) ``lse [B, Hq, Sq]``."""
+    B, Hq, Sq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    else:
+        _req(out, "out", torch.float32, 4)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must have q's shape and device")
+    if lse is not None:
+        _req(lse, "lse", torch.float32, 3)
+        if lse.shape != (B, Hq, Sq) or lse.device != q.device:
+            raise ValueError("lse must be [B, Hq, Sq] on q's device")
+    elif return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
 def _scale(softmax_scale, D):
     return float(1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
 
@@ -227,12 +249,7 @@ def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False,
     """Decode attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)`` (no mask)."""
     tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
     B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len)
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
-    else:
-        _req(out, "out", torch.float32, 4)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(q, out, lse, return_lse)
     need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
     if workspace is None and need > 0:
         workspace = _workspace(q.device, B * Hkv, need)
@@ -258,12 +275,7 @@ def decode_append(q, k_new, v_new, cache, pos, softmax_scale=None, num_splits=0,
     B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, int(pos) + n_new)
     if k_new.shape != (B, Hkv, n_new, D):
         raise ValueError("k_new shape does not match the cache")
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
-    else:
-        _req(out, "out", torch.float32, 4)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(q, out, lse, return_lse)
     need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
     if workspace is None and need > 0:
         workspace = _workspace(q.device, B * Hkv, need)
@@ -276,16 +288,80 @@ def decode_append(q, k_new, v_new, cache, pos, softmax_scale=None, num_splits=0,
     return (out, lse) if return_lse else out
 
 
+def decode_paged(q, cache, kv_lens=None, block_table=None, k_new=None, v_new=None, max_kv_len=None,
+                 softmax_scale=None, num_splits=0, return_lse=False, out=None, lse=None, workspace=None):
+    """Decode step over a ragged, optionally paged cache, in one launch.
+
+    Sequence ``b`` first gets its new rows ``k_new``/``v_new [B, Hkv, n_new, D]``
+    (optional, fp32) quantized into its rows ``[kv_lens[b], kv_lens[b]+n_new)``,
+    then ``q[b]`` attends its rows ``[0, kv_lens[b]+n_new)``.
+
+    * ``cache``: a :class:`KVCache` whose tensors are a page pool
+      ``[num_pages, Hkv, page_size, D/2]`` / ``[num_pages, Hkv, page_size]``.
+      Without ``block_table`` it is an ordinary cache ``[B', Hkv, C, ...]``,
+      ``B' >= B``, and sequence ``b`` uses entry ``b``.
+    * ``kv_lens``: int32 ``[B]`` device tensor of rows already cached (None:
+      every sequence holds ``max_kv_len - n_new``).
+    * ``block_table``: int32 ``[B, max_pages]`` device tensor of page ids
+      (``page_size`` a multiple of 32), or None.
+    * ``max_kv_len``: upper bound of ``kv_lens[b] + n_new``; the split plan and
+      the workspace follow it (default: the capacity ``max_pages * page_size``;
+      a tight bound avoids splits that find nothing to do).
+    """
+    tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    _req(q, "q", torch.bfloat16, 4)
+    kc, ks, vc, vs = tensors
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    B, Hq, Sq, D = q.shape
+    num_pages, Hkv, page_size, half = kc.shape
+    if half * 2 != D or vc.shape != kc.shape or ks.shape != kc.shape[:3] or vs.shape != ks.shape:
+        raise ValueError("cache shape does not match q")
+    if block_table is not None:
+        _req(block_table, "block_table", torch.int32, 2)
+        if block_table.shape[0] != B or block_table.device != q.device:
+            raise ValueError("block_table must be [B, max_pages] on q's device")
+        max_pages = block_table.shape[1]
+    else:
+        max_pages = 1
+    if kv_lens is not None:
+        _req(kv_lens, "kv_lens", torch.int32, 1)
+        if kv_lens.shape[0] != B or kv_lens.device != q.device:
+            raise ValueError("kv_lens must be [B] on q's device")
+    n_new = 0
+    if k_new is not None or v_new is not None:
+        if k_new is None or v_new is None:
+            raise ValueError("pass both k_new and v_new, or neither")
+        _req(k_new, "k_new", torch.float32, 4)
+        _req(v_new, "v_new", torch.float32, 4)
+        n_new = k_new.shape[2]
+        if k_new.shape != (B, Hkv, n_new, D) or v_new.shape != k_new.shape or \
+                k_new.device != q.device or v_new.device != q.device:
+            raise ValueError("k_new and v_new must be [B, Hkv, n_new, D] on q's device")
+    if max_kv_len is None:
+        max_kv_len = max_pages * page_size
+    max_kv_len = int(max_kv_len)
+    out, lse = _outputs(q, out, lse, return_lse)
+    need = decode_workspace_bytes(B, Hq, Hkv, Sq, max_kv_len, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, B * Hkv, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.qkv_decode_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                 _ptr(block_table), _ptr(kv_lens), B, Hq, Hkv, Sq, n_new, max_kv_len,
+                                 page_size, max_pages, num_pages, D, _scale(softmax_scale, D),
+                                 int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                 _stream(q)))
+    return (out, lse) if return_lse else out
+
+
 def prefill(q, cache, kv_len, causal, softmax_scale=None, return_lse=False, out=None, lse=None):
     """Prefill attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)``."""
     tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
     B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len)
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
-    else:
-        _req(out, "out", torch.float32, 4)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(q, out, lse, return_lse)
     kc, ks, vc, vs = tensors
     _check(_lib.qkv_prefill(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
                             C, D, _scale(softmax_scale, D), int(bool(causal)), _ptr(out), _ptr(lse),

@@ -147,13 +147,16 @@ size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq
 
 namespace {
 
-// qkv_decode and qkv_decode_append after their own argument checks.
+// The decode entry points after their own argument checks.  C is the row
+// capacity of one sequence (kv_len <= C); with a ragged / paged cache the
+// launch's per-(batch, KV head) row stride is the page size instead.
 qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
                          const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
                          float softmax_scale, int num_splits, float* out, float* lse,
                          void* workspace, size_t workspace_bytes,
-                         const qkvfa::DecodeAppend* append, void* stream, const char* fn) {
+                         const qkvfa::DecodeAppend* append, const qkvfa::DecodeVarlen* varlen,
+                         void* stream, const char* fn) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -171,8 +174,9 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
       return fail(QKV_ERR_INVALID_ARG, f + ": workspace must be 16-byte aligned");
   }
   return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
-                                         kv_len, C, (int)D, softmax_scale, plan, out, lse,
-                                         workspace, append, static_cast<hipStream_t>(stream)),
+                                         kv_len, varlen ? varlen->page_size : C, (int)D,
+                                         softmax_scale, plan, out, lse, workspace, append, varlen,
+                                         static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -187,7 +191,7 @@ qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t*
                       void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D,
                        softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr,
-                       stream, "qkv_decode");
+                       nullptr, stream, "qkv_decode");
 }
 
 qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float* v_new,
@@ -207,7 +211,49 @@ qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float*
   const qkvfa::DecodeAppend app = {k_new, v_new, n_new};
   return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, pos + n_new, C, D,
                        softmax_scale, num_splits, out, lse, workspace, workspace_bytes, &app,
-                       stream, "qkv_decode_append");
+                       nullptr, stream, "qkv_decode_append");
+}
+
+qkv_status qkv_decode_paged(const uint16_t* q, const float* k_new, const float* v_new,
+                            uint8_t* k_codes, uint16_t* k_scales, uint8_t* v_codes,
+                            uint16_t* v_scales, const int32_t* block_table, const int32_t* kv_lens,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t n_new,
+                            int64_t max_kv_len, int64_t page_size, int64_t max_pages,
+                            int64_t num_pages, int64_t D, float softmax_scale, int num_splits,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const char* fn = "qkv_decode_paged";
+  if (page_size < 1 || max_pages < 1 || num_pages < 1)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_paged: page_size, max_pages and num_pages must be >= 1");
+  if (page_size > 0x7FFFFFFFll / max_pages || num_pages > 0x7FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_paged: max_pages * page_size and num_pages must stay below 2^31");
+  if (block_table) {
+    if (page_size % 32 != 0)
+      return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_paged: page_size must be a multiple of 32");
+    if (!aligned(block_table, 4))
+      return fail(QKV_ERR_INVALID_ARG, "qkv_decode_paged: misaligned block_table");
+  } else if (max_pages != 1 || num_pages < B) {
+    return fail(QKV_ERR_INVALID_ARG,
+                "qkv_decode_paged: without a block table sequence b owns page b: need max_pages == 1 "
+                "and num_pages >= B");
+  }
+  if (kv_lens && !aligned(kv_lens, 4))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_paged: misaligned kv_lens");
+  if (n_new < 0 || n_new > 64)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_paged: n_new must be in [0, 64]");
+  if (max_kv_len < n_new)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_paged: need max_kv_len >= n_new");
+  qkvfa::DecodeAppend app = {k_new, v_new, n_new};
+  if (n_new > 0) {
+    if (!k_new || !v_new)
+      return fail(QKV_ERR_INVALID_ARG, "qkv_decode_paged: null new-row pointer");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+      return fail(QKV_ERR_INVALID_ARG, "qkv_decode_paged: k_new and v_new must be 16-byte aligned");
+  }
+  const qkvfa::DecodeVarlen vl = {kv_lens, block_table, page_size, max_pages, num_pages};
+  return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, max_kv_len,
+                       max_pages * page_size, D, softmax_scale, num_splits, out, lse, workspace,
+                       workspace_bytes, n_new > 0 ? &app : nullptr, &vl, stream, fn);
 }
 
 qkv_status qkv_prefill(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,

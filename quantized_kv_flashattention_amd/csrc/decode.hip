@@ -62,6 +62,7 @@ constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (fits s_o at D = 64)
 constexpr int kMaxNew = 64;                 // rows one append-mode call may add
+constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -84,6 +85,15 @@ struct DecodeArgs {
   uint8_t* vc_w;
   uint16_t* vs_w;
   int pos, n_new;
+  // ragged lengths (kv_lens != nullptr): sequence b attends its own
+  // min(max(kv_lens[b], 0), len_cap) cached rows (+ n_new appended ones).
+  // paged cache (block_table != nullptr, PAGED kernels): the cache arrays are
+  // page pools [num_pages, Hkv, page_size, ...]; token t of sequence b sits in
+  // page block_table[b * max_pages + t / page_size] (clamped into the pool),
+  // row t % page_size.
+  const int32_t* kv_lens;
+  const int32_t* block_table;
+  int len_cap, page_size, max_pages, num_pages;
   int64_t C;
   int Hq, Hkv, G, Sq, kv_len, split_len, n_split;
   float qk_log2;
@@ -130,7 +140,7 @@ struct ChunkRegs {
 // workgroup (two waves per SIMD) per CU; the one-row-block kernel still fits
 // 128 VGPRs so that concurrent launches can share a CU.  The 64-row variant
 // skips the one-chunk prefetch to stay within 256 VGPRs.
-template <int D, int NB>
+template <int D, int NB, bool PAGED>
 __global__ __launch_bounds__(64 * waves_for(NB)) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
   constexpr int kWaves = waves_for(NB);
@@ -152,6 +162,8 @@ void decode_kernel(const DecodeArgs a) {
   __shared__ __align__(16) uint32_t s_nv[kMaxNew * DW];
   __shared__ uint16_t s_nks[kMaxNew];
   __shared__ uint16_t s_nvs[kMaxNew];
+  // paged cache: the page ids of this split's tokens (from page t_begin / P on)
+  __shared__ int s_pid[PAGED ? kMaxSplitPages : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -160,16 +172,44 @@ void decode_kernel(const DecodeArgs a) {
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  const int G = a.G, Sq = a.Sq, kv_len = a.kv_len;
+  const int G = a.G, Sq = a.Sq;
   const int R = G * Sq;
+  const bool append = a.k_new != nullptr;
+  // rows this sequence attends, and where its new rows start (append mode)
+  int pos_b = a.pos;
+  int L_b = a.kv_len;
+  if (a.kv_lens != nullptr) {
+    const int lb = min(max(__builtin_amdgcn_readfirstlane(a.kv_lens[b]), 0), a.len_cap);
+    pos_b = lb;
+    L_b = lb + (append ? a.n_new : 0);
+  }
   const int t_begin = split * a.split_len;
-  const int t_end = min(kv_len, t_begin + a.split_len);
+  const int t_end = min(L_b, t_begin + a.split_len);   // <= t_begin: nothing to attend here
 
+  // Row index (in the cache arrays' row space) of token t of this (batch, KV
+  // head): contiguous cache row (b, g, t), or row t % P of its page.
   const int64_t kvrow0 = ((int64_t)b * a.Hkv + g) * a.C;
-  const uint8_t* kbase = a.kc + kvrow0 * ROWB;
-  const uint8_t* vbase = a.vc + kvrow0 * ROWB;
-  const uint16_t* ksb = a.ks + kvrow0;
-  const uint16_t* vsb = a.vs + kvrow0;
+  const int P = PAGED ? a.page_size : 1;
+  const int pg0 = PAGED ? t_begin / P : 0;
+  // pages of this split whose ids are cached in LDS
+  const int npg = (PAGED && t_end > t_begin) ? min((t_end - 1) / P - pg0 + 1, kMaxSplitPages) : 0;
+  auto page_of = [&](int t) -> int64_t {   // from the table in global memory
+    const int idx = min(t / P, a.max_pages - 1);
+    const int pid = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_pages + idx]);
+    return min(max(pid, 0), a.num_pages - 1);
+  };
+  // from_lds: the page id comes from this split's LDS copy of its table
+  // entries (filled before the chunk loop); pages past the copy (beyond its
+  // capacity, or a prefetch past the split end) are read from the table.
+  auto row_of = [&](int t, bool from_lds) -> int64_t {
+    if constexpr (PAGED) {
+      const int li = t / P - pg0;
+      const int64_t pid = (from_lds && li < npg) ? (int64_t)s_pid[li] : page_of(t);
+      return (pid * a.Hkv + g) * P + t % P;
+    } else {
+      return kvrow0 + t;
+    }
+  };
   const float sc_mul = (lane < 32) ? a.qk_log2 : 1.0f;
 
   // Loop-invariant per-lane byte offsets inside a chunk.
@@ -178,14 +218,13 @@ void decode_kernel(const DecodeArgs a) {
   const uint32_t offs = (uint32_t)(2 * (lane & 31));
 
   // ---- append mode: this split's new rows [new_lo, new_hi)
-  const bool append = a.k_new != nullptr;
-  const int new_lo = append ? max(a.pos, t_begin) : 0;
-  const int new_hi = append ? min(a.pos + a.n_new, t_end) : 0;
+  const int new_lo = append ? max(pos_b, t_begin) : 0;
+  const int new_hi = append ? min(pos_b + a.n_new, t_end) : 0;
   // The chunk loop covers the split up to the first chunk that holds a new
   // row; the remaining (tail) chunks are handled after it, each by the wave
   // the plain decode gives it, so the arithmetic is the plain decode's.
   const int t_main =
-      append ? min(t_end, t_begin + (max(a.pos, t_begin) - t_begin) / kChunk * kChunk) : t_end;
+      append ? min(t_end, t_begin + (max(pos_b, t_begin) - t_begin) / kChunk * kChunk) : t_end;
 
   // Codes of the chunk starting at token c0, through buffer descriptors whose
   // range ends at t_main <= kv_len (the split end, before any new rows): the
@@ -195,12 +234,16 @@ void decode_kernel(const DecodeArgs a) {
   // chunk past the split can be "loaded" unconditionally (all zeros, no
   // traffic), which keeps the prefetch branch-free: a conditional prefetch
   // makes the compiler wait for every outstanding load where the paths join.
-  auto load_chunk = [&](int c0, ChunkRegs<D>& cr, int lim) {
-    const int rows_left = max(lim - c0, 0);
-    const rsrc_t rk = make_rsrc(kbase + (int64_t)c0 * ROWB, rows_left * ROWB);
-    const rsrc_t rv = make_rsrc(vbase + (int64_t)c0 * ROWB, rows_left * ROWB);
-    const rsrc_t rks = make_rsrc(ksb + c0, rows_left * 2);
-    const rsrc_t rvs = make_rsrc(vsb + c0, rows_left * 2);
+  auto load_chunk = [&](int c0, ChunkRegs<D>& cr, int lim, bool from_lds) {
+    // a chunk is 32 rows; with a paged cache it never straddles a page.  The
+    // clamp is made scalar explicitly: computed in a vector register, the
+    // descriptor would look divergent and each load would become a loop.
+    const int rows_left = __builtin_amdgcn_readfirstlane(min(max(lim - c0, 0), kChunk));
+    const int64_t row0 = row_of(c0, from_lds);
+    const rsrc_t rk = make_rsrc(a.kc + row0 * ROWB, rows_left * ROWB);
+    const rsrc_t rv = make_rsrc(a.vc + row0 * ROWB, rows_left * ROWB);
+    const rsrc_t rks = make_rsrc(a.ks + row0, rows_left * 2);
+    const rsrc_t rvs = make_rsrc(a.vs + row0, rows_left * 2);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (KK == 4) {
@@ -221,7 +264,7 @@ void decode_kernel(const DecodeArgs a) {
 
   const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
   ChunkRegs<D> cur;
-  load_chunk(t_begin + wave * kChunk, cur, t_main);
+  load_chunk(t_begin + wave * kChunk, cur, t_main, false);
 
   // ---- append mode: quantize the new rows (one wave per row and tensor,
   //      from the last wave down: with one row block the first half of the
@@ -231,15 +274,23 @@ void decode_kernel(const DecodeArgs a) {
     for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
       const int t = new_lo + (task >> 1);
       const bool isv = (task & 1) != 0;
-      const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - a.pos)) * D;
-      uint8_t* gcodes = (isv ? a.vc_w : a.kc_w) + (kvrow0 + t) * ROWB;
-      uint16_t* gscale = (isv ? a.vs_w : a.ks_w) + kvrow0 + t;
-      uint8_t* lcodes = reinterpret_cast<uint8_t*>(isv ? s_nv : s_nk) + (t - a.pos) * ROWB;
-      uint16_t* lscale = (isv ? s_nvs : s_nks) + (t - a.pos);
+      const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - pos_b)) * D;
+      const int64_t row = row_of(t, false);
+      uint8_t* gcodes = (isv ? a.vc_w : a.kc_w) + row * ROWB;
+      uint16_t* gscale = (isv ? a.vs_w : a.ks_w) + row;
+      uint8_t* lcodes = reinterpret_cast<uint8_t*>(isv ? s_nv : s_nk) + (t - pos_b) * ROWB;
+      uint16_t* lscale = (isv ? s_nvs : s_nks) + (t - pos_b);
       quantize_row_wave<D>(src, lane, gcodes, gscale, lcodes, lscale);
     }
   }
 
+
+  if constexpr (PAGED) {
+    for (int i = threadIdx.x; i < npg; i += 64 * kWaves) {
+      const int idx = min(pg0 + i, a.max_pages - 1);
+      s_pid[i] = min(max(a.block_table[(int64_t)b * a.max_pages + idx], 0), a.num_pages - 1);
+    }
+  }
 
   // Query operand (B of S^T = K Q^T): query row nb*16 + r, k = 8j + e <->
   // head dim 8*(KK*j + kk) + perm8(e), matching the K lane's dword order.
@@ -382,12 +433,12 @@ void decode_kernel(const DecodeArgs a) {
     asm volatile("" ::: "memory");
     if constexpr (kPrefetch) {
       ChunkRegs<D> nxt;
-      load_chunk(c0 + kWaves * kChunk, nxt, t_main);
+      load_chunk(c0 + kWaves * kChunk, nxt, t_main, true);
       process_chunk(c0, cur, t_main);
       cur = nxt;
     } else {
       process_chunk(c0, cur, t_main);
-      load_chunk(c0 + kWaves * kChunk, cur, t_main);
+      load_chunk(c0 + kWaves * kChunk, cur, t_main, true);
     }
   }
 
@@ -398,24 +449,24 @@ void decode_kernel(const DecodeArgs a) {
     for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
       if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
       ChunkRegs<D> cr;
-      load_chunk(c0, cr, max(a.pos, c0));
+      load_chunk(c0, cr, max(pos_b, c0), true);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
-        if (tk >= a.pos && tk < new_hi) {
+        if (tk >= pos_b && tk < new_hi) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) cr.kw[kb][kk] = s_nk[(tk - a.pos) * DW + KK * j + kk];
+          for (int kk = 0; kk < KK; ++kk) cr.kw[kb][kk] = s_nk[(tk - pos_b) * DW + KK * j + kk];
         }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tv = c0 + 8 * j + e;
-        if (tv >= a.pos && tv < new_hi) cr.vw[e] = s_nv[(tv - a.pos) * DW + (r % DW)];
+        if (tv >= pos_b && tv < new_hi) cr.vw[e] = s_nv[(tv - pos_b) * DW + (r % DW)];
       }
       const int ts = c0 + (lane & 31);
-      if (ts >= a.pos && ts < new_hi) {
-        cr.sk = s_nks[ts - a.pos];
-        cr.sv = s_nvs[ts - a.pos];
+      if (ts >= pos_b && ts < new_hi) {
+        cr.sk = s_nks[ts - pos_b];
+        cr.sv = s_nvs[ts - pos_b];
       }
       process_chunk(c0, cr, t_end);
     }
@@ -457,11 +508,13 @@ void decode_kernel(const DecodeArgs a) {
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+      // every wave empty (a split past the sequence's length): weights 0
+      const float Mz = (M == -INFINITY) ? 0.0f : M;
       float4v acc = {0.f, 0.f, 0.f, 0.f};
       float den = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float wt = fast_exp2(s_m[w][rr] - M);   // empty waves: exp2(-inf) = 0
+        const float wt = fast_exp2(s_m[w][rr] - Mz);   // empty waves: exp2(-inf) = 0
         acc += wt * *reinterpret_cast<const float4v*>(&s_o[w][rr * OSTR + d]);
         den += wt * s_l[w][rr];
       }
@@ -469,8 +522,9 @@ void decode_kernel(const DecodeArgs a) {
       const int hg = row / Sq;
       const int sq = row - hg * Sq;
       const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + sq;
-      const float inv = 1.0f / den;
-      const float lse2 = M + log2f(den);
+      // nothing attended: output 0, LSE -inf
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      const float lse2 = den > 0.0f ? M + log2f(den) : -INFINITY;
       if (direct) {
         *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * inv;
         if (d == 0 && a.lse) a.lse[grow] = lse2 * kLn2;
@@ -502,12 +556,14 @@ void decode_kernel(const DecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
   const int n_split = a.n_split;
-  // (1) every split's LSE of this group -> LDS (the wave-merge buffer is free
+  // splits that start before this sequence's length; the rest attended nothing
+  const int n_live = min(n_split, (L_b + a.split_len - 1) / a.split_len);
+  // (1) every live split's LSE of this group -> LDS (the wave-merge buffer is free
   //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
   float* s_w = &s_o[0][0];
   __shared__ float s_den[64];
   {
-    const int total = R * n_split;
+    const int total = R * n_live;
     for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
       float v[8];
 #pragma unroll
@@ -515,10 +571,10 @@ void decode_kernel(const DecodeArgs a) {
         const int idx = base + u * 64 * kWaves;
         v[u] = -INFINITY;
         if (idx < total) {
-          const int row = idx / n_split;
+          const int row = idx / n_live;
           const int hg = row / Sq;
           const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
-          v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_split), __ATOMIC_RELAXED,
+          v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -530,13 +586,13 @@ void decode_kernel(const DecodeArgs a) {
   __syncthreads();
   // (2) per row: max, weights 2^(lse_s - max) (in place), their sum -- one wave per row
   for (int row = wave; row < R; row += kWaves) {
-    float* wr = s_w + row * n_split;
+    float* wr = s_w + row * n_live;
     float M = -INFINITY;
-    for (int s = lane; s < n_split; s += 64) M = fmaxf(M, wr[s]);
+    for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
     float den = 0.0f;
-    for (int s = lane; s < n_split; s += 64) {
+    for (int s = lane; s < n_live; s += 64) {
       const float w = fast_exp2(wr[s] - M);
       wr[s] = w;
       den += w;
@@ -547,7 +603,7 @@ void decode_kernel(const DecodeArgs a) {
       s_den[row] = den;
       const int hg = row / Sq;
       const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
-      if (a.lse) a.lse[grow] = (M + log2f(den)) * kLn2;
+      if (a.lse) a.lse[grow] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
@@ -557,21 +613,22 @@ void decode_kernel(const DecodeArgs a) {
     const int d = 4 * (idx - row * (D / 4));
     const int hg = row / Sq;
     const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
-    const float* wr = s_w + row * n_split;
+    const float* wr = s_w + row * n_live;
     const uint32_t off0 = (uint32_t)((grow * n_split * D + d) * 4);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_split; s0 += 16) {
+    for (int s0 = 0; s0 < n_live; s0 += 16) {
       float4v o[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        o[u] = (s0 + u < n_split)
+        o[u] = (s0 + u < n_live)
                    ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
                    : float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (s0 + u < n_split) acc += wr[s0 + u] * o[u];
+        if (s0 + u < n_live) acc += wr[s0 + u] * o[u];
     }
-    *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (1.0f / s_den[row]);
+    const float den = s_den[row];
+    *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (den > 0.0f ? 1.0f / den : 0.0f);
   }
   if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -579,7 +636,10 @@ void decode_kernel(const DecodeArgs a) {
 template <int D, int NB>
 hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
   dim3 grid((uint32_t)n_split, (uint32_t)Hkv, (uint32_t)B);
-  decode_kernel<D, NB><<<grid, dim3(64 * waves_for(NB)), 0, stream>>>(args);
+  if (args.block_table != nullptr)
+    decode_kernel<D, NB, true><<<grid, dim3(64 * waves_for(NB)), 0, stream>>>(args);
+  else
+    decode_kernel<D, NB, false><<<grid, dim3(64 * waves_for(NB)), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -644,7 +704,8 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
-                         void* workspace, const DecodeAppend* append, hipStream_t stream) {
+                         void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
+                         hipStream_t stream) {
   DecodeArgs a;
   a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.out = out; a.lse = lse;
@@ -660,6 +721,16 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
     a.vs_w = const_cast<uint16_t*>(vs);
     a.n_new = (int)append->n_new;
     a.pos = (int)(kv_len - append->n_new);
+  }
+  a.kv_lens = nullptr; a.block_table = nullptr;
+  a.len_cap = 0; a.page_size = 0; a.max_pages = 0; a.num_pages = 0;
+  if (varlen) {
+    a.kv_lens = varlen->kv_lens;
+    a.block_table = varlen->block_table;
+    a.len_cap = (int)(kv_len - a.n_new);
+    a.page_size = (int)varlen->page_size;
+    a.max_pages = (int)varlen->max_pages;
+    a.num_pages = (int)varlen->num_pages;
   }
   a.part_o = nullptr; a.part_lse = nullptr; a.tickets = nullptr; a.part_bytes = 0;
   if (plan.n_split > 1) {

@@ -25,9 +25,19 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
 // Bytes of decode workspace: split partials plus one ticket per (batch, KV head).
 size_t decode_workspace_bytes(int64_t rows, int64_t units, int D, int n_split);
 
+// Ragged / paged cache (decode): per-sequence lengths and an optional page
+// table; see the kernel's argument block for the meaning.  kv_len is then the
+// upper bound of every sequence's attended length (cached + new rows).
+struct DecodeVarlen {
+  const int32_t* kv_lens;       // [B] rows cached per sequence, or null (all kv_len - n_new)
+  const int32_t* block_table;   // [B, max_pages] page ids, or null (contiguous cache)
+  int64_t page_size, max_pages, num_pages;
+};
+
 // Append mode of a decode launch: n_new fp32 rows [B, Hkv, n_new, D] of K and
-// V are quantized into cache rows [kv_len - n_new, kv_len) first; the cache
-// pointers passed to launch_decode must then be writable.
+// V are quantized into cache rows [kv_len - n_new, kv_len) first (per
+// sequence: from its own length on); the cache pointers passed to
+// launch_decode must then be writable.
 struct DecodeAppend {
   const float* k_new;
   const float* v_new;
@@ -38,7 +48,8 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
-                         void* workspace, const DecodeAppend* append, hipStream_t stream);
+                         void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
+                         hipStream_t stream);
 
 hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,

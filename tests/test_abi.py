@@ -22,6 +22,8 @@ def lib():
     L.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci, vp, vp, vp]
     L.qkv_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                     vp, vp, vp, sz, vp]
+    L.qkv_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                   i64, i64, f32, ci, vp, vp, vp, sz, vp]
     L.qkv_last_error.restype = ctypes.c_char_p
     L.qkv_status_string.restype = ctypes.c_char_p
     L.qkv_decode_workspace_bytes.restype = sz
@@ -37,7 +39,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) >= {"qkv_quantize_append", "qkv_decode", "qkv_decode_append", "qkv_prefill",
+    assert set(names) >= {"qkv_quantize_append", "qkv_decode", "qkv_decode_append", "qkv_decode_paged",
+                          "qkv_prefill",
                           "qkv_quantize_append_kv", "qkv_decode_workspace_bytes",
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version"}
     for n in names:
@@ -154,3 +157,39 @@ def test_decode_append_argument_errors(lib):
     assert _dapp(lib, ns=2) == 3                # needs a workspace
     assert b"qkv_decode_append" in lib.qkv_last_error()
     assert _dapp(lib, q=None) == 1
+
+
+def _paged(lib, **kw):
+    a = dict(q=P, kn=None, vn=None, kc=P, ks=P, vc=P, vs=P, bt=P, lens=P, B=2, Hq=4, Hkv=2, Sq=1, n=0,
+             maxlen=100, ps=64, mp=4, np_=16, D=128, scale=0.1, ns=0, out=P, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qkv_decode_paged(a["q"], a["kn"], a["vn"], a["kc"], a["ks"], a["vc"], a["vs"], a["bt"], a["lens"],
+                                a["B"], a["Hq"], a["Hkv"], a["Sq"], a["n"], a["maxlen"], a["ps"], a["mp"],
+                                a["np_"], a["D"], a["scale"], a["ns"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                None)
+
+
+def test_decode_paged_argument_errors(lib):
+    assert _paged(lib, ps=48) == 2              # a page must hold whole 32-row chunks
+    assert b"multiple of 32" in lib.qkv_last_error()
+    assert _paged(lib, ps=0) == 1
+    assert _paged(lib, mp=0) == 1
+    assert _paged(lib, bt=None, mp=2) == 1      # without a table: one page per sequence
+    assert _paged(lib, bt=None, mp=1, np_=1) == 1   # ... and at least B pages
+    assert b"page b" in lib.qkv_last_error()
+    assert _paged(lib, bt=P + 2) == 1           # misaligned table
+    assert _paged(lib, lens=P + 1) == 1         # misaligned lengths
+    assert _paged(lib, n=65) == 2
+    assert _paged(lib, n=-1) == 2
+    assert _paged(lib, n=1) == 1                # new rows but no k_new / v_new
+    assert b"new-row" in lib.qkv_last_error()
+    assert _paged(lib, n=1, kn=P, vn=P + 4) == 1
+    assert _paged(lib, maxlen=257) == 1         # beyond max_pages * page_size
+    assert _paged(lib, maxlen=0) == 1
+    assert _paged(lib, n=3, kn=P, vn=P, maxlen=2) == 1   # max_kv_len < n_new
+    assert _paged(lib, D=96) == 2
+    assert _paged(lib, Sq=33) == 2              # G * Sq > 64
+    assert _paged(lib, q=None) == 1
+    assert _paged(lib, ps=1 << 20, mp=1 << 12) == 2      # capacity beyond 2^31 rows
+    assert _paged(lib, maxlen=256, ns=3) == 3   # needs a workspace
+    assert b"qkv_decode_paged" in lib.qkv_last_error()
