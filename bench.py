@@ -16,7 +16,8 @@ packed KV bytes (codes + scales) per step, the roofline of the decode kernel
 (achieved HBM GB/s of its algorithmic bytes over its average launch time,
 measured with HIP events on the launch stream), the CPU oracle timed on a
 bounded sample of the same workload, and secondary figures (128K-token
-decode, 16K causal prefill TFLOP/s, ViT-B prefill, bulk quantize-append).
+decode, a ragged 64-sequence batch over a paged cache, 16K causal prefill
+TFLOP/s, ViT-B prefill, bulk quantize-append).
 Everything else goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline]
@@ -207,6 +208,70 @@ def bench_decode(torch, qkv, w, steps, warmup, with_append):
     return res
 
 
+def build_paged(torch, qkv, w, seed=0):
+    """Page pool, table and lengths of a ragged paged workload, quantized on the GPU."""
+    from qkv_inputs import pool_rows, ragged_layout
+    lens, table, num_pages = ragged_layout(w, seed)
+    P, half = w.page_size, w.D // 2
+    pool = qkv.KVCache(torch.empty((num_pages, w.Hkv, P, half), dtype=torch.uint8, device="cuda"),
+                       torch.empty((num_pages, w.Hkv, P), dtype=torch.float16, device="cuda"),
+                       torch.empty((num_pages, w.Hkv, P, half), dtype=torch.uint8, device="cuda"),
+                       torch.empty((num_pages, w.Hkv, P), dtype=torch.float16, device="cuda"))
+    for p0, k, v in pool_rows(w, num_pages, 512, seed):
+        n = k.shape[0]
+        qkv.quantize_append(torch.from_numpy(k).cuda(), pool.k_codes[p0:p0 + n], pool.k_scales[p0:p0 + n], 0)
+        qkv.quantize_append(torch.from_numpy(v).cuda(), pool.v_codes[p0:p0 + n], pool.v_scales[p0:p0 + n], 0)
+    torch.cuda.synchronize()
+    return lens, table, num_pages, pool
+
+
+def paged_bytes(w, lens, num_used_pages):
+    """Algorithmic bytes of one ragged paged step (append 1 token + decode)."""
+    rows = int(lens.sum())
+    kv = 2 * rows * w.Hkv * (w.D // 2 + 2)
+    other = (w.B * w.Hq * w.Sq * w.D * 2 + w.B * w.Hq * w.Sq * w.D * 4   # q, out
+             + 2 * w.B * w.Hkv * w.D * 4                                  # new K/V rows (fp32)
+             + 4 * num_used_pages + 4 * w.B)                              # page ids, lengths
+    return kv, kv + other
+
+
+def bench_paged(torch, qkv, w, steps):
+    """Ragged batch over a shared page pool: one step appends every sequence's
+    new token and attends its own rows (qkv_decode_paged, one launch)."""
+    from qkv_inputs import make_qkv
+    lens, table, num_pages, pool = build_paged(torch, qkv, w)
+    rng_w = w.scaled(L=1)        # q and the new rows only
+    q_bits, k1, v1 = make_qkv(rng_w)
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    k_new, v_new = torch.from_numpy(k1).cuda(), torch.from_numpy(v1).cuda()
+    bt = torch.from_numpy(table).cuda()
+    cached = torch.from_numpy(lens - 1).cuda()        # rows before the step; the step appends one
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    max_len = int(lens.max())
+    # the library's plan for per-sequence lengths: its uniform plan, with splits of at most 4096 tokens
+    ns = max(qkv.decode_auto_splits(w.B, w.Hq, w.Hkv, w.Sq, max_len, w.D), -(-max_len // 4096))
+    ws = torch.zeros(max(qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, max_len, w.D), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(_):
+        qkv.decode_paged(q, pool, cached, bt, k_new, v_new, max_kv_len=max_len, softmax_scale=w.softmax_scale,
+                         out=out, workspace=ws)
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    avg_ms, med_ms = per_launch_ms(torch, step, steps, 1)
+    kv_bytes, alg = paged_bytes(w, lens, num_pages)
+    res = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "page_size": w.page_size,
+           "lengths": f"uniform in [{w.len_min}, {w.L}], sum {int(lens.sum())}", "n_split": ns,
+           "packed_kv_bytes": kv_bytes, "algorithmic_bytes": alg,
+           "avg_ms": avg_ms, "median_ms": med_ms, "GBps": alg / (avg_ms * 1e-3) / 1e9}
+    res["frac_hbm"] = res["GBps"] / HBM_PEAK_GBS
+    del pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(torch, qkv, w, iters):
     from qkv_inputs import make_qkv
     q_bits, k, v = make_qkv(w)
@@ -300,6 +365,19 @@ def profile_target(target: str, iters: int):
             dst.copy_(src)
         torch.cuda.synchronize()
         return
+    if target == "paged":
+        w = workload("ragged_paged_decode")
+        lens, table, _, pool = build_paged(torch, qkv, w)
+        q_bits, k1, v1 = make_qkv(w.scaled(L=1))
+        q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+        k_new, v_new = torch.from_numpy(k1).cuda(), torch.from_numpy(v1).cuda()
+        bt, cached = torch.from_numpy(table).cuda(), torch.from_numpy(lens - 1).cuda()
+        out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+        for _ in range(iters):
+            qkv.decode_paged(q, pool, cached, bt, k_new, v_new, max_kv_len=int(lens.max()),
+                             softmax_scale=w.softmax_scale, out=out)
+        torch.cuda.synchronize()
+        return
     if target == "prefill":
         w = workload("causal_prefill_16k")
         q_bits, k, v = make_qkv(w)
@@ -385,7 +463,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "headline", "decode", "prefill"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--profile-target", choices=["decode", "long", "prefill", "copy"], default=None,
+    ap.add_argument("--profile-target", choices=["decode", "long", "paged", "prefill", "copy"], default=None,
                     help="run one kernel repeatedly for rocprofv3 counter passes, print nothing")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")
@@ -416,6 +494,9 @@ def main():
         secondary["long_context_decode"] = bench_decode(torch, qkv, workload("long_context_decode"),
                                                         max(args.steps // 2, 10), 5, with_append=True)
         log("long:", json.dumps(secondary["long_context_decode"]))
+        secondary["ragged_paged_decode"] = bench_paged(torch, qkv, workload("ragged_paged_decode"),
+                                                       max(args.steps // 2, 10))
+        log("paged:", json.dumps(secondary["ragged_paged_decode"]))
     if args.only in ("all", "prefill"):
         secondary["causal_prefill_16k"] = bench_prefill(torch, qkv, workload("causal_prefill_16k"), 10)
         log("prefill:", json.dumps(secondary["causal_prefill_16k"]))

@@ -134,10 +134,16 @@ qkv_status qkv_quantize_append_kv(const float* k_src, const float* v_src,
  * Requires D in {64, 128}, Hq % Hkv == 0, 1 <= kv_len <= C,
  * 1 <= G * Sq <= 64 (more rows belong to qkv_prefill).
  */
+/* Workspace bytes for a decode of these sizes: enough for qkv_decode,
+ * qkv_decode_append and qkv_decode_paged (kv_len = max_kv_len), whose split
+ * plans may differ; 0 when the plan has a single split. */
 size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                                   int64_t kv_len, int64_t D, int num_splits);
-/* The split count the library would use for num_splits = 0 (device 0's CU
- * count is queried once and cached per device). */
+/* The split count the library would use for num_splits = 0 with every
+ * sequence of length kv_len (the current device's CU count is queried once
+ * and cached per device).  With per-sequence lengths (qkv_decode_paged with
+ * kv_lens) splits are also capped at 4096 tokens each, so the count can be
+ * larger. */
 int qkv_decode_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                            int64_t kv_len, int64_t D);
 qkv_status qkv_decode(const uint16_t* q,

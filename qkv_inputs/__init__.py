@@ -18,7 +18,10 @@ model weights are not available:
   channels of K/V),
 * long-context decode at 128K tokens (Open-TQ-Metal abstract: Llama 3.1 70B at
   128K context with an int4 KV cache),
-* causal GQA prefill at 16K tokens (TurboAttention §5: 4k-32k contexts).
+* causal GQA prefill at 16K tokens (TurboAttention §5: 4k-32k contexts),
+* a ragged serving batch: 64 Llama-3-8B shaped sequences of mixed lengths in
+  a shared page pool (TurboAttention §2.1: every decode step appends each
+  sequence's new token and attends its cache; §5 serves batches of up to 64).
 
 Distributions: every raw value is N(0, 1) in fp32 from numpy's PCG64, seeded
 by ``SeedSequence([seed, config_index])`` and spawned into independent streams
@@ -39,6 +42,8 @@ __all__ = [
     "bf16_bits_to_f32",
     "make_inputs",
     "make_qkv",
+    "ragged_layout",
+    "pool_rows",
 ]
 
 
@@ -58,6 +63,8 @@ class Workload:
     causal: bool
     outlier_frac: float = 0.0    # fraction of Hkv*D channels scaled x outlier_gain
     outlier_gain: float = 8.0
+    len_min: int = 0    # ragged batch: lengths uniform in [len_min, L] (0: every sequence has L)
+    page_size: int = 0  # paged cache: rows per page (0: contiguous cache)
 
     @property
     def G(self) -> int:
@@ -80,6 +87,8 @@ WORKLOADS = [
              outlier_frac=0.01),
     Workload(3, "long_context_decode", "decode", B=1, Hq=64, Hkv=8, D=128, Sq=1, L=131072, causal=False),
     Workload(4, "causal_prefill_16k", "prefill", B=1, Hq=32, Hkv=8, D=128, Sq=16384, L=16384, causal=True),
+    Workload(5, "ragged_paged_decode", "decode", B=64, Hq=32, Hkv=8, D=128, Sq=1, L=16384, causal=False,
+             len_min=512, page_size=64),
 ]
 
 
@@ -137,3 +146,40 @@ def make_inputs(w: Workload, seed: int = 0):
     """Dict form of :func:`make_qkv` with the workload attached."""
     q_bits, k, v = make_qkv(w, seed)
     return {"workload": w, "q_bits": q_bits, "k": k, "v": v}
+
+
+def ragged_layout(w: Workload, seed: int = 0):
+    """Lengths and page table of a ragged, paged workload.
+
+    Returns ``(lens, table, num_pages)``: ``lens`` int32 ``[B]`` attended rows
+    per sequence, uniform in ``[len_min, L]``; ``table`` int32 ``[B,
+    ceil(L / page_size)]``, the pages of every sequence drawn without
+    replacement from a shuffled pool of exactly the pages needed (entries past
+    a sequence's last page are -1); ``num_pages`` the pool size.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, w.index, 7])))
+    lo = w.len_min if w.len_min > 0 else w.L
+    lens = rng.integers(lo, w.L + 1, size=w.B).astype(np.int32)
+    P = w.page_size
+    used = [-(-int(L) // P) for L in lens]
+    num_pages = int(sum(used))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((w.B, -(-w.L // P)), -1, np.int32)
+    k = 0
+    for b, u in enumerate(used):
+        table[b, :u] = perm[k:k + u]
+        k += u
+    return lens, table, num_pages
+
+
+def pool_rows(w: Workload, num_pages: int, chunk_pages: int, seed: int = 0):
+    """fp32 N(0, 1) K and V rows of a page pool, ``chunk_pages`` pages at a time.
+
+    Yields ``(first_page, k, v)`` with ``k``, ``v`` fp32 ``[n, Hkv, page_size, D]``.
+    """
+    ss = np.random.SeedSequence([seed, w.index, 11])
+    rk, rv = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(2))
+    for p0 in range(0, num_pages, chunk_pages):
+        n = min(chunk_pages, num_pages - p0)
+        shape = (n, w.Hkv, w.page_size, w.D)
+        yield p0, rk.standard_normal(shape, dtype=np.float32), rv.standard_normal(shape, dtype=np.float32)

@@ -133,14 +133,17 @@ qkv_status qkv_quantize_append_kv(const float* k_src, const float* v_src, uint8_
 int qkv_decode_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
                            int64_t D) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || kv_len < 1 || (D != 64 && D != 128)) return 1;
-  return qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, 0, current_cus()).n_split;
+  return qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, 0, current_cus(), false).n_split;
 }
 
 size_t qkv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
                                   int64_t D, int num_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || kv_len < 1 || (D != 64 && D != 128)) return 0;
-  const qkvfa::DecodePlan p = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus());
-  return qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, p.n_split);
+  // the larger of the uniform and the ragged plan: one size serves every decode entry point
+  const int cus = current_cus();
+  const qkvfa::DecodePlan p = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, cus, false);
+  const qkvfa::DecodePlan pr = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, cus, true);
+  return qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, p.n_split > pr.n_split ? p.n_split : pr.n_split);
 }
 
 }  // extern "C"
@@ -165,7 +168,12 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
     return fail(QKV_ERR_UNSUPPORTED, f + ": (Hq/Hkv) * Sq must be <= 64; use qkv_prefill");
   if (num_splits < 0 || num_splits > 1024)
     return fail(QKV_ERR_INVALID_ARG, f + ": num_splits must be in [0, 1024]");
-  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus());
+  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus(),
+                                                     varlen != nullptr && varlen->kv_lens != nullptr);
+  // one-dimensional grid: (splits x B x Hkv) workgroups of up to 512 threads,
+  // whose thread count must fit 32 bits
+  if ((int64_t)plan.n_split * B * Hkv > ((int64_t)1 << 32) / 512)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": too many workgroups (num_splits * B * Hkv)");
   const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, plan.n_split);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)

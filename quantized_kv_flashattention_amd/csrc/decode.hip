@@ -60,9 +60,24 @@ namespace {
 __host__ __device__ constexpr int waves_for(int NB) { return NB >= 4 ? 4 : 8; }
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
-constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (fits s_o at D = 64)
+constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (floats)
+
+// Dynamic LDS of a decode launch: the wave-merge buffer (waves x min(16, R)
+// rows x (D + 4) floats), reused for the split-merge weights (R x n_split).
+inline size_t merge_lds_bytes(int D, int waves, int R, int n_split) {
+  const size_t wave_merge = (size_t)waves * (size_t)(R < 16 ? R : 16) * (size_t)(D + 4);
+  const size_t weights = (size_t)R * (size_t)n_split;
+  return 4 * (wave_merge > weights ? wave_merge : weights);
+}
+
+template <int D, int NB>
+constexpr size_t max_merge_lds_bytes() {   // largest merge_lds_bytes of a kernel variant
+  return 4 * ((size_t)waves_for(NB) * 16 * (D + 4) > (size_t)kMaxMergeLse
+                  ? (size_t)waves_for(NB) * 16 * (D + 4) : (size_t)kMaxMergeLse);
+}
 constexpr int kMaxNew = 64;                 // rows one append-mode call may add
-constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
+constexpr int kMaxSplitPages = 512;
+constexpr int kRaggedSplitChunks = 128;     // ragged batches: at most 4096 tokens per split         // page ids of one split cached in LDS (paged cache)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -155,8 +170,11 @@ void decode_kernel(const DecodeArgs a) {
   __shared__ __align__(16) float s_sc[kWaves][96];   // K column scale, V scale, mask bias
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
-  __shared__ __align__(16) float s_o[kWaves][16 * OSTR];
+  // wave-merge buffer [kWaves][rows_o][OSTR] floats, later the split-merge
+  // weights: dynamic, sized by the launch for the rows this call has
+  extern __shared__ __align__(16) float s_o[];
   __shared__ int s_last;
+  __shared__ float s_den[64];
   // append mode: this split's new rows, indexed by row - pos
   __shared__ __align__(16) uint32_t s_nk[kMaxNew * DW];
   __shared__ __align__(16) uint32_t s_nv[kMaxNew * DW];
@@ -169,11 +187,18 @@ void decode_kernel(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int j = lane >> 4;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // One-dimensional grid, split index slowest: consecutive workgroups (which
+  // the dispatcher deals round-robin to the eight XCDs) take different
+  // (batch, KV head) units of one split, so every XCD gets an even share of
+  // each split -- also when the late splits of short sequences are empty.
+  const int n_units = (int)(gridDim.x / (uint32_t)a.n_split);
+  const int split = (int)blockIdx.x / n_units;
+  const int unit = (int)blockIdx.x - split * n_units;
+  const int g = unit % a.Hkv;
+  const int b = unit / a.Hkv;
   const int G = a.G, Sq = a.Sq;
   const int R = G * Sq;
+  const int rows_o = min(16, R);   // rows per wave in the merge buffer
   const bool append = a.k_new != nullptr;
   // rows this sequence attends, and where its new rows start (append mode)
   int pos_b = a.pos;
@@ -225,6 +250,124 @@ void decode_kernel(const DecodeArgs a) {
   // the plain decode gives it, so the arithmetic is the plain decode's.
   const int t_main =
       append ? min(t_end, t_begin + (max(pos_b, t_begin) - t_begin) / kChunk * kChunk) : t_end;
+
+  const bool direct = (a.n_split == 1);
+  // one descriptor over all partial outputs (the planner keeps them < 2 GiB)
+  const rsrc_t rpart = make_rsrc(a.part_o, direct ? 0 : a.part_bytes);
+
+  // ---- split merge by the last workgroup of this (batch, KV head) to finish
+  //      (run after this split's partial is written, or at once by a split
+  //      with nothing to attend)
+  auto merge_splits = [&]() {
+    // ---- split merge by the last workgroup of this (batch, KV head) to finish.
+    // Partials were written with device-coherent stores; waiting for their
+    // completion before the barrier orders them before the ticket increment.
+    // The merging workgroup reads them back with device-coherent loads, so no
+    // L2 writeback or invalidation (an expensive whole-cache operation) is needed.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t* ticket = a.tickets + (int64_t)b * a.Hkv + g;
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (prev == (uint32_t)(a.n_split - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int n_split = a.n_split;
+    // splits that start before this sequence's length; the rest attended nothing
+    const int n_live = min(n_split, (L_b + a.split_len - 1) / a.split_len);
+    // (1) every live split's LSE of this group -> LDS (the wave-merge buffer is free
+    //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
+    float* s_w = s_o;
+    {
+      const int total = R * n_live;
+      for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
+        float v[8];
+  #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + u * 64 * kWaves;
+          v[u] = -INFINITY;
+          if (idx < total) {
+            const int row = idx / n_live;
+            const int hg = row / Sq;
+            const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+            v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+  #pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
+      }
+    }
+    __syncthreads();
+    // (2) per row: max, weights 2^(lse_s - max) (in place), their sum -- one wave per row
+    for (int row = wave; row < R; row += kWaves) {
+      float* wr = s_w + row * n_live;
+      float M = -INFINITY;
+      for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
+  #pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
+      float den = 0.0f;
+      for (int s = lane; s < n_live; s += 64) {
+        const float w = fast_exp2(wr[s] - M);
+        wr[s] = w;
+        den += w;
+      }
+  #pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
+      if (lane == 0) {
+        s_den[row] = den;
+        const int hg = row / Sq;
+        const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+        if (a.lse) a.lse[grow] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per thread
+    for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
+      const int row = idx / (D / 4);
+      const int d = 4 * (idx - row * (D / 4));
+      const int hg = row / Sq;
+      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+      const float* wr = s_w + row * n_live;
+      const uint32_t off0 = (uint32_t)((grow * n_split * D + d) * 4);
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < n_live; s0 += 16) {
+        float4v o[16];
+  #pragma unroll
+        for (int u = 0; u < 16; ++u)
+          o[u] = (s0 + u < n_live)
+                     ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
+                     : float4v{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (s0 + u < n_live) acc += wr[s0 + u] * o[u];
+      }
+      const float den = s_den[row];
+      *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (den > 0.0f ? 1.0f / den : 0.0f);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // ---- a split past this sequence's length: nothing to attend.  It writes
+  //      no partial (the merge skips it), only takes its ticket; alone, it
+  //      writes the empty result (output 0, LSE -inf).
+  if (t_end <= t_begin) {
+    if (direct) {
+      for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
+        const int row = idx / (D / 4);
+        const int d = 4 * (idx - row * (D / 4));
+        const int hg = row / Sq;
+        const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+        *reinterpret_cast<float4v*>(a.out + grow * D + d) = float4v{0.f, 0.f, 0.f, 0.f};
+        if (d == 0 && a.lse) a.lse[grow] = -INFINITY;
+      }
+      return;
+    }
+    merge_splits();
+    return;
+  }
 
   // Codes of the chunk starting at token c0, through buffer descriptors whose
   // range ends at t_main <= kv_len (the split end, before any new rows): the
@@ -473,9 +616,6 @@ void decode_kernel(const DecodeArgs a) {
   }
 
   // ---- merge the eight waves through LDS, one 16-row block at a time
-  const bool direct = (a.n_split == 1);
-  // one descriptor over all partial outputs (the planner keeps them < 2 GiB)
-  const rsrc_t rpart = make_rsrc(a.part_o, direct ? 0 : a.part_bytes);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float l = xor_sum(l_run[nb], 16);
@@ -484,20 +624,22 @@ void decode_kernel(const DecodeArgs a) {
       s_m[wave][r] = m_run[nb];
       s_l[wave][r] = l;
     }
-    float* orow = &s_o[wave][r * OSTR];
+    float* orow = s_o + (wave * rows_o + r) * OSTR;
+    if (r < rows_o) {   // rows past R are padding of the 16-row block
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (D == 128) {
-        // head dims 32j + 8i + p, p = 0..7
-        float4v lo = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
-        float4v hi = {o_acc[nb][4][i], o_acc[nb][5][i], o_acc[nb][6][i], o_acc[nb][7][i]};
-        *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i) = lo;
-        *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i + 4) = hi;
-      } else {
-        // M-row m = 4j + i holds head dims 8(m%8) + 4(m/8) + p, p = 0..3
-        const int m = 4 * j + i;
-        float4v v4 = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
-        *reinterpret_cast<float4v*>(orow + 8 * (m & 7) + 4 * (m >> 3)) = v4;
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (D == 128) {
+          // head dims 32j + 8i + p, p = 0..7
+          float4v lo = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
+          float4v hi = {o_acc[nb][4][i], o_acc[nb][5][i], o_acc[nb][6][i], o_acc[nb][7][i]};
+          *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i) = lo;
+          *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i + 4) = hi;
+        } else {
+          // M-row m = 4j + i holds head dims 8(m%8) + 4(m/8) + p, p = 0..3
+          const int m = 4 * j + i;
+          float4v v4 = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
+          *reinterpret_cast<float4v*>(orow + 8 * (m & 7) + 4 * (m >> 3)) = v4;
+        }
       }
     }
     __syncthreads();
@@ -508,14 +650,14 @@ void decode_kernel(const DecodeArgs a) {
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
-      // every wave empty (a split past the sequence's length): weights 0
+      // every wave empty: weights 0 (not reached by a split with rows)
       const float Mz = (M == -INFINITY) ? 0.0f : M;
       float4v acc = {0.f, 0.f, 0.f, 0.f};
       float den = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wt = fast_exp2(s_m[w][rr] - Mz);   // empty waves: exp2(-inf) = 0
-        acc += wt * *reinterpret_cast<const float4v*>(&s_o[w][rr * OSTR + d]);
+        acc += wt * *reinterpret_cast<const float4v*>(s_o + (w * rows_o + rr) * OSTR + d);
         den += wt * s_l[w][rr];
       }
       const int row = nb * 16 + rr;
@@ -541,106 +683,28 @@ void decode_kernel(const DecodeArgs a) {
   }
   if (direct) return;
 
-  // ---- split merge by the last workgroup of this (batch, KV head) to finish.
-  // Partials were written with device-coherent stores; waiting for their
-  // completion before the barrier orders them before the ticket increment.
-  // The merging workgroup reads them back with device-coherent loads, so no
-  // L2 writeback or invalidation (an expensive whole-cache operation) is needed.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  uint32_t* ticket = a.tickets + (int64_t)b * a.Hkv + g;
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (uint32_t)(a.n_split - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  const int n_split = a.n_split;
-  // splits that start before this sequence's length; the rest attended nothing
-  const int n_live = min(n_split, (L_b + a.split_len - 1) / a.split_len);
-  // (1) every live split's LSE of this group -> LDS (the wave-merge buffer is free
-  //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
-  float* s_w = &s_o[0][0];
-  __shared__ float s_den[64];
-  {
-    const int total = R * n_live;
-    for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 64 * kWaves;
-        v[u] = -INFINITY;
-        if (idx < total) {
-          const int row = idx / n_live;
-          const int hg = row / Sq;
-          const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
-          v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
-    }
-  }
-  __syncthreads();
-  // (2) per row: max, weights 2^(lse_s - max) (in place), their sum -- one wave per row
-  for (int row = wave; row < R; row += kWaves) {
-    float* wr = s_w + row * n_live;
-    float M = -INFINITY;
-    for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
-    float den = 0.0f;
-    for (int s = lane; s < n_live; s += 64) {
-      const float w = fast_exp2(wr[s] - M);
-      wr[s] = w;
-      den += w;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
-    if (lane == 0) {
-      s_den[row] = den;
-      const int hg = row / Sq;
-      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
-      if (a.lse) a.lse[grow] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
-    }
-  }
-  __syncthreads();
-  // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per thread
-  for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
-    const int row = idx / (D / 4);
-    const int d = 4 * (idx - row * (D / 4));
-    const int hg = row / Sq;
-    const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
-    const float* wr = s_w + row * n_live;
-    const uint32_t off0 = (uint32_t)((grow * n_split * D + d) * 4);
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_live; s0 += 16) {
-      float4v o[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        o[u] = (s0 + u < n_live)
-                   ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
-                   : float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (s0 + u < n_live) acc += wr[s0 + u] * o[u];
-    }
-    const float den = s_den[row];
-    *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (den > 0.0f ? 1.0f / den : 0.0f);
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_splits();
+}
+
+template <int D, int NB, bool PAGED>
+hipError_t launch_paged(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
+  // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
+  // this kernel the larger dynamic LDS once
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
+  if (attr != hipSuccess) return attr;
+  decode_kernel<D, NB, PAGED><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  return hipGetLastError();
 }
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
-  dim3 grid((uint32_t)n_split, (uint32_t)Hkv, (uint32_t)B);
-  if (args.block_table != nullptr)
-    decode_kernel<D, NB, true><<<grid, dim3(64 * waves_for(NB)), 0, stream>>>(args);
-  else
-    decode_kernel<D, NB, false><<<grid, dim3(64 * waves_for(NB)), 0, stream>>>(args);
-  return hipGetLastError();
+  dim3 grid((uint32_t)n_split * (uint32_t)Hkv * (uint32_t)B);
+  const int R = args.G * args.Sq;
+  const size_t lds = merge_lds_bytes(D, waves_for(NB), R, n_split);
+  if (args.block_table != nullptr) return launch_paged<D, NB, true>(args, grid, lds, stream);
+  return launch_paged<D, NB, false>(args, grid, lds, stream);
 }
 
 template <int D>
@@ -654,7 +718,7 @@ hipError_t launch_d(const DecodeArgs& args, int B, int Hkv, int n_split, hipStre
 }  // namespace
 
 DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int D, int num_splits,
-                       int num_cus) {
+                       int num_cus, bool ragged) {
   const int64_t chunks = (kv_len + kChunk - 1) / kChunk;
   const int64_t units = B * Hkv;
   const int64_t rows_per_group = rows / units;
@@ -670,6 +734,15 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
     ns = (target_wgs + units - 1) / units;
     const int64_t max_ns = chunks / waves > 0 ? chunks / waves : 1;   // >= one chunk per wave
     if (ns > max_ns) ns = max_ns;
+    // Lengths that differ per sequence (known only on the device): the plan
+    // covers the longest, so a sequence's work is its number of non-empty
+    // splits.  Splits of at most kRaggedSplitChunks chunks keep the longest
+    // sequences from finishing alone (measured on a 64-sequence batch of
+    // 512..16384 tokens: 4096-token splits 138 us, one split each 158 us)
+    if (ragged) {
+      const int64_t ns_r = (chunks + kRaggedSplitChunks - 1) / kRaggedSplitChunks;
+      if (ns < ns_r) ns = ns_r;
+    }
   } else {
     ns = num_splits;
   }

@@ -19,8 +19,10 @@ struct DecodePlan {
 };
 
 // Split plan for rows = B*Hq*Sq query rows; num_splits = 0 picks the count.
+// ragged: per-sequence lengths up to kv_len (the count then also bounds the
+// tokens per split).
 DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int D, int num_splits,
-                       int num_cus);
+                       int num_cus, bool ragged);
 
 // Bytes of decode workspace: split partials plus one ticket per (batch, KV head).
 size_t decode_workspace_bytes(int64_t rows, int64_t units, int D, int n_split);

@@ -97,6 +97,8 @@ def test_decode_argument_errors(lib):
     assert _dec(lib, ns=2) == 3                 # needs a workspace
     assert b"workspace" in lib.qkv_last_error()
     assert _dec(lib, ns=2, ws=P, wsb=10) == 3
+    assert _dec(lib, B=65535, Hkv=256, Hq=256, L=64, C=64, D=64, ns=1) == 2   # grid beyond 2^32 threads
+    assert b"workgroups" in lib.qkv_last_error()
 
 
 def test_decode_workspace_size(lib):
