@@ -276,6 +276,34 @@ void decode_kernel(const DecodeArgs a) {
     const int n_split = a.n_split;
     // splits that start before this sequence's length; the rest attended nothing
     const int n_live = min(n_split, (L_b + a.split_len - 1) / a.split_len);
+    // item idx: four output values (query row idx / (D/4), dims 4 (idx % (D/4)) + 0..3)
+    const int n_items = R * (D / 4);
+    auto item_grow = [&](int idx) -> int64_t {
+      const int row = idx / (D / 4);
+      const int hg = row / Sq;
+      return ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+    };
+    auto load16 = [&](uint32_t off0, int s0, float4v (&o)[16]) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        o[u] = (s0 + u < n_live)
+                   ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
+                   : float4v{0.f, 0.f, 0.f, 0.f};
+    };
+    auto item_off = [&](int idx) -> uint32_t {
+      return (uint32_t)((item_grow(idx) * n_split * D + 4 * (idx % (D / 4))) * 4);
+    };
+    // (0) the partial outputs of this thread's first item (first kPre splits),
+    //     issued now: their round trip overlaps the LSE loads'
+    constexpr int kPre = 8;
+    float4v pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      pre[u] = float4v{0.f, 0.f, 0.f, 0.f};
+      if ((int)threadIdx.x < n_items && u < n_live)
+        pre[u] = __builtin_amdgcn_raw_buffer_load_b128(rpart, item_off(threadIdx.x) + (uint32_t)(u * D * 4), 0,
+                                                       kCoherent);
+    }
     // (1) every live split's LSE of this group -> LDS (the wave-merge buffer is free
     //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
     float* s_w = s_o;
@@ -283,7 +311,7 @@ void decode_kernel(const DecodeArgs a) {
       const int total = R * n_live;
       for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
         float v[8];
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int idx = base + u * 64 * kWaves;
           v[u] = -INFINITY;
@@ -295,7 +323,7 @@ void decode_kernel(const DecodeArgs a) {
                                      __HIP_MEMORY_SCOPE_AGENT);
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 8; ++u)
           if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
       }
@@ -306,7 +334,7 @@ void decode_kernel(const DecodeArgs a) {
       float* wr = s_w + row * n_live;
       float M = -INFINITY;
       for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
-  #pragma unroll
+#pragma unroll
       for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
       float den = 0.0f;
       for (int s = lane; s < n_live; s += 64) {
@@ -314,7 +342,7 @@ void decode_kernel(const DecodeArgs a) {
         wr[s] = w;
         den += w;
       }
-  #pragma unroll
+#pragma unroll
       for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
       if (lane == 0) {
         s_den[row] = den;
@@ -324,29 +352,33 @@ void decode_kernel(const DecodeArgs a) {
       }
     }
     __syncthreads();
-    // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per thread
-    for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
+    // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per
+    //     thread; the first item starts from its prefetched splits
+    auto finish_item = [&](int idx, bool first) {
       const int row = idx / (D / 4);
       const int d = 4 * (idx - row * (D / 4));
-      const int hg = row / Sq;
-      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
       const float* wr = s_w + row * n_live;
-      const uint32_t off0 = (uint32_t)((grow * n_split * D + d) * 4);
+      const uint32_t off0 = item_off(idx);
       float4v acc = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < n_live; s0 += 16) {
+      int s0 = 0;
+      if (first) {
+#pragma unroll
+        for (int u = 0; u < kPre; ++u)
+          if (u < n_live) acc += wr[u] * pre[u];
+        s0 = kPre;
+      }
+      for (; s0 < n_live; s0 += 16) {
         float4v o[16];
-  #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          o[u] = (s0 + u < n_live)
-                     ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
-                     : float4v{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+        load16(off0, s0, o);
+#pragma unroll
         for (int u = 0; u < 16; ++u)
           if (s0 + u < n_live) acc += wr[s0 + u] * o[u];
       }
       const float den = s_den[row];
-      *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * (den > 0.0f ? 1.0f / den : 0.0f);
-    }
+      *reinterpret_cast<float4v*>(a.out + item_grow(idx) * D + d) = acc * (den > 0.0f ? 1.0f / den : 0.0f);
+    };
+    if ((int)threadIdx.x < n_items) finish_item(threadIdx.x, true);
+    for (int idx = threadIdx.x + 64 * kWaves; idx < n_items; idx += 64 * kWaves) finish_item(idx, false);
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
