@@ -20,7 +20,10 @@ exact arithmetic):
   natural-log log-sum-exp of each row;
 * ``attention_partial`` / ``lse_merge``: the same attention restricted to a
   key range, and the log-sum-exp merge of such partial results (the
-  definition the split-K decode reaches).
+  definition the split-K decode reaches);
+* ``buffer``: the INT8 decode buffer -- universal scale from the cache's
+  value range, symmetric clamped 8-bit codes, the flush to int4, and
+  attention over int4 rows followed by buffered INT8 rows.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against hand
 derived examples, exact rational arithmetic, brute force on tiny inputs,
@@ -28,6 +31,7 @@ closed forms and invariants.
 """
 from .quantize import quantize_rows, dequantize_rows, quantize_append, dequantize_cache
 from .attention import attention, attention_partial, lse_merge
+from .buffer import buffer_scale, quantize_int8, dequantize_int8, flush_rows, attention_buffered
 
 __all__ = [
     "quantize_rows",
@@ -37,4 +41,9 @@ __all__ = [
     "attention",
     "attention_partial",
     "lse_merge",
+    "buffer_scale",
+    "quantize_int8",
+    "dequantize_int8",
+    "flush_rows",
+    "attention_buffered",
 ]
