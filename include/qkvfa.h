@@ -228,6 +228,63 @@ qkv_status qkv_decode_paged(const uint16_t* q, const float* k_new, const float* 
                             void* stream);
 
 /*
+ * INT8 decode buffer (TurboAttention §3.3 decoding buffer, and the
+ * implementation paragraph of its §5): the newest tokens of every
+ * (batch, KV head) -- at most 64 -- are kept as INT8 codes under one
+ * universal scale, so a decode step quantizes only its own token; outliers
+ * beyond the scale's range are clamped, so buffered rows are never
+ * re-quantized.  A full buffer is flushed into the int4 cache.
+ * Buffer layout: k_buf, v_buf int8 [B, Hkv, buf_rows, D] (1 <= buf_rows <=
+ * 64), device, 16-byte aligned; k_s8, v_s8 float [B, Hkv] universal scales.
+ * A buffered value is s8 * code, code = clamp(rint(x / s8), -127, 127) with
+ * IEEE fp32 division (s8 = 0 gives code 0).
+ */
+
+/* Universal scales from the cache's value range: s8 = (7 * max_t s[t]) / 127
+ * over rows [0, L) of every (batch, KV head), for K (k_scales -> k_s8) and V;
+ * 0 when L = 0.  k_scales, v_scales uint16 fp16 bits [B, Hkv, C], device.
+ * Requires 0 <= L <= C. */
+qkv_status qkv_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales,
+                            int64_t B, int64_t Hkv, int64_t L, int64_t C,
+                            float* k_s8, float* v_s8, void* stream);
+
+/* Flush: buffered rows [0, T) of every (batch, KV head), each value taken as
+ * the fp32 product s8 * code, quantized as int4 rows (as
+ * qkv_quantize_append_kv does) into cache rows [pos, pos + T).  The buffer is
+ * only read.  Requires 0 <= T <= buf_rows <= 64, 0 <= pos, pos + T <= C. */
+qkv_status qkv_buffer_flush(const int8_t* k_buf, const int8_t* v_buf,
+                            const float* k_s8, const float* v_s8,
+                            int64_t buf_rows, int64_t T,
+                            uint8_t* k_codes, uint16_t* k_scales,
+                            uint8_t* v_codes, uint16_t* v_scales,
+                            int64_t B, int64_t Hkv, int64_t D, int64_t C, int64_t pos,
+                            void* stream);
+
+/* Decode over int4 cache rows [0, kv_len) followed by buffered rows
+ * [0, buf_len + n_new), in one launch.  The n_new new rows k_new, v_new
+ * (float [B, Hkv, n_new, D], device, 16-byte aligned; may be NULL when n_new
+ * is 0) are first quantized into buffer rows [buf_len, buf_len + n_new).  The
+ * cache rows are split as by qkv_decode (num_splits applies to them); one
+ * more split per (batch, KV head) attends the buffered rows, and the LSE merge
+ * combines them.  Other arguments as for qkv_decode; the workspace size is
+ * qkv_decode_buffered_workspace_bytes (0 when there is a single split).
+ * Requires 0 <= kv_len <= C, 0 <= buf_len, 0 <= n_new,
+ * buf_len + n_new <= buf_rows <= 64, kv_len + buf_len + n_new >= 1, and the
+ * qkv_decode requirements on the other arguments. */
+size_t qkv_decode_buffered_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                                           int64_t kv_len, int64_t D, int num_splits);
+qkv_status qkv_decode_buffered(const uint16_t* q, const float* k_new, const float* v_new,
+                               const uint8_t* k_codes, const uint16_t* k_scales,
+                               const uint8_t* v_codes, const uint16_t* v_scales,
+                               int8_t* k_buf, int8_t* v_buf,
+                               const float* k_s8, const float* v_s8,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                               int64_t kv_len, int64_t C,
+                               int64_t buf_rows, int64_t buf_len, int64_t n_new, int64_t D,
+                               float softmax_scale, int num_splits, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * (c) Prefill attention, tiled with online softmax (FlashAttention tiling,
  * TurboAttention §2.2).  causal = 0: every row sees [0, kv_len).
  * causal = 1: query row i (0 <= i < Sq) is token kv_len - Sq + i and sees

@@ -30,6 +30,11 @@ __all__ = [
     "decode",
     "decode_append",
     "decode_paged",
+    "DecodeBuffer",
+    "buffer_scale",
+    "buffer_flush",
+    "decode_buffered",
+    "decode_buffered_workspace_bytes",
     "prefill",
     "decode_workspace_bytes",
     "decode_auto_splits",
@@ -79,6 +84,14 @@ def _load():
     lib.qkv_decode_paged.restype = ci
     lib.qkv_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                      i64, i64, i64, f32, ci, vp, vp, vp, sz, vp]
+    lib.qkv_buffer_scale.restype = ci
+    lib.qkv_buffer_scale.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.qkv_buffer_flush.restype = ci
+    lib.qkv_buffer_flush.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.qkv_decode_buffered_workspace_bytes.restype = sz
+    lib.qkv_decode_buffered_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+    lib.qkv_decode_buffered.restype = ci
+    lib.qkv_decode_buffered.argtypes = [vp] * 11 + [i64] * 10 + [f32, ci, vp, vp, vp, sz, vp]
     lib.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                 vp, vp, vp]
     return lib
@@ -354,6 +367,113 @@ def decode_paged(q, cache, kv_lens=None, block_table=None, k_new=None, v_new=Non
                                  page_size, max_pages, num_pages, D, _scale(softmax_scale, D),
                                  int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                  _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+@dataclasses.dataclass
+class DecodeBuffer:
+    """INT8 decode buffer of one layer: the newest tokens of every (batch, KV
+    head) as INT8 codes under one universal scale each (TurboAttention §3.3).
+
+    ``length`` is the number of buffered rows (host-side, the same for every
+    sequence); :func:`decode_buffered` advances it, :func:`buffer_flush`
+    resets it.
+    """
+
+    k: torch.Tensor      # int8 [B, Hkv, rows, D]
+    v: torch.Tensor
+    k_s8: torch.Tensor   # float32 [B, Hkv]
+    v_s8: torch.Tensor
+    length: int = 0
+
+    @staticmethod
+    def empty(B: int, Hkv: int, D: int, rows: int = 64, device="cuda") -> "DecodeBuffer":
+        mk = lambda: torch.zeros((B, Hkv, rows, D), dtype=torch.int8, device=device)
+        ms = lambda: torch.zeros((B, Hkv), dtype=torch.float32, device=device)
+        return DecodeBuffer(mk(), mk(), ms(), ms(), 0)
+
+    @property
+    def rows(self) -> int:
+        return self.k.shape[2]
+
+    def _check(self, device):
+        for name, t, dt, nd in (("k", self.k, torch.int8, 4), ("v", self.v, torch.int8, 4),
+                                ("k_s8", self.k_s8, torch.float32, 2), ("v_s8", self.v_s8, torch.float32, 2)):
+            _req(t, f"buffer.{name}", dt, nd)
+            if t.device != device:
+                raise ValueError("all tensors must be on one device")
+        if self.v.shape != self.k.shape or self.k_s8.shape != self.k.shape[:2] or self.v_s8.shape != self.k_s8.shape:
+            raise ValueError("inconsistent buffer shapes")
+
+
+def buffer_scale(cache, kv_len: int, buf: "DecodeBuffer"):
+    """Set ``buf``'s universal scales from cache rows ``[0, kv_len)``:
+    ``s8 = 7 * max_t scale[t] / 127`` per (batch, KV head), K and V."""
+    kc, ks, vc, vs = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    _req(ks, "k_scales", torch.float16, 3)
+    _req(vs, "v_scales", torch.float16, 3)
+    buf._check(ks.device)
+    B, Hkv, C = ks.shape
+    if vs.shape != ks.shape or buf.k_s8.shape != (B, Hkv):
+        raise ValueError("cache and buffer shapes do not match")
+    _check(_lib.qkv_buffer_scale(_ptr(ks), _ptr(vs), B, Hkv, int(kv_len), C, _ptr(buf.k_s8), _ptr(buf.v_s8),
+                                 _stream(ks)))
+
+
+def buffer_flush(buf: "DecodeBuffer", cache, pos: int):
+    """Quantize the buffered rows into int4 cache rows ``[pos, pos + buf.length)``
+    and empty the buffer (its scales are kept)."""
+    kc, ks, vc, vs = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+    buf._check(kc.device)
+    B, Hkv, C, half = kc.shape
+    D = buf.k.shape[3]
+    if buf.k.shape[:2] != (B, Hkv) or half * 2 != D or vc.shape != kc.shape or ks.shape != (B, Hkv, C) \
+            or vs.shape != ks.shape:
+        raise ValueError("cache and buffer shapes do not match")
+    _check(_lib.qkv_buffer_flush(_ptr(buf.k), _ptr(buf.v), _ptr(buf.k_s8), _ptr(buf.v_s8), buf.rows, buf.length,
+                                 _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hkv, D, C, int(pos), _stream(kc)))
+    buf.length = 0
+
+
+def decode_buffered_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits=0) -> int:
+    return int(_lib.qkv_decode_buffered_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits))
+
+
+def decode_buffered(q, cache, kv_len, buf: "DecodeBuffer", k_new=None, v_new=None, softmax_scale=None,
+                    num_splits=0, return_lse=False, out=None, lse=None, workspace=None):
+    """Decode step over int4 cache rows ``[0, kv_len)`` followed by the buffered
+    INT8 rows, in one launch.  New rows ``k_new``/``v_new [B, Hkv, n, D]``
+    (optional, fp32) are first quantized into the buffer under its universal
+    scales (outliers clamped) and attended; ``buf.length`` grows by ``n``."""
+    tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    B, Hq, Hkv, Sq, _, C, D = _attn_args(q, tensors, kv_len)
+    buf._check(q.device)
+    if buf.k.shape[:2] != (B, Hkv) or buf.k.shape[3] != D:
+        raise ValueError("buffer shape does not match the cache")
+    n_new = 0
+    if k_new is not None or v_new is not None:
+        if k_new is None or v_new is None:
+            raise ValueError("pass both k_new and v_new, or neither")
+        _req(k_new, "k_new", torch.float32, 4)
+        _req(v_new, "v_new", torch.float32, 4)
+        n_new = k_new.shape[2]
+        if k_new.shape != (B, Hkv, n_new, D) or v_new.shape != k_new.shape or \
+                k_new.device != q.device or v_new.device != q.device:
+            raise ValueError("k_new and v_new must be [B, Hkv, n_new, D] on q's device")
+    out, lse = _outputs(q, out, lse, return_lse)
+    need = decode_buffered_workspace_bytes(B, Hq, Hkv, Sq, int(kv_len), D, num_splits)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, B * Hkv, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kc, ks, vc, vs = tensors
+    _check(_lib.qkv_decode_buffered(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                    _ptr(buf.k), _ptr(buf.v), _ptr(buf.k_s8), _ptr(buf.v_s8), B, Hq, Hkv, Sq,
+                                    int(kv_len), C, buf.rows, buf.length, n_new, D, _scale(softmax_scale, D),
+                                    int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
+    buf.length += n_new
     return (out, lse) if return_lse else out
 
 

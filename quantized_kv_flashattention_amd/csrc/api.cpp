@@ -184,7 +184,7 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
   return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
                                          kv_len, varlen ? varlen->page_size : C, (int)D,
                                          softmax_scale, plan, out, lse, workspace, append, varlen,
-                                         static_cast<hipStream_t>(stream)),
+                                         nullptr, static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -262,6 +262,124 @@ qkv_status qkv_decode_paged(const uint16_t* q, const float* k_new, const float* 
   return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, max_kv_len,
                        max_pages * page_size, D, softmax_scale, num_splits, out, lse, workspace,
                        workspace_bytes, n_new > 0 ? &app : nullptr, &vl, stream, fn);
+}
+
+qkv_status qkv_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales, int64_t B, int64_t Hkv,
+                            int64_t L, int64_t C, float* k_s8, float* v_s8, void* stream) {
+  if (!k_scales || !v_scales || !k_s8 || !v_s8)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_scale: null pointer");
+  if (B < 1 || Hkv < 1 || C < 1 || L < 0 || L > C)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_scale: need B, Hkv, C >= 1 and 0 <= L <= C");
+  if (!aligned(k_scales, 2) || !aligned(v_scales, 2) || !aligned(k_s8, 4) || !aligned(v_s8, 4))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_scale: misaligned pointer");
+  if (B * Hkv > 0x3FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_buffer_scale: B * Hkv too large");
+  return hip_status(qkvfa::launch_buffer_scale(k_scales, v_scales, k_s8, v_s8, B * Hkv, L, C,
+                                               static_cast<hipStream_t>(stream)),
+                    "qkv_buffer_scale");
+}
+
+qkv_status qkv_buffer_flush(const int8_t* k_buf, const int8_t* v_buf, const float* k_s8, const float* v_s8,
+                            int64_t buf_rows, int64_t T, uint8_t* k_codes, uint16_t* k_scales,
+                            uint8_t* v_codes, uint16_t* v_scales, int64_t B, int64_t Hkv, int64_t D, int64_t C,
+                            int64_t pos, void* stream) {
+  if (B < 1 || Hkv < 1 || C < 1 || T < 0 || buf_rows < 1 || buf_rows > 64 || T > buf_rows)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_flush: need B, Hkv, C >= 1, 1 <= buf_rows <= 64, 0 <= T <= buf_rows");
+  if (D != 64 && D != 128) return fail(QKV_ERR_UNSUPPORTED, "qkv_buffer_flush: head dim must be 64 or 128");
+  if (pos < 0 || pos + T > C)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_flush: need 0 <= pos and pos + T <= C");
+  if (T == 0) return QKV_OK;
+  if (!k_buf || !v_buf || !k_s8 || !v_s8 || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_flush: null pointer");
+  if (!aligned(k_buf, 16) || !aligned(v_buf, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 2) || !aligned(v_scales, 2) || !aligned(k_s8, 4) || !aligned(v_s8, 4))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_buffer_flush: misaligned pointer");
+  if (B * Hkv > 0x3FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_buffer_flush: B * Hkv too large");
+  return hip_status(qkvfa::launch_buffer_flush(k_buf, v_buf, k_s8, v_s8, k_codes, k_scales, v_codes, v_scales,
+                                               B * Hkv, T, buf_rows, (int)D, C, pos,
+                                               static_cast<hipStream_t>(stream)),
+                    "qkv_buffer_flush");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split plan of a buffered decode: the int4 rows' plan (none when kv_len = 0)
+// plus one split for the buffered rows when there are any.
+qkvfa::DecodePlan buffered_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t D,
+                                int num_splits, int64_t tail_rows) {
+  qkvfa::DecodePlan p;
+  if (kv_len >= 1) {
+    p = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus(), false);
+  } else {
+    p.n_split = 0;
+    p.split_len = 32;
+  }
+  if (tail_rows > 0) p.n_split += 1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qkv_decode_buffered_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                                           int64_t D, int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || kv_len < 0 || (D != 64 && D != 128)) return 0;
+  const qkvfa::DecodePlan p = buffered_plan(B, Hq, Hkv, Sq, kv_len, D, num_splits, 1);
+  return qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, p.n_split);
+}
+
+qkv_status qkv_decode_buffered(const uint16_t* q, const float* k_new, const float* v_new,
+                               const uint8_t* k_codes, const uint16_t* k_scales, const uint8_t* v_codes,
+                               const uint16_t* v_scales, int8_t* k_buf, int8_t* v_buf, const float* k_s8,
+                               const float* v_s8, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                               int64_t kv_len, int64_t C, int64_t buf_rows, int64_t buf_len, int64_t n_new,
+                               int64_t D, float softmax_scale, int num_splits, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  const std::string f("qkv_decode_buffered");
+  if (buf_rows < 1 || buf_rows > 64)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": buf_rows must be in [1, 64]");
+  if (buf_len < 0 || n_new < 0 || buf_len + n_new > buf_rows)
+    return fail(QKV_ERR_INVALID_ARG, f + ": need 0 <= buf_len, 0 <= n_new, buf_len + n_new <= buf_rows");
+  if (kv_len < 0 || kv_len > C || kv_len + buf_len + n_new < 1)
+    return fail(QKV_ERR_INVALID_ARG, f + ": need 0 <= kv_len <= C and at least one row to attend");
+  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
+                                  kv_len > 0 ? kv_len : 1, C, D, out, lse, "qkv_decode_buffered");
+  if (st != QKV_OK) return st;
+  if ((Hq / Hkv) * Sq > 64)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": (Hq/Hkv) * Sq must be <= 64");
+  if (num_splits < 0 || num_splits > 1024)
+    return fail(QKV_ERR_INVALID_ARG, f + ": num_splits must be in [0, 1024]");
+  const int64_t tail_rows = buf_len + n_new;
+  if (tail_rows > 0) {
+    if (!k_buf || !v_buf || !k_s8 || !v_s8)
+      return fail(QKV_ERR_INVALID_ARG, f + ": null buffer pointer");
+    if (!aligned(k_buf, 16) || !aligned(v_buf, 16) || !aligned(k_s8, 4) || !aligned(v_s8, 4))
+      return fail(QKV_ERR_INVALID_ARG, f + ": misaligned buffer pointer");
+  }
+  if (n_new > 0) {
+    if (!k_new || !v_new) return fail(QKV_ERR_INVALID_ARG, f + ": null new-row pointer");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+      return fail(QKV_ERR_INVALID_ARG, f + ": k_new and v_new must be 16-byte aligned");
+  }
+  const qkvfa::DecodePlan plan = buffered_plan(B, Hq, Hkv, Sq, kv_len, D, num_splits, tail_rows);
+  if ((int64_t)plan.n_split * B * Hkv > ((int64_t)1 << 32) / 512)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": too many workgroups (num_splits * B * Hkv)");
+  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, plan.n_split);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(QKV_ERR_WORKSPACE, f + ": workspace smaller than qkv_decode_buffered_workspace_bytes()");
+    if (!aligned(workspace, 16))
+      return fail(QKV_ERR_INVALID_ARG, f + ": workspace must be 16-byte aligned");
+  }
+  const qkvfa::DecodeTail tail = {k_buf, v_buf, k_s8, v_s8, k_new, v_new, buf_rows, buf_len, n_new};
+  return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C,
+                                         (int)D, softmax_scale, plan, out, lse, workspace, nullptr, nullptr,
+                                         &tail, static_cast<hipStream_t>(stream)),
+                    "qkv_decode_buffered");
 }
 
 qkv_status qkv_prefill(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,

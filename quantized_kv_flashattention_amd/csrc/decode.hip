@@ -60,6 +60,9 @@ namespace {
 __host__ __device__ constexpr int waves_for(int NB) { return NB >= 4 ? 4 : 8; }
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
+constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
+constexpr int kRaggedSplitChunks = 128;     // ragged batches: at most 4096 tokens per split
+constexpr int kMaxTail = 64;                // rows of the INT8 decode buffer one call attends
 constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (floats)
 
 // Dynamic LDS of a decode launch: the wave-merge buffer (waves x min(16, R)
@@ -70,14 +73,20 @@ inline size_t merge_lds_bytes(int D, int waves, int R, int n_split) {
   return 4 * (wave_merge > weights ? wave_merge : weights);
 }
 
+// Dynamic LDS of the buffer split: the buffered K and V rows (int8) and the
+// R x kMaxTail score table.
+inline size_t tail_lds_bytes(int D, int R) {
+  return (size_t)2 * kMaxTail * D + (size_t)4 * R * kMaxTail;
+}
+
 template <int D, int NB>
-constexpr size_t max_merge_lds_bytes() {   // largest merge_lds_bytes of a kernel variant
-  return 4 * ((size_t)waves_for(NB) * 16 * (D + 4) > (size_t)kMaxMergeLse
-                  ? (size_t)waves_for(NB) * 16 * (D + 4) : (size_t)kMaxMergeLse);
+constexpr size_t max_merge_lds_bytes() {   // largest dynamic LDS of a kernel variant
+  const size_t merge = 4 * ((size_t)waves_for(NB) * 16 * (D + 4) > (size_t)kMaxMergeLse
+                                ? (size_t)waves_for(NB) * 16 * (D + 4) : (size_t)kMaxMergeLse);
+  const size_t tail = (size_t)2 * kMaxTail * D + (size_t)4 * 64 * kMaxTail;
+  return merge > tail ? merge : tail;
 }
 constexpr int kMaxNew = 64;                 // rows one append-mode call may add
-constexpr int kMaxSplitPages = 512;
-constexpr int kRaggedSplitChunks = 128;     // ragged batches: at most 4096 tokens per split         // page ids of one split cached in LDS (paged cache)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -109,6 +118,18 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   const int32_t* block_table;
   int len_cap, page_size, max_pages, num_pages;
+  // INT8 decode buffer (tail_rows > 0): the last split attends buffered rows
+  // [0, tail_rows) of tk/tv [B, Hkv, buf_rows, D] after the kv_len cache
+  // rows the other splits attend; rows [tail_len, tail_rows) are the call's
+  // new rows tk_new/tv_new [B, Hkv, tail_rows - tail_len, D] fp32, quantized
+  // into the buffer first under the universal scales tsk/tsv [B, Hkv].
+  int8_t* tk;
+  int8_t* tv;
+  const float* tsk;
+  const float* tsv;
+  const float* tk_new;
+  const float* tv_new;
+  int tail_len, tail_rows, buf_rows;
   int64_t C;
   int Hq, Hkv, G, Sq, kv_len, split_len, n_split;
   float qk_log2;
@@ -175,6 +196,7 @@ void decode_kernel(const DecodeArgs a) {
   extern __shared__ __align__(16) float s_o[];
   __shared__ int s_last;
   __shared__ float s_den[64];
+  __shared__ float s_tm[64];    // buffer split: per-row score maximum
   // append mode: this split's new rows, indexed by row - pos
   __shared__ __align__(16) uint32_t s_nk[kMaxNew * DW];
   __shared__ __align__(16) uint32_t s_nv[kMaxNew * DW];
@@ -275,7 +297,7 @@ void decode_kernel(const DecodeArgs a) {
     if (!s_last) return;
     const int n_split = a.n_split;
     // splits that start before this sequence's length; the rest attended nothing
-    const int n_live = min(n_split, (L_b + a.split_len - 1) / a.split_len);
+    const int n_live = a.tail_rows > 0 ? n_split : min(n_split, (L_b + a.split_len - 1) / a.split_len);
     // item idx: four output values (query row idx / (D/4), dims 4 (idx % (D/4)) + 0..3)
     const int n_items = R * (D / 4);
     auto item_grow = [&](int idx) -> int64_t {
@@ -381,6 +403,118 @@ void decode_kernel(const DecodeArgs a) {
     for (int idx = threadIdx.x + 64 * kWaves; idx < n_items; idx += 64 * kWaves) finish_item(idx, false);
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
+
+  // ---- the INT8 decode buffer (TurboAttention §3.3): the last split attends
+  //      the buffered rows with plain VALU arithmetic (at most 64 rows), and
+  //      first quantizes the call's new rows into the buffer
+  if (a.tail_rows > 0 && split == a.n_split - 1) {
+    constexpr int nthr = 64 * kWaves;
+    const int T = a.tail_rows;
+    const int n_tnew = T - a.tail_len;
+    const int64_t unit64 = (int64_t)b * a.Hkv + g;
+    int8_t* gk = a.tk + unit64 * a.buf_rows * D;
+    int8_t* gv = a.tv + unit64 * a.buf_rows * D;
+    const float s8k = a.tsk[unit64];
+    const float s8v = a.tsv[unit64];
+    int8_t* lk = reinterpret_cast<int8_t*>(s_o);        // [kMaxTail][D]
+    int8_t* lv = lk + kMaxTail * D;                     // [kMaxTail][D]
+    float* lp = reinterpret_cast<float*>(lv + kMaxTail * D);   // [R][kMaxTail]
+    // (1) buffered rows -> LDS; new rows quantized into the buffer and LDS
+    for (int i = threadIdx.x; i < a.tail_len * (D / 16); i += nthr) {
+      reinterpret_cast<uint4v*>(lk)[i] = reinterpret_cast<const uint4v*>(gk)[i];
+      reinterpret_cast<uint4v*>(lv)[i] = reinterpret_cast<const uint4v*>(gv)[i];
+    }
+    for (int i = threadIdx.x; i < 2 * n_tnew * (D / 4); i += nthr) {
+      const bool isv = i >= n_tnew * (D / 4);
+      const int j4 = isv ? i - n_tnew * (D / 4) : i;
+      const int row = j4 / (D / 4);
+      const int c4 = j4 - row * (D / 4);
+      const float* src = (isv ? a.tv_new : a.tk_new) + (unit64 * n_tnew + row) * D + 4 * c4;
+      const float4v x = *reinterpret_cast<const float4v*>(src);
+      const float s8 = isv ? s8v : s8k;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) packed |= ((uint32_t)quant_code8(x[e], s8) & 0xFFu) << (8 * e);
+      const int off = (a.tail_len + row) * D + 4 * c4;
+      *reinterpret_cast<uint32_t*>((isv ? gv : gk) + off) = packed;
+      *reinterpret_cast<uint32_t*>((isv ? lv : lk) + off) = packed;
+    }
+    __syncthreads();
+    // (2) scores in log2 units, one (query row, buffered row) pair per thread
+    const float kscale = s8k * a.qk_log2;
+    for (int i = threadIdx.x; i < R * T; i += nthr) {
+      const int r = i / T;
+      const int t = i - r * T;
+      const int hg = r / Sq;
+      const uint16_t* qr = a.q + (((int64_t)b * a.Hq + g * G + hg) * Sq + (r - hg * Sq)) * D;
+      const int8_t* kr = lk + t * D;
+      float acc = 0.0f;
+#pragma unroll 4
+      for (int d = 0; d < D; d += 8) {
+        const uint4v qw = *reinterpret_cast<const uint4v*>(qr + d);
+        const uint2v kw = *reinterpret_cast<const uint2v*>(kr + d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t qb = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
+          const float kv = (float)(int8_t)(kw[e >> 2] >> (8 * (e & 3)));
+          acc = fmaf(bf16_to_f32(qb), kv, acc);
+        }
+      }
+      lp[r * kMaxTail + t] = acc * kscale;
+    }
+    __syncthreads();
+    // (3) per query row: maximum, p = 2^(s - max) in place, sum -- one wave per row
+    for (int r = wave; r < R; r += kWaves) {
+      float m = -INFINITY;
+      for (int t = lane; t < T; t += 64) m = fmaxf(m, lp[r * kMaxTail + t]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = xor_max(m, o);
+      float l = 0.0f;
+      for (int t = lane; t < T; t += 64) {
+        const float p = fast_exp2(lp[r * kMaxTail + t] - m);
+        lp[r * kMaxTail + t] = p;
+        l += p;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) l = xor_sum(l, o);
+      if (lane == 0) {
+        s_tm[r] = m;
+        s_den[r] = l;
+      }
+    }
+    __syncthreads();
+    // (4) O = s8v * sum_t p_t c_t / l, four head dims per thread; the
+    //     normalized partial and its LSE go where a split's go
+    for (int i = threadIdx.x; i < R * (D / 4); i += nthr) {
+      const int r = i / (D / 4);
+      const int d = 4 * (i - r * (D / 4));
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < T; ++t) {
+        const float p = lp[r * kMaxTail + t];
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(lv + t * D + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(p, (float)(int8_t)(cw >> (8 * e)), acc[e]);
+      }
+      const float l = s_den[r];
+      const float lse2 = s_tm[r] + log2f(l);
+      const int hg = r / Sq;
+      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (r - hg * Sq);
+      const float4v o = acc * (s8v / l);
+      if (direct) {
+        *reinterpret_cast<float4v*>(a.out + grow * D + d) = o;
+        if (d == 0 && a.lse) a.lse[grow] = lse2 * kLn2;
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(o, rpart, (uint32_t)(((grow * a.n_split + split) * D + d) * 4), 0,
+                                               kCoherent);
+        if (d == 0)
+          __hip_atomic_store(a.part_lse + grow * a.n_split + split, lse2, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (direct) return;
+    merge_splits();
+    return;
+  }
 
   // ---- a split past this sequence's length: nothing to attend.  It writes
   //      no partial (the merge skips it), only takes its ticket; alone, it
@@ -734,7 +868,8 @@ template <int D, int NB>
 hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
   dim3 grid((uint32_t)n_split * (uint32_t)Hkv * (uint32_t)B);
   const int R = args.G * args.Sq;
-  const size_t lds = merge_lds_bytes(D, waves_for(NB), R, n_split);
+  size_t lds = merge_lds_bytes(D, waves_for(NB), R, n_split);
+  if (args.tail_rows > 0 && lds < tail_lds_bytes(D, R)) lds = tail_lds_bytes(D, R);
   if (args.block_table != nullptr) return launch_paged<D, NB, true>(args, grid, lds, stream);
   return launch_paged<D, NB, false>(args, grid, lds, stream);
 }
@@ -810,7 +945,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         hipStream_t stream) {
+                         const DecodeTail* tail, hipStream_t stream) {
   DecodeArgs a;
   a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.out = out; a.lse = lse;
@@ -836,6 +971,16 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
     a.page_size = (int)varlen->page_size;
     a.max_pages = (int)varlen->max_pages;
     a.num_pages = (int)varlen->num_pages;
+  }
+  a.tk = nullptr; a.tv = nullptr; a.tsk = nullptr; a.tsv = nullptr; a.tk_new = nullptr; a.tv_new = nullptr;
+  a.tail_len = 0; a.tail_rows = 0; a.buf_rows = 0;
+  if (tail && tail->buf_len + tail->n_new > 0) {
+    a.tk = tail->k_buf; a.tv = tail->v_buf;
+    a.tsk = tail->k_s8; a.tsv = tail->v_s8;
+    a.tk_new = tail->k_new; a.tv_new = tail->v_new;
+    a.tail_len = (int)tail->buf_len;
+    a.tail_rows = (int)(tail->buf_len + tail->n_new);
+    a.buf_rows = (int)tail->buf_rows;
   }
   a.part_o = nullptr; a.part_lse = nullptr; a.tickets = nullptr; a.part_bytes = 0;
   if (plan.n_split > 1) {

@@ -100,6 +100,13 @@ __device__ __forceinline__ uint32_t quant_code(float x, float scale) {
   return (uint32_t)(int)c & 0xFu;
 }
 
+// INT8 decode-buffer code under a universal scale: clamp(rint(x / s8), -127,
+// 127) by IEEE fp32 division (outliers clamp to the range end); s8 = 0 gives 0.
+__device__ __forceinline__ int quant_code8(float x, float s8) {
+  if (s8 == 0.0f) return 0;
+  return (int)fminf(fmaxf(rintf(x / s8), -127.0f), 127.0f);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return bitcast<float>((uint32_t)b << 16);
 }

@@ -40,6 +40,21 @@ struct DecodeVarlen {
 // V are quantized into cache rows [kv_len - n_new, kv_len) first (per
 // sequence: from its own length on); the cache pointers passed to
 // launch_decode must then be writable.
+// INT8 decode buffer of a decode launch: one more split attends buffered rows
+// [0, buf_len + n_new) of k_buf/v_buf [B, Hkv, buf_rows, D] after the cache
+// rows, first quantizing the n_new fp32 rows k_new/v_new [B, Hkv, n_new, D]
+// into buffer rows [buf_len, buf_len + n_new) under the universal scales
+// k_s8/v_s8 [B, Hkv].  The plan passed to launch_decode counts that split.
+struct DecodeTail {
+  int8_t* k_buf;
+  int8_t* v_buf;
+  const float* k_s8;
+  const float* v_s8;
+  const float* k_new;
+  const float* v_new;
+  int64_t buf_rows, buf_len, n_new;
+};
+
 struct DecodeAppend {
   const float* k_new;
   const float* v_new;
@@ -51,7 +66,15 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         hipStream_t stream);
+                         const DecodeTail* tail, hipStream_t stream);
+
+hipError_t launch_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales, float* k_s8, float* v_s8,
+                               int64_t BH, int64_t L, int64_t C, hipStream_t stream);
+
+hipError_t launch_buffer_flush(const int8_t* k_buf, const int8_t* v_buf, const float* k_s8, const float* v_s8,
+                               uint8_t* k_codes, uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                               int64_t BH, int64_t T, int64_t buf_rows, int D, int64_t C, int64_t pos,
+                               hipStream_t stream);
 
 hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,

@@ -30,6 +30,28 @@ struct QuantTarget {
   uint16_t* scales;
 };
 
+// The TPR = D/8 lanes of one row, each holding 8 consecutive elements x:
+// the row's absmax (cross-lane), its fp16 scale, and this lane's dword of codes.
+template <int D>
+__device__ __forceinline__ void quantize_row_part(const float (&x)[8], int sub, uint8_t* codes_row,
+                                                  uint16_t* scale_ptr) {
+  constexpr int TPR = D / 8;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, TPR));
+  const _Float16 s16 = quant_scale(m);
+  const float s = (float)s16;
+  uint32_t packed = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= quant_code(x[i], s) << (4 * i);
+  }
+  reinterpret_cast<uint32_t*>(codes_row)[sub] = packed;
+  if (sub == 0) *scale_ptr = bitcast<uint16_t>(s16);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void quantize_append_kernel(QuantTarget t0, QuantTarget t1,
                                                               uint32_t nblk, int64_t T, int64_t C,
@@ -50,24 +72,97 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantTarget t0, Qu
   const float4* p = reinterpret_cast<const float4*>(src + ((int64_t)bh * T + t) * D) + 2 * sub;
   const float4 a = p[0];
   const float4 b = p[1];
-  float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int64_t row = (int64_t)bh * C + pos + t;
+  quantize_row_part<D>(x, sub, codes + row * (D / 2), scales + row);
+}
 
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
-#pragma unroll
-  for (int o = TPR / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, TPR));
+// Flush of the INT8 decode buffer (TurboAttention §3.3: a full buffer is
+// compressed to the low-bit cache format): buffered rows [0, T) of every
+// (batch, KV head), dequantized as the fp32 product s8 * code, are quantized
+// as int4 rows into cache rows [pos, pos + T).  Blocks [0, nblk) take K,
+// [nblk, 2 nblk) V.
+struct FlushTarget {
+  const int8_t* buf;     // [BH, buf_rows, D]
+  const float* s8;       // [BH]
+  uint8_t* codes;        // [BH, C, D/2]
+  uint16_t* scales;      // [BH, C]
+};
 
-  const _Float16 s16 = quant_scale(m);
-  const float s = (float)s16;
-  uint32_t packed = 0;
-  if (s != 0.0f) {
+template <int D>
+__global__ __launch_bounds__(256) void buffer_flush_kernel(FlushTarget t0, FlushTarget t1, uint32_t nblk,
+                                                           int64_t T, int64_t buf_rows, int64_t C, int64_t pos,
+                                                           uint32_t tblocks) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const bool second = blockIdx.x >= nblk;
+  const uint32_t blk = second ? blockIdx.x - nblk : blockIdx.x;
+  const FlushTarget& tg = second ? t1 : t0;
+  const uint32_t bh = blk / tblocks;
+  const uint32_t tb = blk - bh * tblocks;
+  const int sub = threadIdx.x % TPR;
+  const int64_t t = (int64_t)tb * RPB + threadIdx.x / TPR;
+  if (t >= T) return;  // whole TPR-lane groups leave together
+  const float s8 = tg.s8[bh];
+  const uint2 c = *reinterpret_cast<const uint2*>(tg.buf + ((int64_t)bh * buf_rows + t) * D + 8 * sub);
+  float x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= quant_code(x[i], s) << (4 * i);
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s8 * (float)(int8_t)(c.x >> (8 * i));
+    x[4 + i] = s8 * (float)(int8_t)(c.y >> (8 * i));
   }
   const int64_t row = (int64_t)bh * C + pos + t;
-  reinterpret_cast<uint32_t*>(codes + row * (D / 2))[sub] = packed;
-  if (sub == 0) scales[row] = bitcast<uint16_t>(s16);
+  quantize_row_part<D>(x, sub, tg.codes + row * (D / 2), tg.scales + row);
+}
+
+hipError_t launch_buffer_flush(const int8_t* k_buf, const int8_t* v_buf, const float* k_s8, const float* v_s8,
+                               uint8_t* k_codes, uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                               int64_t BH, int64_t T, int64_t buf_rows, int D, int64_t C, int64_t pos,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int rpb = 256 / (D / 8);
+  const int64_t tblocks = (T + rpb - 1) / rpb;
+  const int64_t nblk = BH * tblocks;
+  if (2 * nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const FlushTarget t0 = {k_buf, k_s8, k_codes, k_scales};
+  const FlushTarget t1 = {v_buf, v_s8, v_codes, v_scales};
+  const dim3 grid((uint32_t)(2 * nblk));
+  if (D == 128)
+    buffer_flush_kernel<128><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, buf_rows, C, pos,
+                                                             (uint32_t)tblocks);
+  else
+    buffer_flush_kernel<64><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, buf_rows, C, pos,
+                                                            (uint32_t)tblocks);
+  return hipGetLastError();
+}
+
+// Universal INT8 scale of the decode buffer (TurboAttention §3.3 and §5: the
+// previous cache's value-range maximum; newer values beyond it are clamped):
+// s8 = (7 * max_t s4[t]) / 127 over cache rows [0, L) of every (batch, KV
+// head), with 7 * s4 (an fp16 value times 7, exact in fp32) the row's absmax
+// as its int4 scale records it.  One wave per (batch, KV head) and tensor.
+__global__ __launch_bounds__(256) void buffer_scale_kernel(const uint16_t* k_scales, const uint16_t* v_scales,
+                                                           float* k_s8, float* v_s8, int64_t BH, int64_t L,
+                                                           int64_t C) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= 2 * BH) return;   // whole waves leave together
+  const bool isv = w >= BH;
+  const int64_t bh = isv ? w - BH : w;
+  const uint16_t* sc = (isv ? v_scales : k_scales) + bh * C;
+  float m = 0.0f;   // scales are non-negative
+  for (int64_t t = lane; t < L; t += 64) m = fmaxf(m, (float)bitcast<_Float16>(sc[t]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) (isv ? v_s8 : k_s8)[bh] = (m * 7.0f) / 127.0f;
+}
+
+hipError_t launch_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales, float* k_s8, float* v_s8,
+                               int64_t BH, int64_t L, int64_t C, hipStream_t stream) {
+  const int64_t nblk = (2 * BH + 3) / 4;
+  if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+  buffer_scale_kernel<<<dim3((uint32_t)nblk), dim3(256), 0, stream>>>(k_scales, v_scales, k_s8, v_s8, BH, L, C);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,

@@ -24,6 +24,11 @@ def lib():
                                     vp, vp, vp, sz, vp]
     L.qkv_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                    i64, i64, f32, ci, vp, vp, vp, sz, vp]
+    L.qkv_buffer_scale.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    L.qkv_buffer_flush.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    L.qkv_decode_buffered.argtypes = [vp] * 11 + [i64] * 10 + [f32, ci, vp, vp, vp, sz, vp]
+    L.qkv_decode_buffered_workspace_bytes.restype = sz
+    L.qkv_decode_buffered_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
     L.qkv_last_error.restype = ctypes.c_char_p
     L.qkv_status_string.restype = ctypes.c_char_p
     L.qkv_decode_workspace_bytes.restype = sz
@@ -40,7 +45,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"qkv_quantize_append", "qkv_decode", "qkv_decode_append", "qkv_decode_paged",
-                          "qkv_prefill",
+                          "qkv_buffer_scale", "qkv_buffer_flush", "qkv_decode_buffered",
+                          "qkv_decode_buffered_workspace_bytes", "qkv_prefill",
                           "qkv_quantize_append_kv", "qkv_decode_workspace_bytes",
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version"}
     for n in names:
@@ -195,3 +201,64 @@ def test_decode_paged_argument_errors(lib):
     assert _paged(lib, ps=1 << 20, mp=1 << 12) == 2      # capacity beyond 2^31 rows
     assert _paged(lib, maxlen=256, ns=3) == 3   # needs a workspace
     assert b"qkv_decode_paged" in lib.qkv_last_error()
+
+
+def test_buffer_scale_argument_errors(lib):
+    f = lambda **kw: lib.qkv_buffer_scale(kw.get("ks", P), kw.get("vs", P), kw.get("B", 1), 1, kw.get("L", 4),
+                                          kw.get("C", 8), kw.get("k8", P), kw.get("v8", P), None)
+    assert f(L=9) == 1
+    assert f(L=-1) == 1
+    assert f(ks=None) == 1
+    assert f(k8=P + 2) == 1
+    assert f(B=0) == 1
+
+
+def test_buffer_flush_argument_errors(lib):
+    def f(**kw):
+        a = dict(kb=P, vb=P, k8=P, v8=P, rows=64, T=10, kc=P, ks=P, vc=P, vs=P, B=1, Hkv=1, D=128, C=100, pos=0)
+        a.update(kw)
+        return lib.qkv_buffer_flush(a["kb"], a["vb"], a["k8"], a["v8"], a["rows"], a["T"], a["kc"], a["ks"],
+                                    a["vc"], a["vs"], a["B"], a["Hkv"], a["D"], a["C"], a["pos"], None)
+    assert f(rows=65) == 1
+    assert f(T=65, rows=64) == 1
+    assert f(pos=91) == 1
+    assert f(D=96) == 2
+    assert f(kb=None) == 1
+    assert f(vb=P + 8) == 1
+    assert f(T=0, kb=None) == 0        # nothing to do
+
+
+def _dbuf(lib, **kw):
+    a = dict(q=P, kn=P, vn=P, kc=P, ks=P, vc=P, vs=P, kb=P, vb=P, k8=P, v8=P, B=1, Hq=4, Hkv=2, Sq=1, L=100,
+             C=128, rows=64, blen=3, n=1, D=128, scale=0.1, ns=0, out=P, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qkv_decode_buffered(a["q"], a["kn"], a["vn"], a["kc"], a["ks"], a["vc"], a["vs"], a["kb"], a["vb"],
+                                   a["k8"], a["v8"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["L"], a["C"], a["rows"],
+                                   a["blen"], a["n"], a["D"], a["scale"], a["ns"], a["out"], a["lse"], a["ws"],
+                                   a["wsb"], None)
+
+
+def test_decode_buffered_argument_errors(lib):
+    assert _dbuf(lib, rows=65) == 2
+    assert _dbuf(lib, blen=64, n=1) == 1        # more rows than the buffer holds
+    assert _dbuf(lib, blen=-1) == 1
+    assert _dbuf(lib, L=129) == 1
+    assert _dbuf(lib, L=0, blen=0, n=0) == 1    # nothing to attend
+    assert _dbuf(lib, kb=None) == 1
+    assert b"buffer" in lib.qkv_last_error()
+    assert _dbuf(lib, k8=P + 1) == 1
+    assert _dbuf(lib, kn=None) == 1
+    assert _dbuf(lib, vn=P + 4) == 1
+    assert _dbuf(lib, D=80) == 2
+    assert _dbuf(lib, Sq=33) == 2
+    assert _dbuf(lib, ns=3) == 3                # body splits + the buffer split need a workspace
+    assert b"qkv_decode_buffered" in lib.qkv_last_error()
+    assert _dbuf(lib, q=None) == 1
+
+
+def test_decode_buffered_workspace_size(lib):
+    # no cache rows: the buffer split alone writes the output directly
+    assert lib.qkv_decode_buffered_workspace_bytes(1, 4, 2, 1, 0, 128, 0) == 0
+    # one cache split + the buffer split
+    n = lib.qkv_decode_buffered_workspace_bytes(1, 4, 2, 1, 100, 128, 1)
+    assert n >= 4 * 2 * 128 * 4
