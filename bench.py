@@ -17,7 +17,8 @@ packed KV bytes (codes + scales) per step, the roofline of the decode kernel
 in the timed region -- one launch per step -- measured with HIP events on the
 launch stream), the CPU oracle timed on a
 bounded sample of the same workload, and secondary figures (128K-token
-decode, a ragged 64-sequence batch over a paged cache, 16K causal prefill
+decode, a ragged 64-sequence batch over a paged cache, the decode step with
+the INT8 buffer, 16K causal prefill
 TFLOP/s, ViT-B prefill, bulk quantize-append).
 Everything else goes to stderr.
 
@@ -293,6 +294,68 @@ def bench_paged(torch, qkv, w, steps):
     return res
 
 
+def bench_buffered(torch, qkv, w, steps, buf_len=31):
+    """Decode step with the INT8 buffer: int4 rows [0, L - buf_len - 1), buf_len
+    buffered rows, and the step's new row quantized into the buffer -- L rows
+    attended in all, as in the headline step.  Also the flush of a full
+    buffer (64 rows) into the int4 cache, which runs once every 64 steps."""
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w)
+    kv_bytes, _ = decode_bytes(w)
+    n_copies = max(4, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    caches = upload_cache(torch, qkv, k, v, n_copies)
+    body = w.L - buf_len - 1
+    rows = torch.from_numpy(k[:, :, body:].copy()).cuda(), torch.from_numpy(v[:, :, body:].copy()).cuda()
+    del k, v
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    bufs = []
+    for c in caches:
+        b = qkv.DecodeBuffer.empty(w.B, w.Hkv, w.D, device="cuda")
+        qkv.buffer_scale(c, body, b)
+        qkv.decode_buffered(q, c, body, b, rows[0][:, :, :buf_len].contiguous(), rows[1][:, :, :buf_len].contiguous(),
+                            out=out)
+        bufs.append(b)
+    k_new, v_new = rows[0][:, :, buf_len:].contiguous(), rows[1][:, :, buf_len:].contiguous()
+    ws = torch.zeros(max(qkv.decode_buffered_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, body, w.D), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        bufs[i].length = buf_len          # every timed step appends the same row
+        qkv.decode_buffered(q, caches[i], body, bufs[i], k_new, v_new, softmax_scale=w.softmax_scale, out=out,
+                            workspace=ws)
+
+    for i in range(5):
+        step(i % n_copies)
+    torch.cuda.synchronize()
+    ms = region_ms(torch, step, steps, n_copies)
+    # flush of a full buffer (64 rows) into int4 cache rows
+    full = qkv.DecodeBuffer.empty(w.B, w.Hkv, w.D, device="cuda")
+    full.k.random_(-127, 128)
+    full.v.random_(-127, 128)
+    full.k_s8.fill_(0.02)
+    full.v_s8.fill_(0.02)
+
+    def flush(i):
+        full.length = 64
+        qkv.buffer_flush(full, caches[i], 0)
+
+    for i in range(3):
+        flush(i % n_copies)
+    flush_ms = region_ms(torch, flush, 20, n_copies)
+    int4 = 2 * w.B * w.Hkv * body * (w.D // 2 + 2)
+    buffered = 2 * w.B * w.Hkv * (buf_len + 1) * w.D + 2 * w.B * w.Hkv * 4
+    other = w.B * w.Hq * w.Sq * w.D * 6 + 2 * w.B * w.Hkv * w.D * 4
+    res = {"workload": w.name + "+int8_buffer", "int4_rows": body, "buffered_rows": buf_len + 1,
+           "step_ms": ms, "algorithmic_bytes": int4 + buffered + other,
+           "GBps": (int4 + buffered + other) / (ms * 1e-3) / 1e9,
+           "flush_64_rows_ms": flush_ms, "flush_ms_per_step": flush_ms / 64}
+    res["frac_hbm"] = res["GBps"] / HBM_PEAK_GBS
+    del caches, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(torch, qkv, w, iters):
     from qkv_inputs import make_qkv
     q_bits, k, v = make_qkv(w)
@@ -518,6 +581,8 @@ def main():
         secondary["ragged_paged_decode"] = bench_paged(torch, qkv, workload("ragged_paged_decode"),
                                                        max(args.steps // 2, 10))
         log("paged:", json.dumps(secondary["ragged_paged_decode"]))
+        secondary["int8_buffer_decode"] = bench_buffered(torch, qkv, w3, max(args.steps, 20))
+        log("buffered:", json.dumps(secondary["int8_buffer_decode"]))
     if args.only in ("all", "prefill"):
         secondary["causal_prefill_16k"] = bench_prefill(torch, qkv, workload("causal_prefill_16k"), 10)
         log("prefill:", json.dumps(secondary["causal_prefill_16k"]))
