@@ -45,6 +45,12 @@
 // waves whose rows see nothing of a tile skip its math.  Workgroups are
 // dispatched longest-first (highest query block first).
 //
+// The tile loop is instantiated twice: tiles visible to every row of the
+// workgroup (all but the last few of a causal block) run a body with no
+// mask, no per-wave skip and no bound/mask join, which saves about a third
+// of the vector instructions per tile; the remaining tiles run the general
+// body.
+//
 // LDS layouts (one buffer):
 //   K: fp16 16-byte chunk planes: chunk c (head dims 8c..8c+7 in
 //      unpack8_perm order) of token t at [c][t][8].  The QK reads of 16
@@ -60,6 +66,8 @@
 //      ordered [j][tb][vq][i] for token 32 tb + 8 vq + 4 j + i, so a lane
 //      reads the 32 V scales of its tokens as four 16-byte loads.
 #include <math.h>
+
+#include <type_traits>
 
 #include "qkvfa_device.hpp"
 #include "qkvfa_internal.h"
@@ -271,13 +279,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   load_tile(BN);
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  // One key tile.  ALL_FULL: the tile is visible to every row of the
+  // workgroup, so no wave skips it and no mask is evaluated.
+  auto step = [&](int kt, auto all_full) {
+    constexpr bool ALL_FULL = decltype(all_full)::value;
     const int t0 = kt * BN;
     const int buf = kt & 1;
     const _Float16* sk_ = s_k + buf * KBUF;
     const _Float16* sv_ = s_v + buf * VBUF;
     const float* csk_ = s_csk[buf];
-    const bool need = wave_active && (!CAUSAL || t0 <= wrow_hi + off);
+    const bool need = ALL_FULL || (wave_active && (!CAUSAL || t0 <= wrow_hi + off));
 
     // Convert the next tile into the other buffer and fetch the one after.
     // On the last tiles this converts and fetches past the end (zeros, or
@@ -304,7 +315,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     if (need) {
       // ---- online softmax; lane's tokens: 32 tb + 8 (v/4) + 4 j + v%4
-      const bool full = (t0 + BN <= kv_len) && (!CAUSAL || t0 + BN - 1 <= wrow_lo + off);
+      const bool full = ALL_FULL || ((t0 + BN <= kv_len) && (!CAUSAL || t0 + BN - 1 <= wrow_lo + off));
       auto csk4 = [&](int tb, int vq) {
         return *reinterpret_cast<const float4v*>(csk_ + 32 * tb + 8 * vq + 4 * j);
       };
@@ -402,7 +413,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
     __syncthreads();  // tile kt+1 is in LDS; nobody still reads buffer `buf`
-  }
+  };
+  int n_full = kv_len / BN;
+  if (CAUSAL) n_full = min(n_full, (q0 + off + 1) / BN);
+  n_full = min(n_full, n_tiles);
+  int kt = 0;
+  for (; kt < n_full; ++kt) step(kt, std::integral_constant<bool, true>{});
+  for (; kt < n_tiles; ++kt) step(kt, std::integral_constant<bool, false>{});
 
   // ---- epilogue: O = O^T / l; lane owns row qrow, head dims 32 db + 8 vq + 4 j + i
   const float l = xor_sum(l_run, 32);
