@@ -521,7 +521,7 @@ def summarize_profiles(root: str):
     w_scale = wc * 1024 / COPY_BYTES     # same, writes
     from qkv_inputs import workload
     w = workload("llama3_8b_decode")
-    alg = decode_bytes(w)[1]
+    alg = decode_bytes(w)[1] + 2 * w.B * w.Hkv * w.D * 4   # + the appended rows (fp32 K and V)
     read_b = fd * 1024 / f_scale
     write_b = wd * 1024 / w_scale
     result = {

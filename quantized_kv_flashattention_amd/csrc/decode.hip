@@ -230,6 +230,9 @@ void decode_kernel(const DecodeArgs a) {
     pos_b = lb;
     L_b = lb + (append ? a.n_new : 0);
   }
+  // Query row `row` of this group (head g G + row / Sq, position row % Sq)
+  // is row grow0 + row of q, out and lse: heads of a group are adjacent.
+  const int64_t grow0 = ((int64_t)b * a.Hq + (int64_t)g * G) * Sq;
   const int t_begin = split * a.split_len;
   const int t_end = min(L_b, t_begin + a.split_len);   // <= t_begin: nothing to attend here
 
@@ -257,7 +260,6 @@ void decode_kernel(const DecodeArgs a) {
       return kvrow0 + t;
     }
   };
-  const float sc_mul = (lane < 32) ? a.qk_log2 : 1.0f;
 
   // Loop-invariant per-lane byte offsets inside a chunk.
   const uint32_t offk = (uint32_t)((8 * (r >> 2) + (r & 3)) * ROWB + 4 * KK * j);  // +4 rows for kb = 1
@@ -302,8 +304,7 @@ void decode_kernel(const DecodeArgs a) {
     const int n_items = R * (D / 4);
     auto item_grow = [&](int idx) -> int64_t {
       const int row = idx / (D / 4);
-      const int hg = row / Sq;
-      return ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+      return grow0 + row;
     };
     auto load16 = [&](uint32_t off0, int s0, float4v (&o)[16]) {
 #pragma unroll
@@ -339,8 +340,7 @@ void decode_kernel(const DecodeArgs a) {
           v[u] = -INFINITY;
           if (idx < total) {
             const int row = idx / n_live;
-            const int hg = row / Sq;
-            const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+            const int64_t grow = grow0 + row;
             v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
           }
@@ -368,8 +368,7 @@ void decode_kernel(const DecodeArgs a) {
       for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
       if (lane == 0) {
         s_den[row] = den;
-        const int hg = row / Sq;
-        const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+        const int64_t grow = grow0 + row;
         if (a.lse) a.lse[grow] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
       }
     }
@@ -402,6 +401,320 @@ void decode_kernel(const DecodeArgs a) {
     if ((int)threadIdx.x < n_items) finish_item(threadIdx.x, true);
     for (int idx = threadIdx.x + 64 * kWaves; idx < n_items; idx += 64 * kWaves) finish_item(idx, false);
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // The chunk loop, the wave merge and the partial (or direct) output of a
+  // split that has cache rows to attend.
+  auto main_body = [&]() {
+    // Codes of the chunk starting at token c0, through buffer descriptors whose
+    // range ends at t_main <= kv_len (the split end, before any new rows): the
+    // hardware returns zero for
+    // any row at or past it (those tokens are masked) without touching memory.
+    // So no load leaves the valid rows, the last chunk needs no clamping, and a
+    // chunk past the split can be "loaded" unconditionally (all zeros, no
+    // traffic), which keeps the prefetch branch-free: a conditional prefetch
+    // makes the compiler wait for every outstanding load where the paths join.
+    auto load_chunk = [&](int c0, ChunkRegs<D>& cr, int lim, bool from_lds) {
+      // a chunk is 32 rows; with a paged cache it never straddles a page.  The
+      // clamp is made scalar explicitly: computed in a vector register, the
+      // descriptor would look divergent and each load would become a loop.
+      const int rows_left = __builtin_amdgcn_readfirstlane(min(max(lim - c0, 0), kChunk));
+      const int64_t row0 = row_of(c0, from_lds);
+      const rsrc_t rk = make_rsrc(a.kc + row0 * ROWB, rows_left * ROWB);
+      const rsrc_t rv = make_rsrc(a.vc + row0 * ROWB, rows_left * ROWB);
+      const rsrc_t rks = make_rsrc(a.ks + row0, rows_left * 2);
+      const rsrc_t rvs = make_rsrc(a.vs + row0, rows_left * 2);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (KK == 4) {
+          const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
+        } else {
+          const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
+          cr.kw[kb][0] = w[0];
+          cr.kw[kb][1] = w[1];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
+      cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
+      cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
+    };
+
+    const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
+    ChunkRegs<D> cur;
+    load_chunk(t_begin + wave * kChunk, cur, t_main, false);
+
+    // ---- append mode: quantize the new rows (one wave per row and tensor,
+    //      from the last wave down: with one row block the first half of the
+    //      waves converts the query meanwhile), while the first chunk loads
+    if (append) {
+      const int ntask = 2 * max(new_hi - new_lo, 0);
+      for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
+        const int t = new_lo + (task >> 1);
+        const bool isv = (task & 1) != 0;
+        const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - pos_b)) * D;
+        const int64_t row = row_of(t, false);
+        uint8_t* gcodes = (isv ? a.vc_w : a.kc_w) + row * ROWB;
+        uint16_t* gscale = (isv ? a.vs_w : a.ks_w) + row;
+        uint8_t* lcodes = reinterpret_cast<uint8_t*>(isv ? s_nv : s_nk) + (t - pos_b) * ROWB;
+        uint16_t* lscale = (isv ? s_nvs : s_nks) + (t - pos_b);
+        quantize_row_wave<D>(src, lane, gcodes, gscale, lcodes, lscale);
+      }
+    }
+
+
+    if constexpr (PAGED) {
+      for (int i = threadIdx.x; i < npg; i += 64 * kWaves) {
+        const int idx = min(pg0 + i, a.max_pages - 1);
+        s_pid[i] = min(max(a.block_table[(int64_t)b * a.max_pages + idx], 0), a.num_pages - 1);
+      }
+    }
+
+    // Query operand (B of S^T = K Q^T): query row nb*16 + r, k = 8j + e <->
+    // head dim 8*(KK*j + kk) + perm8(e), matching the K lane's dword order.
+    // Converted once into LDS (shared by the eight waves): 16-byte chunk c of
+    // row x sits at chunk c ^ (x % 16), so the 16 rows a wave reads together
+    // fall in different banks.
+    for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 64 * kWaves) {
+      const int row = idx / DW;
+      const int c = idx - row * DW;
+      half8v h = half8v{};
+      if (row < R) {
+        const uint16_t* qr = a.q + (grow0 + row) * D + 8 * c;
+        const uint4v w = *reinterpret_cast<const uint4v*>(qr);
+        uint16_t e16[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
+          e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)bf16_to_f32(e16[perm8(e)]);
+      }
+      *reinterpret_cast<half8v*>(&s_q[(row * DW + (c ^ (row & 15 & (DW - 1)))) * 8]) = h;
+    }
+    __syncthreads();
+
+    float m_run[NB], l_run[NB];
+    float4v o_acc[NB][NPB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_run[nb] = -INFINITY;
+      l_run[nb] = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NPB; ++p) o_acc[nb][p] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
+    auto process_chunk = [&](int c0, ChunkRegs<D>& cr, int lim) {
+        // ---- scales: each lane converts one, the wave reads its eight back.  A
+        //      token at or past the split end gets bias -inf (score masked), so
+        //      the score is one FMA on every chunk, full or not.
+        // lanes 0-31: K column scale x softmax scale x log2 e; lanes 32-63: V scale
+        const float scv = f16bits_to_f32(lane < 32 ? cr.sk : cr.sv);
+        s_sc[wave][lane] = lane < 32 ? scv * a.qk_log2 : scv;
+        if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < lim) ? 0.0f : -INFINITY;
+        const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
+        const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
+        const float4v sv0 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j]);
+        const float4v sv1 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j + 4]);
+        const float4v mb0 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j]);
+        const float4v mb1 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j + 4]);
+        const float csk[8] = {ck0[0], ck0[1], ck0[2], ck0[3], ck1[0], ck1[1], ck1[2], ck1[3]};
+        const float sv[8] = {sv0[0], sv0[1], sv0[2], sv0[3], sv1[0], sv1[1], sv1[2], sv1[3]};
+        const float mbias[8] = {mb0[0], mb0[1], mb0[2], mb0[3], mb1[0], mb1[1], mb1[2], mb1[3]};
+
+        if constexpr (D == 64) {
+          // lanes 8..15 own nibbles 4..7 of their dword: move them down
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cr.vw[e] = (r >= 8) ? (cr.vw[e] >> 16) : cr.vw[e];
+        }
+
+        // ---- scores S^T for 2 x 16 tokens and every 16-row block; each K operand
+        //      is converted once and used for all row blocks
+        float4v s_t[NB][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const half8v kop = unpack8_perm(cr.kw[kb][kk]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              const int qrow = nb * 16 + r;
+              const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
+              const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+              s_t[nb][kb] = mfma16x16x32(kop, qop, s_t[nb][kb]);
+            }
+          }
+        }
+
+        // ---- online softmax per row block -> P^T operand (V scale folded in)
+        half8v pop[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float x[8];
+          float mloc = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = fmaf(s_t[nb][e >> 2][e & 3], csk[e], mbias[e]);
+            mloc = fmaxf(mloc, x[e]);
+          }
+          mloc = xor_max(mloc, 16);
+          mloc = xor_max(mloc, 32);
+          const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
+          const float alpha = fast_exp2(m_run[nb] - m_new);
+          float lsum = 0.0f;
+          uint4v pw;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(x[e] - m_new);
+            const float p1 = fast_exp2(x[e + 1] - m_new);
+            lsum += p0 + p1;
+            pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
+          }
+          pop[nb] = bitcast<half8v>(pw);
+          l_run[nb] = l_run[nb] * alpha + lsum;
+          m_run[nb] = m_new;
+          if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
+          }
+        }
+
+        // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
+        //      token dwords, low and high nibble -> exact fp16 (token e = k index)
+#pragma unroll
+        for (int k = 0; k < NPB / 2; ++k) {
+          uint4v wlo, whi;
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh) {
+            const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
+            wlo[hh] = bitcast<uint32_t>(nib_lo_pair(xb));
+            whi[hh] = bitcast<uint32_t>(nib_hi_pair(xb));
+          }
+          const half8v vlo = bitcast<half8v>(wlo);
+          const half8v vhi = bitcast<half8v>(whi);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
+            o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
+          }
+        }
+    };
+
+    for (int c = wave; c < n_chunks; c += kWaves) {
+      const int c0 = t_begin + c * kChunk;
+      // Compiler-only barrier: keeps the query-operand LDS reads inside the loop
+      // instead of hoisted into (NB * D / 8) live registers per lane.
+      asm volatile("" ::: "memory");
+      if constexpr (kPrefetch) {
+        ChunkRegs<D> nxt;
+        load_chunk(c0 + kWaves * kChunk, nxt, t_main, true);
+        process_chunk(c0, cur, t_main);
+        cur = nxt;
+      } else {
+        process_chunk(c0, cur, t_main);
+        load_chunk(c0 + kWaves * kChunk, cur, t_main, true);
+      }
+    }
+
+    // ---- append mode: tail chunks [t_main, t_end).  Rows before pos come from
+    //      the cache (the load range ends at pos, so no row at or past it is
+    //      read), rows from pos on from the LDS copy of the new rows.
+    if (append) {
+      for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
+        if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
+        ChunkRegs<D> cr;
+        load_chunk(c0, cr, max(pos_b, c0), true);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
+          if (tk >= pos_b && tk < new_hi) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) cr.kw[kb][kk] = s_nk[(tk - pos_b) * DW + KK * j + kk];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tv = c0 + 8 * j + e;
+          if (tv >= pos_b && tv < new_hi) cr.vw[e] = s_nv[(tv - pos_b) * DW + (r % DW)];
+        }
+        const int ts = c0 + (lane & 31);
+        if (ts >= pos_b && ts < new_hi) {
+          cr.sk = s_nks[ts - pos_b];
+          cr.sv = s_nvs[ts - pos_b];
+        }
+        process_chunk(c0, cr, t_end);
+      }
+    }
+
+    // ---- merge the eight waves through LDS, one 16-row block at a time
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float l = xor_sum(l_run[nb], 16);
+      l = xor_sum(l, 32);
+      if (j == 0) {
+        s_m[wave][r] = m_run[nb];
+        s_l[wave][r] = l;
+      }
+      float* orow = s_o + (wave * rows_o + r) * OSTR;
+      if (r < rows_o) {   // rows past R are padding of the 16-row block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (D == 128) {
+            // head dims 32j + 8i + p, p = 0..7
+            float4v lo = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
+            float4v hi = {o_acc[nb][4][i], o_acc[nb][5][i], o_acc[nb][6][i], o_acc[nb][7][i]};
+            *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i) = lo;
+            *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i + 4) = hi;
+          } else {
+            // M-row m = 4j + i holds head dims 8(m%8) + 4(m/8) + p, p = 0..3
+            const int m = 4 * j + i;
+            float4v v4 = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
+            *reinterpret_cast<float4v*>(orow + 8 * (m & 7) + 4 * (m >> 3)) = v4;
+          }
+        }
+      }
+      __syncthreads();
+      const int rows_here = min(16, R - nb * 16);
+      for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += 64 * kWaves) {
+        const int rr = idx / (D / 4);
+        const int d = 4 * (idx - rr * (D / 4));
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+        // every wave empty: weights 0 (not reached by a split with rows)
+        const float Mz = (M == -INFINITY) ? 0.0f : M;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float wt = fast_exp2(s_m[w][rr] - Mz);   // empty waves: exp2(-inf) = 0
+          acc += wt * *reinterpret_cast<const float4v*>(s_o + (w * rows_o + rr) * OSTR + d);
+          den += wt * s_l[w][rr];
+        }
+        const int64_t grow = grow0 + nb * 16 + rr;
+        // nothing attended: output 0, LSE -inf
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        const float lse2 = den > 0.0f ? M + log2f(den) : -INFINITY;
+        if (direct) {
+          *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * inv;
+          if (d == 0 && a.lse) a.lse[grow] = lse2 * kLn2;
+        } else {
+          // device-coherent stores (sc1): visible to every XCD without an L2 writeback
+          __builtin_amdgcn_raw_buffer_store_b128(
+              acc * inv, rpart, (uint32_t)(((grow * a.n_split + split) * D + d) * 4), 0, kCoherent);
+          if (d == 0)   // log2 units
+            __hip_atomic_store(a.part_lse + grow * a.n_split + split, lse2, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+    }
   };
 
   // ---- the INT8 decode buffer (TurboAttention §3.3): the last split attends
@@ -445,8 +758,7 @@ void decode_kernel(const DecodeArgs a) {
     for (int i = threadIdx.x; i < R * T; i += nthr) {
       const int r = i / T;
       const int t = i - r * T;
-      const int hg = r / Sq;
-      const uint16_t* qr = a.q + (((int64_t)b * a.Hq + g * G + hg) * Sq + (r - hg * Sq)) * D;
+      const uint16_t* qr = a.q + (grow0 + r) * D;
       const int8_t* kr = lk + t * D;
       float acc = 0.0f;
 #pragma unroll 4
@@ -497,8 +809,7 @@ void decode_kernel(const DecodeArgs a) {
       }
       const float l = s_den[r];
       const float lse2 = s_tm[r] + log2f(l);
-      const int hg = r / Sq;
-      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (r - hg * Sq);
+      const int64_t grow = grow0 + r;
       const float4v o = acc * (s8v / l);
       if (direct) {
         *reinterpret_cast<float4v*>(a.out + grow * D + d) = o;
@@ -511,344 +822,23 @@ void decode_kernel(const DecodeArgs a) {
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (direct) return;
-    merge_splits();
-    return;
-  }
-
   // ---- a split past this sequence's length: nothing to attend.  It writes
   //      no partial (the merge skips it), only takes its ticket; alone, it
   //      writes the empty result (output 0, LSE -inf).
-  if (t_end <= t_begin) {
+  } else if (t_end <= t_begin) {
     if (direct) {
       for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
         const int row = idx / (D / 4);
         const int d = 4 * (idx - row * (D / 4));
-        const int hg = row / Sq;
-        const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + (row - hg * Sq);
+        const int64_t grow = grow0 + row;
         *reinterpret_cast<float4v*>(a.out + grow * D + d) = float4v{0.f, 0.f, 0.f, 0.f};
         if (d == 0 && a.lse) a.lse[grow] = -INFINITY;
       }
-      return;
     }
-    merge_splits();
-    return;
-  }
-
-  // Codes of the chunk starting at token c0, through buffer descriptors whose
-  // range ends at t_main <= kv_len (the split end, before any new rows): the
-  // hardware returns zero for
-  // any row at or past it (those tokens are masked) without touching memory.
-  // So no load leaves the valid rows, the last chunk needs no clamping, and a
-  // chunk past the split can be "loaded" unconditionally (all zeros, no
-  // traffic), which keeps the prefetch branch-free: a conditional prefetch
-  // makes the compiler wait for every outstanding load where the paths join.
-  auto load_chunk = [&](int c0, ChunkRegs<D>& cr, int lim, bool from_lds) {
-    // a chunk is 32 rows; with a paged cache it never straddles a page.  The
-    // clamp is made scalar explicitly: computed in a vector register, the
-    // descriptor would look divergent and each load would become a loop.
-    const int rows_left = __builtin_amdgcn_readfirstlane(min(max(lim - c0, 0), kChunk));
-    const int64_t row0 = row_of(c0, from_lds);
-    const rsrc_t rk = make_rsrc(a.kc + row0 * ROWB, rows_left * ROWB);
-    const rsrc_t rv = make_rsrc(a.vc + row0 * ROWB, rows_left * ROWB);
-    const rsrc_t rks = make_rsrc(a.ks + row0, rows_left * 2);
-    const rsrc_t rvs = make_rsrc(a.vs + row0, rows_left * 2);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (KK == 4) {
-        const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
-      } else {
-        const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
-        cr.kw[kb][0] = w[0];
-        cr.kw[kb][1] = w[1];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
-    cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
-    cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
-  };
-
-  const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
-  ChunkRegs<D> cur;
-  load_chunk(t_begin + wave * kChunk, cur, t_main, false);
-
-  // ---- append mode: quantize the new rows (one wave per row and tensor,
-  //      from the last wave down: with one row block the first half of the
-  //      waves converts the query meanwhile), while the first chunk loads
-  if (append) {
-    const int ntask = 2 * max(new_hi - new_lo, 0);
-    for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
-      const int t = new_lo + (task >> 1);
-      const bool isv = (task & 1) != 0;
-      const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - pos_b)) * D;
-      const int64_t row = row_of(t, false);
-      uint8_t* gcodes = (isv ? a.vc_w : a.kc_w) + row * ROWB;
-      uint16_t* gscale = (isv ? a.vs_w : a.ks_w) + row;
-      uint8_t* lcodes = reinterpret_cast<uint8_t*>(isv ? s_nv : s_nk) + (t - pos_b) * ROWB;
-      uint16_t* lscale = (isv ? s_nvs : s_nks) + (t - pos_b);
-      quantize_row_wave<D>(src, lane, gcodes, gscale, lcodes, lscale);
-    }
-  }
-
-
-  if constexpr (PAGED) {
-    for (int i = threadIdx.x; i < npg; i += 64 * kWaves) {
-      const int idx = min(pg0 + i, a.max_pages - 1);
-      s_pid[i] = min(max(a.block_table[(int64_t)b * a.max_pages + idx], 0), a.num_pages - 1);
-    }
-  }
-
-  // Query operand (B of S^T = K Q^T): query row nb*16 + r, k = 8j + e <->
-  // head dim 8*(KK*j + kk) + perm8(e), matching the K lane's dword order.
-  // Converted once into LDS (shared by the eight waves): 16-byte chunk c of
-  // row x sits at chunk c ^ (x % 16), so the 16 rows a wave reads together
-  // fall in different banks.
-  for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 64 * kWaves) {
-    const int row = idx / DW;
-    const int c = idx - row * DW;
-    half8v h = half8v{};
-    if (row < R) {
-      const int hg = row / Sq;
-      const int sq = row - hg * Sq;
-      const uint16_t* qr = a.q + (((int64_t)b * a.Hq + g * G + hg) * Sq + sq) * D + 8 * c;
-      const uint4v w = *reinterpret_cast<const uint4v*>(qr);
-      uint16_t e16[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
-        e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (_Float16)bf16_to_f32(e16[perm8(e)]);
-    }
-    *reinterpret_cast<half8v*>(&s_q[(row * DW + (c ^ (row & 15 & (DW - 1)))) * 8]) = h;
-  }
-  __syncthreads();
-
-  float m_run[NB], l_run[NB];
-  float4v o_acc[NB][NPB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < NPB; ++p) o_acc[nb][p] = float4v{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
-  auto process_chunk = [&](int c0, ChunkRegs<D>& cr, int lim) {
-      // ---- scales: each lane converts one, the wave reads its eight back.  A
-      //      token at or past the split end gets bias -inf (score masked), so
-      //      the score is one FMA on every chunk, full or not.
-      s_sc[wave][lane] = f16bits_to_f32(lane < 32 ? cr.sk : cr.sv) * sc_mul;
-      if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < lim) ? 0.0f : -INFINITY;
-      const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
-      const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
-      const float4v sv0 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j]);
-      const float4v sv1 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + 8 * j + 4]);
-      const float4v mb0 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j]);
-      const float4v mb1 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j + 4]);
-      const float csk[8] = {ck0[0], ck0[1], ck0[2], ck0[3], ck1[0], ck1[1], ck1[2], ck1[3]};
-      const float sv[8] = {sv0[0], sv0[1], sv0[2], sv0[3], sv1[0], sv1[1], sv1[2], sv1[3]};
-      const float mbias[8] = {mb0[0], mb0[1], mb0[2], mb0[3], mb1[0], mb1[1], mb1[2], mb1[3]};
-
-      if constexpr (D == 64) {
-        // lanes 8..15 own nibbles 4..7 of their dword: move them down
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cr.vw[e] = (r >= 8) ? (cr.vw[e] >> 16) : cr.vw[e];
-      }
-
-      // ---- scores S^T for 2 x 16 tokens and every 16-row block; each K operand
-      //      is converted once and used for all row blocks
-      float4v s_t[NB][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const half8v kop = unpack8_perm(cr.kw[kb][kk]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int qrow = nb * 16 + r;
-            const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
-            const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
-            s_t[nb][kb] = mfma16x16x32(kop, qop, s_t[nb][kb]);
-          }
-        }
-      }
-
-      // ---- online softmax per row block -> P^T operand (V scale folded in)
-      half8v pop[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float x[8];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[e] = fmaf(s_t[nb][e >> 2][e & 3], csk[e], mbias[e]);
-          mloc = fmaxf(mloc, x[e]);
-        }
-        mloc = xor_max(mloc, 16);
-        mloc = xor_max(mloc, 32);
-        const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
-        const float alpha = fast_exp2(m_run[nb] - m_new);
-        float lsum = 0.0f;
-        uint4v pw;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(x[e] - m_new);
-          const float p1 = fast_exp2(x[e + 1] - m_new);
-          lsum += p0 + p1;
-          pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
-        }
-        pop[nb] = bitcast<half8v>(pw);
-        l_run[nb] = l_run[nb] * alpha + lsum;
-        m_run[nb] = m_new;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-          for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
-        }
-      }
-
-      // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
-      //      token dwords, low and high nibble -> exact fp16 (token e = k index)
-#pragma unroll
-      for (int k = 0; k < NPB / 2; ++k) {
-        uint4v wlo, whi;
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
-          wlo[hh] = bitcast<uint32_t>(nib_lo_pair(xb));
-          whi[hh] = bitcast<uint32_t>(nib_hi_pair(xb));
-        }
-        const half8v vlo = bitcast<half8v>(wlo);
-        const half8v vhi = bitcast<half8v>(whi);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
-          o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
-        }
-      }
-  };
-
-  for (int c = wave; c < n_chunks; c += kWaves) {
-    const int c0 = t_begin + c * kChunk;
-    // Compiler-only barrier: keeps the query-operand LDS reads inside the loop
-    // instead of hoisted into (NB * D / 8) live registers per lane.
-    asm volatile("" ::: "memory");
-    if constexpr (kPrefetch) {
-      ChunkRegs<D> nxt;
-      load_chunk(c0 + kWaves * kChunk, nxt, t_main, true);
-      process_chunk(c0, cur, t_main);
-      cur = nxt;
-    } else {
-      process_chunk(c0, cur, t_main);
-      load_chunk(c0 + kWaves * kChunk, cur, t_main, true);
-    }
-  }
-
-  // ---- append mode: tail chunks [t_main, t_end).  Rows before pos come from
-  //      the cache (the load range ends at pos, so no row at or past it is
-  //      read), rows from pos on from the LDS copy of the new rows.
-  if (append) {
-    for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
-      if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
-      ChunkRegs<D> cr;
-      load_chunk(c0, cr, max(pos_b, c0), true);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
-        if (tk >= pos_b && tk < new_hi) {
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) cr.kw[kb][kk] = s_nk[(tk - pos_b) * DW + KK * j + kk];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tv = c0 + 8 * j + e;
-        if (tv >= pos_b && tv < new_hi) cr.vw[e] = s_nv[(tv - pos_b) * DW + (r % DW)];
-      }
-      const int ts = c0 + (lane & 31);
-      if (ts >= pos_b && ts < new_hi) {
-        cr.sk = s_nks[ts - pos_b];
-        cr.sv = s_nvs[ts - pos_b];
-      }
-      process_chunk(c0, cr, t_end);
-    }
-  }
-
-  // ---- merge the eight waves through LDS, one 16-row block at a time
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float l = xor_sum(l_run[nb], 16);
-    l = xor_sum(l, 32);
-    if (j == 0) {
-      s_m[wave][r] = m_run[nb];
-      s_l[wave][r] = l;
-    }
-    float* orow = s_o + (wave * rows_o + r) * OSTR;
-    if (r < rows_o) {   // rows past R are padding of the 16-row block
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (D == 128) {
-          // head dims 32j + 8i + p, p = 0..7
-          float4v lo = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
-          float4v hi = {o_acc[nb][4][i], o_acc[nb][5][i], o_acc[nb][6][i], o_acc[nb][7][i]};
-          *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i) = lo;
-          *reinterpret_cast<float4v*>(orow + 32 * j + 8 * i + 4) = hi;
-        } else {
-          // M-row m = 4j + i holds head dims 8(m%8) + 4(m/8) + p, p = 0..3
-          const int m = 4 * j + i;
-          float4v v4 = {o_acc[nb][0][i], o_acc[nb][1][i], o_acc[nb][2][i], o_acc[nb][3][i]};
-          *reinterpret_cast<float4v*>(orow + 8 * (m & 7) + 4 * (m >> 3)) = v4;
-        }
-      }
-    }
-    __syncthreads();
-    const int rows_here = min(16, R - nb * 16);
-    for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += 64 * kWaves) {
-      const int rr = idx / (D / 4);
-      const int d = 4 * (idx - rr * (D / 4));
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
-      // every wave empty: weights 0 (not reached by a split with rows)
-      const float Mz = (M == -INFINITY) ? 0.0f : M;
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-      float den = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float wt = fast_exp2(s_m[w][rr] - Mz);   // empty waves: exp2(-inf) = 0
-        acc += wt * *reinterpret_cast<const float4v*>(s_o + (w * rows_o + rr) * OSTR + d);
-        den += wt * s_l[w][rr];
-      }
-      const int row = nb * 16 + rr;
-      const int hg = row / Sq;
-      const int sq = row - hg * Sq;
-      const int64_t grow = ((int64_t)b * a.Hq + g * G + hg) * Sq + sq;
-      // nothing attended: output 0, LSE -inf
-      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-      const float lse2 = den > 0.0f ? M + log2f(den) : -INFINITY;
-      if (direct) {
-        *reinterpret_cast<float4v*>(a.out + grow * D + d) = acc * inv;
-        if (d == 0 && a.lse) a.lse[grow] = lse2 * kLn2;
-      } else {
-        // device-coherent stores (sc1): visible to every XCD without an L2 writeback
-        __builtin_amdgcn_raw_buffer_store_b128(
-            acc * inv, rpart, (uint32_t)(((grow * a.n_split + split) * D + d) * 4), 0, kCoherent);
-        if (d == 0)   // log2 units
-          __hip_atomic_store(a.part_lse + grow * a.n_split + split, lse2, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
+  } else {
+    main_body();
   }
   if (direct) return;
-
   merge_splits();
 }
 
