@@ -21,6 +21,8 @@ exact arithmetic):
 * ``attention_partial`` / ``lse_merge``: the same attention restricted to a
   key range, and the log-sum-exp merge of such partial results (the
   definition the split-K decode reaches);
+* ``lowbit``: 2- and 3-bit rows (the int4 rule widened to b bits, packing
+  of 2-bit rows and of 3-bit rows as two bit planes) and attention over them;
 * ``buffer``: the INT8 decode buffer -- universal scale from the cache's
   value range, symmetric clamped 8-bit codes, the flush to int4, and
   attention over int4 rows followed by buffered INT8 rows.
@@ -32,6 +34,8 @@ closed forms and invariants.
 from .quantize import quantize_rows, dequantize_rows, quantize_append, dequantize_cache
 from .attention import attention, attention_partial, lse_merge
 from .buffer import buffer_scale, quantize_int8, dequantize_int8, flush_rows, attention_buffered
+from .lowbit import (row_bytes, quantize_rows_bits, unpack_bits, dequantize_rows_bits, dequantize_cache_bits,
+                     attention_bits)
 
 __all__ = [
     "quantize_rows",
@@ -46,4 +50,10 @@ __all__ = [
     "dequantize_int8",
     "flush_rows",
     "attention_buffered",
+    "row_bytes",
+    "quantize_rows_bits",
+    "unpack_bits",
+    "dequantize_rows_bits",
+    "dequantize_cache_bits",
+    "attention_bits",
 ]
