@@ -155,6 +155,34 @@ qkv_status qkv_decode(const uint16_t* q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * 2- and 3-bit rows (the bit-width parameter of "Quantized Cross-Attention"
+ * §4.1; 2-bit heads in TurboAttention §3.2).  A b-bit row of D codes takes
+ * D*b/8 bytes: scale = fp16(absmax / (2^(b-1) - 1)) by IEEE fp32 division,
+ * code = clamp(rint(x / scale), -2^(b-1), 2^(b-1) - 1).  2 bits: element i
+ * in bits 2(i % 4) of byte i / 4.  3 bits: those 2-bit fields of the low two
+ * bits (D/4 bytes), then the top bit of every code, element i at bit i % 8 of
+ * byte D/4 + i / 8.  bits = 4 is the int4 format of the other calls.
+ *   qkv_quantize_append_kv_bits: qkv_quantize_append_kv for b-bit rows;
+ *     k_codes, v_codes uint8 [B, Hkv, C, D*bits/8].
+ *   qkv_decode_bits: qkv_decode over b-bit rows (same workspace as
+ *     qkv_decode: qkv_decode_workspace_bytes).
+ * Requires bits in {2, 3, 4} (QKV_ERR_UNSUPPORTED otherwise) and the
+ * requirements of the int4 calls.
+ */
+qkv_status qkv_quantize_append_kv_bits(const float* k_src, const float* v_src,
+                                       uint8_t* k_codes, uint16_t* k_scales,
+                                       uint8_t* v_codes, uint16_t* v_scales,
+                                       int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                                       int64_t C, int64_t pos, int bits, void* stream);
+qkv_status qkv_decode_bits(const uint16_t* q,
+                           const uint8_t* k_codes, const uint16_t* k_scales,
+                           const uint8_t* v_codes, const uint16_t* v_scales,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                           int64_t C, int64_t D, int bits, float softmax_scale, int num_splits,
+                           float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * (a)+(b) One decode step in one launch: append, then attend.  Quantizes
  * n_new new K and V rows into cache rows [pos, pos + n_new), exactly as
  * qkv_quantize_append_kv does, then computes qkv_decode over cache rows

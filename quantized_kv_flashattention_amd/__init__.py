@@ -92,6 +92,11 @@ def _load():
     lib.qkv_decode_buffered_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
     lib.qkv_decode_buffered.restype = ci
     lib.qkv_decode_buffered.argtypes = [vp] * 11 + [i64] * 10 + [f32, ci, vp, vp, vp, sz, vp]
+    lib.qkv_quantize_append_kv_bits.restype = ci
+    lib.qkv_quantize_append_kv_bits.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.qkv_decode_bits.restype = ci
+    lib.qkv_decode_bits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                    vp, vp, vp, sz, vp]
     lib.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                 vp, vp, vp]
     return lib
@@ -144,8 +149,9 @@ class KVCache:
     v_scales: torch.Tensor
 
     @staticmethod
-    def empty(B: int, Hkv: int, C: int, D: int, device="cuda") -> "KVCache":
-        mk = lambda: torch.empty((B, Hkv, C, D // 2), dtype=torch.uint8, device=device)
+    def empty(B: int, Hkv: int, C: int, D: int, device="cuda", bits: int = 4) -> "KVCache":
+        """Cache of ``bits``-bit rows (``D * bits / 8`` bytes of codes per row)."""
+        mk = lambda: torch.empty((B, Hkv, C, D * bits // 8), dtype=torch.uint8, device=device)
         ms = lambda: torch.empty((B, Hkv, C), dtype=torch.float16, device=device)
         return KVCache(mk(), ms(), mk(), ms())
 
@@ -173,8 +179,9 @@ def quantize_append(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor
                                     _stream(src)))
 
 
-def quantize_append_kv(k_src: torch.Tensor, v_src: torch.Tensor, cache: "KVCache", pos: int):
-    """Quantize new K and V rows ``[B, Hkv, T, D]`` into cache rows ``[pos, pos+T)`` in one launch."""
+def quantize_append_kv(k_src: torch.Tensor, v_src: torch.Tensor, cache: "KVCache", pos: int, bits: int = 4):
+    """Quantize new K and V rows ``[B, Hkv, T, D]`` into cache rows ``[pos, pos+T)`` in one launch
+    (``bits`` = 2, 3 or 4; the cache's code rows hold ``D * bits / 8`` bytes)."""
     _req(k_src, "k_src", torch.float32, 4)
     _req(v_src, "v_src", torch.float32, 4)
     if k_src.shape != v_src.shape or k_src.device != v_src.device:
@@ -186,14 +193,18 @@ def quantize_append_kv(k_src: torch.Tensor, v_src: torch.Tensor, cache: "KVCache
         if t.device != k_src.device:
             raise ValueError("all tensors must be on one device")
     B, Hkv, T, D = k_src.shape
-    if kc.shape[:2] != (B, Hkv) or kc.shape[3] * 2 != D or vc.shape != kc.shape or \
+    if kc.shape[:2] != (B, Hkv) or kc.shape[3] * 8 != D * bits or vc.shape != kc.shape or \
             ks.shape != kc.shape[:3] or vs.shape != ks.shape:
         raise ValueError("cache shape does not match src")
-    _check(_lib.qkv_quantize_append_kv(_ptr(k_src), _ptr(v_src), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
-                                       B, Hkv, T, D, kc.shape[2], int(pos), _stream(k_src)))
+    if bits == 4:
+        _check(_lib.qkv_quantize_append_kv(_ptr(k_src), _ptr(v_src), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                           B, Hkv, T, D, kc.shape[2], int(pos), _stream(k_src)))
+    else:
+        _check(_lib.qkv_quantize_append_kv_bits(_ptr(k_src), _ptr(v_src), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                                B, Hkv, T, D, kc.shape[2], int(pos), int(bits), _stream(k_src)))
 
 
-def _attn_args(q, cache_tensors, kv_len):
+def _attn_args(q, cache_tensors, kv_len, bits=4):
     _req(q, "q", torch.bfloat16, 4)
     kc, ks, vc, vs = cache_tensors
     for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
@@ -202,8 +213,8 @@ def _attn_args(q, cache_tensors, kv_len):
         if t.device != q.device:
             raise ValueError("all tensors must be on one device")
     B, Hq, Sq, D = q.shape
-    Bk, Hkv, C, half = kc.shape
-    if Bk != B or half * 2 != D or vc.shape != kc.shape or ks.shape != (B, Hkv, C) or vs.shape != ks.shape:
+    Bk, Hkv, C, rowb = kc.shape
+    if Bk != B or rowb * 8 != D * bits or vc.shape != kc.shape or ks.shape != (B, Hkv, C) or vs.shape != ks.shape:
         raise ValueError("cache shape does not match q")
     return B, Hq, Hkv, Sq, int(kv_len), C, D
 
@@ -258,19 +269,25 @@ def _workspace(device, units, nbytes):
 
 
 def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False, out=None,
-           lse=None, workspace=None):
-    """Decode attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)`` (no mask)."""
+           lse=None, workspace=None, bits=4):
+    """Decode attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)`` (no mask);
+    ``bits`` = 2, 3 or 4 is the width of the cache's codes."""
     tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
-    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len)
+    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len, bits)
     out, lse = _outputs(q, out, lse, return_lse)
     need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
     if workspace is None and need > 0:
         workspace = _workspace(q.device, B * Hkv, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     kc, ks, vc, vs = tensors
-    _check(_lib.qkv_decode(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
-                           C, D, _scale(softmax_scale, D), int(num_splits), _ptr(out), _ptr(lse),
-                           _ptr(workspace), ws_bytes, _stream(q)))
+    if bits == 4:
+        _check(_lib.qkv_decode(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                               C, D, _scale(softmax_scale, D), int(num_splits), _ptr(out), _ptr(lse),
+                               _ptr(workspace), ws_bytes, _stream(q)))
+    else:
+        _check(_lib.qkv_decode_bits(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                                    C, D, int(bits), _scale(softmax_scale, D), int(num_splits), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
     return (out, lse) if return_lse else out
 
 

@@ -159,7 +159,7 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
                          float softmax_scale, int num_splits, float* out, float* lse,
                          void* workspace, size_t workspace_bytes,
                          const qkvfa::DecodeAppend* append, const qkvfa::DecodeVarlen* varlen,
-                         void* stream, const char* fn) {
+                         void* stream, const char* fn, int bits = 4) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -184,7 +184,7 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
   return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
                                          kv_len, varlen ? varlen->page_size : C, (int)D,
                                          softmax_scale, plan, out, lse, workspace, append, varlen,
-                                         nullptr, static_cast<hipStream_t>(stream)),
+                                         nullptr, bits, static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -200,6 +200,44 @@ qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t*
   return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D,
                        softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr,
                        nullptr, stream, "qkv_decode");
+}
+
+qkv_status qkv_decode_bits(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                           const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D, int bits,
+                           float softmax_scale, int num_splits, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (bits != 2 && bits != 3 && bits != 4)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_bits: bits must be 2, 3 or 4");
+  return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D,
+                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr,
+                       nullptr, stream, "qkv_decode_bits", bits);
+}
+
+qkv_status qkv_quantize_append_kv_bits(const float* k_src, const float* v_src, uint8_t* k_codes,
+                                       uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                                       int64_t B, int64_t Hkv, int64_t T, int64_t D, int64_t C,
+                                       int64_t pos, int bits, void* stream) {
+  if (bits != 2 && bits != 3 && bits != 4)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append_kv_bits: bits must be 2, 3 or 4");
+  if (B < 1 || Hkv < 1 || T < 0 || C < 1)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv_bits: need B, Hkv, C >= 1 and T >= 0");
+  if (D != 64 && D != 128)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append_kv_bits: head dim must be 64 or 128");
+  if (pos < 0 || pos + T > C)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv_bits: need 0 <= pos and pos + T <= C");
+  if (T == 0) return QKV_OK;
+  if (!k_src || !v_src || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv_bits: null tensor pointer");
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 2) || !aligned(v_scales, 2))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_quantize_append_kv_bits: misaligned pointer");
+  if (B * Hkv > 0x3FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_quantize_append_kv_bits: B * Hkv too large");
+  return hip_status(qkvfa::launch_quantize_append_bits(k_src, k_codes, k_scales, v_src, v_codes, v_scales,
+                                                       B * Hkv, T, (int)D, C, pos, bits,
+                                                       static_cast<hipStream_t>(stream)),
+                    "qkv_quantize_append_kv_bits");
 }
 
 qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float* v_new,
@@ -378,7 +416,7 @@ qkv_status qkv_decode_buffered(const uint16_t* q, const float* k_new, const floa
   const qkvfa::DecodeTail tail = {k_buf, v_buf, k_s8, v_s8, k_new, v_new, buf_rows, buf_len, n_new};
   return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C,
                                          (int)D, softmax_scale, plan, out, lse, workspace, nullptr, nullptr,
-                                         &tail, static_cast<hipStream_t>(stream)),
+                                         &tail, 4, static_cast<hipStream_t>(stream)),
                     "qkv_decode_buffered");
 }
 

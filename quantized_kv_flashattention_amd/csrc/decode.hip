@@ -165,10 +165,17 @@ __device__ __forceinline__ void quantize_row_wave(const float* __restrict__ src,
   }
 }
 
-template <int D>
+template <int D, int BITS>
 struct ChunkRegs {
-  uint32_t kw[2][D / 32];
+  // K: the lane's D/4 elements of rows kb = 0, 1 (nibbles, or for 2/3 bits
+  // the low-bit bytes: two per 8 elements); V: the lane's 8 elements of 8
+  // rows (a dword of nibbles, or the low 16 bits); 3 bits also keep the top
+  // bits (K: one byte per 8 elements; V: one byte per row)
+  static constexpr int KW = BITS == 4 ? D / 32 : D / 64;
+  uint32_t kw[2][KW];
   uint32_t vw[8];
+  uint32_t kh[BITS == 3 ? 2 : 1];
+  uint32_t vh[BITS == 3 ? 8 : 1];
   uint16_t sk, sv;   // K and V scale of token (lane % 32) of the chunk
 };
 
@@ -176,15 +183,19 @@ struct ChunkRegs {
 // workgroup (two waves per SIMD) per CU; the one-row-block kernel still fits
 // 128 VGPRs so that concurrent launches can share a CU.  The 64-row variant
 // skips the one-chunk prefetch to stay within 256 VGPRs.
-template <int D, int NB, bool PAGED>
-__global__ __launch_bounds__(64 * waves_for(NB)) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1, 8)))
+// (3-bit rows keep a second set of top-bit registers per chunk: their one
+// row-block variant asks for three waves per SIMD instead of four.)
+template <int D, int NB, bool PAGED, int BITS>
+__global__ __launch_bounds__(64 * waves_for(NB))
+__attribute__((amdgpu_waves_per_eu(NB == 1 ? (BITS == 3 ? 3 : 4) : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
   constexpr int kWaves = waves_for(NB);
   constexpr bool kPrefetch = (NB <= 2);
   constexpr int KK = D / 32;    // QK MFMAs per 16-token block
   constexpr int DW = D / 8;     // dwords per packed row
   constexpr int NPB = D / 16;   // PV MFMAs (16 head dims each)
-  constexpr int ROWB = D / 2;   // bytes per packed row
+  constexpr int ROWB = D * BITS / 8;   // bytes per packed row
+  static_assert(BITS == 4 || !PAGED, "the paged cache holds 4-bit rows");
   constexpr int OSTR = D + 4;   // padded LDS row stride of the merge buffer (floats)
 
   __shared__ __align__(16) _Float16 s_q[NB * 16 * D];
@@ -262,8 +273,11 @@ void decode_kernel(const DecodeArgs a) {
   };
 
   // Loop-invariant per-lane byte offsets inside a chunk.
-  const uint32_t offk = (uint32_t)((8 * (r >> 2) + (r & 3)) * ROWB + 4 * KK * j);  // +4 rows for kb = 1
-  const uint32_t offv = (uint32_t)(8 * j * ROWB + 4 * (r % DW));
+  // K: the lane's D/4 elements start at byte KK j * BITS of its row (its low
+  // bits; 3 bits: top bits KK bytes from D/4 + KK j); V: its 8 elements at
+  // byte BITS (r % DW) (3 bits: low bits at 2 (r % DW), top bits at D/4 + r % DW)
+  const uint32_t offk = (uint32_t)((8 * (r >> 2) + (r & 3)) * ROWB + (BITS == 4 ? 4 : 2) * KK * j);  // +4 rows for kb = 1
+  const uint32_t offv = (uint32_t)(8 * j * ROWB + (BITS == 4 ? 4 : 2) * (r % DW));
   const uint32_t offs = (uint32_t)(2 * (lane & 31));
 
   // ---- append mode: this split's new rows [new_lo, new_hi)
@@ -414,7 +428,7 @@ void decode_kernel(const DecodeArgs a) {
     // chunk past the split can be "loaded" unconditionally (all zeros, no
     // traffic), which keeps the prefetch branch-free: a conditional prefetch
     // makes the compiler wait for every outstanding load where the paths join.
-    auto load_chunk = [&](int c0, ChunkRegs<D>& cr, int lim, bool from_lds) {
+    auto load_chunk = [&](int c0, ChunkRegs<D, BITS>& cr, int lim, bool from_lds) {
       // a chunk is 32 rows; with a paged cache it never straddles a page.  The
       // clamp is made scalar explicitly: computed in a vector register, the
       // descriptor would look divergent and each load would become a loop.
@@ -424,32 +438,56 @@ void decode_kernel(const DecodeArgs a) {
       const rsrc_t rv = make_rsrc(a.vc + row0 * ROWB, rows_left * ROWB);
       const rsrc_t rks = make_rsrc(a.ks + row0, rows_left * 2);
       const rsrc_t rvs = make_rsrc(a.vs + row0, rows_left * 2);
+      if constexpr (BITS == 4) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if constexpr (KK == 4) {
-          const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (KK == 4) {
+            const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
-        } else {
-          const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
-          cr.kw[kb][0] = w[0];
-          cr.kw[kb][1] = w[1];
+            for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
+          } else {
+            const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
+            cr.kw[kb][0] = w[0];
+            cr.kw[kb][1] = w[1];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t o = offk + kb * 4 * ROWB;
+          if constexpr (KK == 4) {
+            const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0);
+            cr.kw[kb][0] = w[0];
+            cr.kw[kb][1] = w[1];
+            // top bits: KK bytes at D/4 + KK j of the row (o sits at 2 KK j)
+            if constexpr (BITS == 3) cr.kh[kb] = __builtin_amdgcn_raw_buffer_load_b32(rk, o + D / 4 - KK * j, 0, 0);
+          } else {
+            cr.kw[kb][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o, 0, 0);
+            if constexpr (BITS == 3) cr.kh[kb] = __builtin_amdgcn_raw_buffer_load_b16(rk, o + D / 4 - KK * j, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, offv + e * ROWB, 0, 0);
+          if constexpr (BITS == 3)   // top bits: byte D/4 + r % DW of the row (offv sits at 2 (r % DW))
+            cr.vh[e] = __builtin_amdgcn_raw_buffer_load_b8(rv, offv + e * ROWB + D / 4 - (r % DW), 0, 0);
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
       cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
       cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
     };
 
     const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
-    ChunkRegs<D> cur;
+    ChunkRegs<D, BITS> cur;
     load_chunk(t_begin + wave * kChunk, cur, t_main, false);
 
     // ---- append mode: quantize the new rows (one wave per row and tensor,
     //      from the last wave down: with one row block the first half of the
     //      waves converts the query meanwhile), while the first chunk loads
-    if (append) {
+    //      (4-bit caches only)
+    if (BITS == 4 && append) {
       const int ntask = 2 * max(new_hi - new_lo, 0);
       for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
         const int t = new_lo + (task >> 1);
@@ -508,7 +546,7 @@ void decode_kernel(const DecodeArgs a) {
     }
 
     // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
-    auto process_chunk = [&](int c0, ChunkRegs<D>& cr, int lim) {
+    auto process_chunk = [&](int c0, ChunkRegs<D, BITS>& cr, int lim) {
         // ---- scales: each lane converts one, the wave reads its eight back.  A
         //      token at or past the split end gets bias -inf (score masked), so
         //      the score is one FMA on every chunk, full or not.
@@ -527,9 +565,12 @@ void decode_kernel(const DecodeArgs a) {
         const float mbias[8] = {mb0[0], mb0[1], mb0[2], mb0[3], mb1[0], mb1[1], mb1[2], mb1[3]};
 
         if constexpr (D == 64) {
-          // lanes 8..15 own nibbles 4..7 of their dword: move them down
+          // lanes 8..15 own elements 4..7 of their 8: move them down
 #pragma unroll
-          for (int e = 0; e < 8; ++e) cr.vw[e] = (r >= 8) ? (cr.vw[e] >> 16) : cr.vw[e];
+          for (int e = 0; e < 8; ++e) {
+            cr.vw[e] = (r >= 8) ? (cr.vw[e] >> (BITS == 4 ? 16 : 8)) : cr.vw[e];
+            if constexpr (BITS == 3) cr.vh[e] = (r >= 8) ? (cr.vh[e] >> 4) : cr.vh[e];
+          }
         }
 
         // ---- scores S^T for 2 x 16 tokens and every 16-row block; each K operand
@@ -541,7 +582,15 @@ void decode_kernel(const DecodeArgs a) {
           for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk) {
-            const half8v kop = unpack8_perm(cr.kw[kb][kk]);
+            half8v kop;
+            if constexpr (BITS == 4) {
+              kop = unpack8_perm(cr.kw[kb][kk]);
+            } else {
+              // chunk kk: low bits in bytes 2 (kk % 2), +1 of dword kk / 2; top bits in byte kk
+              const uint32_t lo16 = cr.kw[kb][kk >> 1] >> (16 * (kk & 1));
+              const uint32_t top8 = BITS == 3 ? (cr.kh[kb] >> (8 * kk)) & 0xFFu : 0u;
+              kop = unpack8_lowbit<BITS>(lo16, top8);
+            }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
               const int qrow = nb * 16 + r;
@@ -585,23 +634,49 @@ void decode_kernel(const DecodeArgs a) {
           }
         }
 
-        // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
-        //      token dwords, low and high nibble -> exact fp16 (token e = k index)
+        if constexpr (BITS == 4) {
+          // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
+          //      token dwords, low and high nibble -> exact fp16 (token e = k index)
 #pragma unroll
-        for (int k = 0; k < NPB / 2; ++k) {
-          uint4v wlo, whi;
+          for (int k = 0; k < NPB / 2; ++k) {
+            uint4v wlo, whi;
 #pragma unroll
-          for (int hh = 0; hh < 4; ++hh) {
-            const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
-            wlo[hh] = bitcast<uint32_t>(nib_lo_pair(xb));
-            whi[hh] = bitcast<uint32_t>(nib_hi_pair(xb));
+            for (int hh = 0; hh < 4; ++hh) {
+              const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
+              wlo[hh] = bitcast<uint32_t>(nib_lo_pair(xb));
+              whi[hh] = bitcast<uint32_t>(nib_hi_pair(xb));
+            }
+            const half8v vlo = bitcast<half8v>(wlo);
+            const half8v vhi = bitcast<half8v>(whi);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
+              o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
+            }
           }
-          const half8v vlo = bitcast<half8v>(wlo);
-          const half8v vhi = bitcast<half8v>(whi);
+        } else {
+          // ---- O^T += V^T P^T for 2/3-bit rows.  V operand of block 4 k2 + f: the
+          //      2-bit field f of byte k2 of the eight tokens' low bits (3 bits:
+          //      with top bit 4 k2 + f of their top-bit bytes)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
-            o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
+          for (int k2 = 0; k2 < NPB / 4; ++k2) {
+            uint32_t xb[4], zb[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+              xb[hh] = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k2);
+              zb[hh] = BITS == 3 ? pair_bytes(cr.vh[2 * hh], cr.vh[2 * hh + 1], 0) >> (4 * k2) : 0u;
+            }
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+              uint4v w;
+#pragma unroll
+              for (int hh = 0; hh < 4; ++hh)
+                w[hh] = bitcast<uint32_t>(BITS == 2 ? b2_pair(xb[hh], f) : b3_pair(xb[hh], zb[hh], f));
+              const half8v vop = bitcast<half8v>(w);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                o_acc[nb][4 * k2 + f] = mfma16x16x32(vop, pop[nb], o_acc[nb][4 * k2 + f]);
+            }
           }
         }
     };
@@ -612,7 +687,7 @@ void decode_kernel(const DecodeArgs a) {
       // instead of hoisted into (NB * D / 8) live registers per lane.
       asm volatile("" ::: "memory");
       if constexpr (kPrefetch) {
-        ChunkRegs<D> nxt;
+        ChunkRegs<D, BITS> nxt;
         load_chunk(c0 + kWaves * kChunk, nxt, t_main, true);
         process_chunk(c0, cur, t_main);
         cur = nxt;
@@ -625,10 +700,10 @@ void decode_kernel(const DecodeArgs a) {
     // ---- append mode: tail chunks [t_main, t_end).  Rows before pos come from
     //      the cache (the load range ends at pos, so no row at or past it is
     //      read), rows from pos on from the LDS copy of the new rows.
-    if (append) {
+    if constexpr (BITS == 4) if (append) {
       for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
         if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
-        ChunkRegs<D> cr;
+        ChunkRegs<D, BITS> cr;
         load_chunk(c0, cr, max(pos_b, c0), true);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -842,34 +917,36 @@ void decode_kernel(const DecodeArgs a) {
   merge_splits();
 }
 
-template <int D, int NB, bool PAGED>
-hipError_t launch_paged(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
+template <int D, int NB, bool PAGED, int BITS>
+hipError_t launch_kernel(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
   // this kernel the larger dynamic LDS once
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED>),
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
   if (attr != hipSuccess) return attr;
-  decode_kernel<D, NB, PAGED><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  decode_kernel<D, NB, PAGED, BITS><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
   return hipGetLastError();
 }
 
 template <int D, int NB>
-hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
+hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, int bits, hipStream_t stream) {
   dim3 grid((uint32_t)n_split * (uint32_t)Hkv * (uint32_t)B);
   const int R = args.G * args.Sq;
   size_t lds = merge_lds_bytes(D, waves_for(NB), R, n_split);
   if (args.tail_rows > 0 && lds < tail_lds_bytes(D, R)) lds = tail_lds_bytes(D, R);
-  if (args.block_table != nullptr) return launch_paged<D, NB, true>(args, grid, lds, stream);
-  return launch_paged<D, NB, false>(args, grid, lds, stream);
+  if (bits == 2) return launch_kernel<D, NB, false, 2>(args, grid, lds, stream);
+  if (bits == 3) return launch_kernel<D, NB, false, 3>(args, grid, lds, stream);
+  if (args.block_table != nullptr) return launch_kernel<D, NB, true, 4>(args, grid, lds, stream);
+  return launch_kernel<D, NB, false, 4>(args, grid, lds, stream);
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs& args, int B, int Hkv, int n_split, hipStream_t stream) {
+hipError_t launch_d(const DecodeArgs& args, int B, int Hkv, int n_split, int bits, hipStream_t stream) {
   const int R = args.G * args.Sq;
-  if (R <= 16) return launch_nb<D, 1>(args, B, Hkv, n_split, stream);
-  if (R <= 32) return launch_nb<D, 2>(args, B, Hkv, n_split, stream);
-  return launch_nb<D, 4>(args, B, Hkv, n_split, stream);
+  if (R <= 16) return launch_nb<D, 1>(args, B, Hkv, n_split, bits, stream);
+  if (R <= 32) return launch_nb<D, 2>(args, B, Hkv, n_split, bits, stream);
+  return launch_nb<D, 4>(args, B, Hkv, n_split, bits, stream);
 }
 
 }  // namespace
@@ -935,7 +1012,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         const DecodeTail* tail, hipStream_t stream) {
+                         const DecodeTail* tail, int bits, hipStream_t stream) {
   DecodeArgs a;
   a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.out = out; a.lse = lse;
@@ -987,8 +1064,8 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
   a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv); a.Sq = (int)Sq; a.kv_len = (int)kv_len;
   a.split_len = plan.split_len; a.n_split = plan.n_split;
   a.qk_log2 = softmax_scale * kLog2e;
-  if (D == 128) return launch_d<128>(a, (int)B, (int)Hkv, plan.n_split, stream);
-  return launch_d<64>(a, (int)B, (int)Hkv, plan.n_split, stream);
+  if (D == 128) return launch_d<128>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);
+  return launch_d<64>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);
 }
 
 }  // namespace qkvfa

@@ -80,6 +80,63 @@ __device__ __forceinline__ half2v nib_pair2(uint32_t a, uint32_t b, int nib) {
   return (nib & 1) ? nib_hi_pair(x) : nib_lo_pair(x);
 }
 
+// 2- and 3-bit codes.  A 2-bit row packs element i into bits 2(i % 4) of
+// byte i / 4; a 3-bit row is that 2-bit row of the low bits followed by one
+// bit per element (element i at bit i % 8 of byte i / 8) holding the top
+// (sign) bit.  The same magic-number conversion as for nibbles works for a
+// 2-bit field f (bits 2f, 2f+1) with an fp16 whose mantissa unit puts weight
+// 1 on bit 2f: 1024, 256, 64, 16 for f = 0..3.
+__host__ __device__ constexpr uint32_t field_magic(int f) {
+  return f == 0 ? 0x6400u : f == 1 ? 0x5C00u : f == 2 ? 0x5400u : 0x4C00u;
+}
+__host__ __device__ constexpr float field_base(int f) {
+  return f == 0 ? 1024.0f : f == 1 ? 256.0f : f == 2 ? 64.0f : 16.0f;
+}
+
+// 2-bit field f of the bytes in bits 0-7 and 16-23 of x -> exact fp16 pair
+// (two's complement codes -2..1; the sign flip makes them offset binary).
+__device__ __forceinline__ half2v b2_pair(uint32_t x, int f) {
+  const uint32_t m = field_magic(f);
+  const uint32_t y = ((x ^ (0x00020002u << (2 * f))) & (0x00030003u << (2 * f))) | (m | (m << 16));
+  const _Float16 bias = (_Float16)(field_base(f) + 2.0f);
+  return bitcast<half2v>(y) - half2v{bias, bias};
+}
+
+// 3-bit code from the 2-bit field f of x (bytes in bits 0-7 and 16-23) and
+// the top bits in bit f and bit 16 + f of z -> exact fp16 pair (codes -4..3).
+// Offset binary n = c + 4 has the inverted top bit at field bit 2f + 2.
+__device__ __forceinline__ half2v b3_pair(uint32_t x, uint32_t z, int f) {
+  const uint32_t m = field_magic(f);
+  const uint32_t lo = (x & (0x00030003u << (2 * f))) | (m | (m << 16));
+  const uint32_t y = lo | ((~z << (f + 2)) & (0x00040004u << (2 * f)));
+  const _Float16 bias = (_Float16)(field_base(f) + 4.0f);
+  return bitcast<half2v>(y) - half2v{bias, bias};
+}
+
+// Bytes k and k + 1 of w into bits 0-7 and 16-23 (other bits zero).
+__device__ __forceinline__ uint32_t spread_bytes(uint32_t w, int k) {
+  const uint32_t sel = (uint32_t)k | (12u << 8) | ((uint32_t)(k + 1) << 16) | (12u << 24);
+  return __builtin_amdgcn_perm(w, w, sel);
+}
+
+// Eight 2- or 3-bit codes -> 8 exact fp16 values in the unpack8_perm order
+// [c0, c4, c1, c5, c2, c6, c3, c7].  lo16: the two bytes of their low bits
+// (elements 0-3, 4-7); top8 (3-bit only): their top bits, element i at bit i.
+template <int BITS>
+__device__ __forceinline__ half8v unpack8_lowbit(uint32_t lo16, uint32_t top8) {
+  const uint32_t x = spread_bytes(lo16, 0);
+  uint4v w;
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) w[f] = bitcast<uint32_t>(b2_pair(x, f));
+  } else {
+    const uint32_t z = top8 | (top8 << 12);   // bits of elements f and 4 + f at f and 16 + f
+#pragma unroll
+    for (int f = 0; f < 4; ++f) w[f] = bitcast<uint32_t>(b3_pair(x, z, f));
+  }
+  return bitcast<half8v>(w);
+}
+
 // Raw buffer descriptor over [base, base + num_bytes): loads at offsets past
 // num_bytes return zero instead of touching memory (gfx9-family raw buffer
 // range check; the fourth descriptor word selects 32-bit data format).

@@ -66,7 +66,14 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         const DecodeTail* tail, hipStream_t stream);
+                         const DecodeTail* tail, int bits, hipStream_t stream);
+
+// Quantize-append of K and V rows at 2, 3 or 4 bits (4: launch_quantize_append's
+// arithmetic and layout).
+hipError_t launch_quantize_append_bits(const float* src, uint8_t* codes, uint16_t* scales,
+                                       const float* src2, uint8_t* codes2, uint16_t* scales2,
+                                       int64_t BH, int64_t T, int D, int64_t C, int64_t pos, int bits,
+                                       hipStream_t stream);
 
 hipError_t launch_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales, float* k_s8, float* v_s8,
                                int64_t BH, int64_t L, int64_t C, hipStream_t stream);

@@ -77,6 +77,87 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantTarget t0, Qu
   quantize_row_part<D>(x, sub, codes + row * (D / 2), scales + row);
 }
 
+// 2- and 3-bit rows (the int4 rule widened: scale = fp16(max|x| / (2^(b-1) - 1)),
+// codes clamp(rint(x / scale), -2^(b-1), 2^(b-1) - 1) by IEEE fp32 division).
+// A lane's 8 consecutive elements become 16 low bits (element i at bit 2i) at
+// byte 2 sub of the row, and for 3 bits one byte of top bits at D/4 + sub.
+template <int D, int BITS>
+__device__ __forceinline__ void quantize_row_part_lowbit(const float (&x)[8], int sub, uint8_t* codes_row,
+                                                         uint16_t* scale_ptr) {
+  constexpr int TPR = D / 8;
+  constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+  constexpr float qmin = -(float)(1 << (BITS - 1));
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, TPR));
+  const _Float16 s16 = (_Float16)(m / qmax);
+  const float s = (float)s16;
+  uint32_t lo = 0, top = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (uint32_t)(int)fminf(fmaxf(rintf(x[i] / s), qmin), qmax);
+      lo |= (c & 3u) << (2 * i);
+      top |= ((c >> 2) & 1u) << i;
+    }
+  }
+  reinterpret_cast<uint16_t*>(codes_row)[sub] = (uint16_t)lo;
+  if constexpr (BITS == 3) codes_row[D / 4 + sub] = (uint8_t)top;
+  if (sub == 0) *scale_ptr = bitcast<uint16_t>(s16);
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void quantize_append_lowbit_kernel(QuantTarget t0, QuantTarget t1,
+                                                                     uint32_t nblk, int64_t T, int64_t C,
+                                                                     int64_t pos, uint32_t tblocks) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  constexpr int ROWB = D * BITS / 8;
+  const bool second = blockIdx.x >= nblk;
+  const uint32_t blk = second ? blockIdx.x - nblk : blockIdx.x;
+  const QuantTarget& tg = second ? t1 : t0;
+  const uint32_t bh = blk / tblocks;
+  const uint32_t tb = blk - bh * tblocks;
+  const int sub = threadIdx.x % TPR;
+  const int64_t t = (int64_t)tb * RPB + threadIdx.x / TPR;
+  if (t >= T) return;  // whole TPR-lane groups leave together
+  const float4* p = reinterpret_cast<const float4*>(tg.src + ((int64_t)bh * T + t) * D) + 2 * sub;
+  const float4 a = p[0];
+  const float4 b = p[1];
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int64_t row = (int64_t)bh * C + pos + t;
+  quantize_row_part_lowbit<D, BITS>(x, sub, tg.codes + row * ROWB, tg.scales + row);
+}
+
+hipError_t launch_quantize_append_bits(const float* src, uint8_t* codes, uint16_t* scales,
+                                       const float* src2, uint8_t* codes2, uint16_t* scales2,
+                                       int64_t BH, int64_t T, int D, int64_t C, int64_t pos, int bits,
+                                       hipStream_t stream) {
+  if (bits == 4)
+    return launch_quantize_append(src, codes, scales, src2, codes2, scales2, BH, T, D, C, pos, stream);
+  if (T == 0) return hipSuccess;
+  const int rpb = 256 / (D / 8);
+  const int64_t tblocks = (T + rpb - 1) / rpb;
+  const int64_t nblk = BH * tblocks;
+  const int ntensors = src2 ? 2 : 1;
+  if (nblk * ntensors > 0x7FFFFFFF || tblocks > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  const QuantTarget t0 = {src, codes, scales};
+  const QuantTarget t1 = src2 ? QuantTarget{src2, codes2, scales2} : t0;
+  const dim3 grid((uint32_t)(nblk * ntensors));
+  const uint32_t nb = (uint32_t)nblk, tbk = (uint32_t)tblocks;
+  if (D == 128 && bits == 2)
+    quantize_append_lowbit_kernel<128, 2><<<grid, dim3(256), 0, stream>>>(t0, t1, nb, T, C, pos, tbk);
+  else if (D == 128)
+    quantize_append_lowbit_kernel<128, 3><<<grid, dim3(256), 0, stream>>>(t0, t1, nb, T, C, pos, tbk);
+  else if (bits == 2)
+    quantize_append_lowbit_kernel<64, 2><<<grid, dim3(256), 0, stream>>>(t0, t1, nb, T, C, pos, tbk);
+  else
+    quantize_append_lowbit_kernel<64, 3><<<grid, dim3(256), 0, stream>>>(t0, t1, nb, T, C, pos, tbk);
+  return hipGetLastError();
+}
+
 // Flush of the INT8 decode buffer (TurboAttention §3.3: a full buffer is
 // compressed to the low-bit cache format): buffered rows [0, T) of every
 // (batch, KV head), dequantized as the fp32 product s8 * code, are quantized
@@ -140,28 +221,42 @@ hipError_t launch_buffer_flush(const int8_t* k_buf, const int8_t* v_buf, const f
 // previous cache's value-range maximum; newer values beyond it are clamped):
 // s8 = (7 * max_t s4[t]) / 127 over cache rows [0, L) of every (batch, KV
 // head), with 7 * s4 (an fp16 value times 7, exact in fp32) the row's absmax
-// as its int4 scale records it.  One wave per (batch, KV head) and tensor.
+// as its int4 scale records it.  One 256-thread workgroup per (batch, KV
+// head) and tensor, four independent loads in flight per thread.
 __global__ __launch_bounds__(256) void buffer_scale_kernel(const uint16_t* k_scales, const uint16_t* v_scales,
                                                            float* k_s8, float* v_s8, int64_t BH, int64_t L,
                                                            int64_t C) {
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (w >= 2 * BH) return;   // whole waves leave together
+  __shared__ float s_m[4];
+  const int64_t w = blockIdx.x;          // [0, BH): K, [BH, 2 BH): V
   const bool isv = w >= BH;
   const int64_t bh = isv ? w - BH : w;
   const uint16_t* sc = (isv ? v_scales : k_scales) + bh * C;
   float m = 0.0f;   // scales are non-negative
-  for (int64_t t = lane; t < L; t += 64) m = fmaxf(m, (float)bitcast<_Float16>(sc[t]));
+  for (int64_t t0 = threadIdx.x; t0 < L; t0 += 4 * 256) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t t = t0 + u * 256;
+      v[u] = t < L ? (float)bitcast<_Float16>(sc[t]) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = fmaxf(m, v[u]);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if (lane == 0) (isv ? v_s8 : k_s8)[bh] = (m * 7.0f) / 127.0f;
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    (isv ? v_s8 : k_s8)[bh] = (m * 7.0f) / 127.0f;
+  }
 }
 
 hipError_t launch_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales, float* k_s8, float* v_s8,
                                int64_t BH, int64_t L, int64_t C, hipStream_t stream) {
-  const int64_t nblk = (2 * BH + 3) / 4;
-  if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-  buffer_scale_kernel<<<dim3((uint32_t)nblk), dim3(256), 0, stream>>>(k_scales, v_scales, k_s8, v_s8, BH, L, C);
+  if (2 * BH > 0x7FFFFFFF) return hipErrorInvalidValue;
+  buffer_scale_kernel<<<dim3((uint32_t)(2 * BH)), dim3(256), 0, stream>>>(k_scales, v_scales, k_s8, v_s8, BH, L,
+                                                                           C);
   return hipGetLastError();
 }
 

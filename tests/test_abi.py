@@ -262,3 +262,24 @@ def test_decode_buffered_workspace_size(lib):
     # one cache split + the buffer split
     n = lib.qkv_decode_buffered_workspace_bytes(1, 4, 2, 1, 100, 128, 1)
     assert n >= 4 * 2 * 128 * 4
+
+
+def test_lowbit_argument_errors(lib):
+    i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    lib.qkv_quantize_append_kv_bits.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.qkv_decode_bits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                    vp, vp, vp, sz, vp]
+    qb = lambda **kw: lib.qkv_quantize_append_kv_bits(P, P, P, P, P, P, 1, 1, kw.get("T", 4), kw.get("D", 64), 8,
+                                                      kw.get("pos", 0), kw.get("bits", 2), None)
+    assert qb(bits=5) == 2
+    assert qb(bits=1) == 2
+    assert qb(D=96) == 2
+    assert qb(pos=5) == 1
+    assert qb(T=0) == 0
+    db = lambda **kw: lib.qkv_decode_bits(P, P, P, P, P, 1, 4, 2, 1, kw.get("L", 100), 128, kw.get("D", 128),
+                                          kw.get("bits", 3), 0.1, kw.get("ns", 0), P, None, None, 0, None)
+    assert db(bits=8) == 2
+    assert db(D=80) == 2
+    assert db(L=129) == 1
+    assert db(ns=2) == 3
+    assert b"qkv_decode_bits" in lib.qkv_last_error()
