@@ -18,7 +18,7 @@ in the timed region -- one launch per step -- measured with HIP events on the
 launch stream), the CPU oracle timed on a
 bounded sample of the same workload, and secondary figures (128K-token
 decode, a ragged 64-sequence batch over a paged cache, the decode step with
-the INT8 buffer, 16K causal prefill
+the INT8 buffer, decode over 2- and 3-bit caches, 16K causal prefill
 TFLOP/s, ViT-B prefill, bulk quantize-append).
 Everything else goes to stderr.
 
@@ -356,6 +356,42 @@ def bench_buffered(torch, qkv, w, steps, buf_len=31):
     return res
 
 
+def bench_lowbit(torch, qkv, w, steps):
+    """Decode over 2-, 3- and 4-bit caches of the same workload (decode only,
+    timed region of back-to-back launches, caches rotated past the MALL)."""
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w)
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D), 1), dtype=torch.uint8,
+                     device="cuda")
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    del k, v
+    res = {"workload": w.name, "n_split": qkv.decode_auto_splits(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D)}
+    for bits in (4, 3, 2):
+        kv_bytes = 2 * w.B * w.Hkv * w.L * (w.D * bits // 8 + 2)
+        n_copies = max(4, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+        c0 = qkv.KVCache.empty(w.B, w.Hkv, w.L, w.D, bits=bits)
+        qkv.quantize_append_kv(kt, vt, c0, 0, bits=bits)
+        caches = [c0] + [qkv.KVCache(*(t.clone() for t in c0.tensors())) for _ in range(n_copies - 1)]
+
+        def run(i):
+            qkv.decode(q, caches[i], w.L, softmax_scale=w.softmax_scale, out=out, workspace=ws, bits=bits)
+
+        for i in range(5):
+            run(i % n_copies)
+        torch.cuda.synchronize()
+        ms = region_ms(torch, run, steps, n_copies)
+        alg = kv_bytes + w.B * w.Hq * w.Sq * w.D * 6
+        res[f"{bits}bit"] = {"ms": ms, "kv_bytes": kv_bytes, "GBps": alg / (ms * 1e-3) / 1e9,
+                             "frac_hbm": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del caches, c0
+        torch.cuda.empty_cache()
+    for bits in (3, 2):
+        res[f"{bits}bit"]["speedup_vs_4bit"] = res["4bit"]["ms"] / res[f"{bits}bit"]["ms"]
+    return res
+
+
 def bench_prefill(torch, qkv, w, iters):
     from qkv_inputs import make_qkv
     q_bits, k, v = make_qkv(w)
@@ -583,6 +619,8 @@ def main():
         log("paged:", json.dumps(secondary["ragged_paged_decode"]))
         secondary["int8_buffer_decode"] = bench_buffered(torch, qkv, w3, max(args.steps, 20))
         log("buffered:", json.dumps(secondary["int8_buffer_decode"]))
+        secondary["lowbit_decode"] = bench_lowbit(torch, qkv, w3, max(args.steps, 20))
+        log("lowbit:", json.dumps(secondary["lowbit_decode"]))
     if args.only in ("all", "prefill"):
         secondary["causal_prefill_16k"] = bench_prefill(torch, qkv, workload("causal_prefill_16k"), 10)
         log("prefill:", json.dumps(secondary["causal_prefill_16k"]))
