@@ -195,6 +195,9 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int DW = D / 8;     // dwords per packed row
   constexpr int NPB = D / 16;   // PV MFMAs (16 head dims each)
   constexpr int ROWB = D * BITS / 8;   // bytes per packed row
+  // bias of element e (0..7) of a K operand and of the codes of PV block p
+  auto kbias = [](int e) { return BITS == 4 ? kNibBias : lowbit_bias<BITS>(e >> 1); };
+  auto vbias = [](int p) { return BITS == 4 ? kNibBias : lowbit_bias<BITS>(p & 3); };
   static_assert(BITS == 4 || !PAGED, "the paged cache holds 4-bit rows");
   constexpr int OSTR = D + 4;   // padded LDS row stride of the merge buffer (floats)
 
@@ -535,14 +538,32 @@ void decode_kernel(const DecodeArgs a) {
     }
     __syncthreads();
 
-    float m_run[NB], l_run[NB];
+    // Codes enter the MFMAs as exact fp16 values c + b (the bias b depends on
+    // the code's position only).  Scores: each QK accumulator starts at
+    // -sum_d q_d b_d of its query row, so it ends at the plain dot product.
+    // Outputs: s_run sums the fp16 P~ values the PV MFMAs consumed (rescaled
+    // like O), and the wave merge takes b x s_run out of each output.
+    float m_run[NB], l_run[NB], s_run[NB], kinit[NB];
     float4v o_acc[NB][NPB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m_run[nb] = -INFINITY;
       l_run[nb] = 0.0f;
+      s_run[nb] = 0.0f;
 #pragma unroll
       for (int p = 0; p < NPB; ++p) o_acc[nb][p] = float4v{0.f, 0.f, 0.f, 0.f};
+      const int qrow = nb * 16 + r;
+      float qb = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
+        const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb = fmaf((float)qop[e], kbias(e), qb);
+      }
+      qb = xor_sum(qb, 16);
+      qb = xor_sum(qb, 32);
+      kinit[nb] = -qb;
     }
 
     // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
@@ -579,17 +600,17 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{0.f, 0.f, 0.f, 0.f};
+          for (int nb = 0; nb < NB; ++nb) s_t[nb][kb] = float4v{kinit[nb], kinit[nb], kinit[nb], kinit[nb]};
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk) {
             half8v kop;
             if constexpr (BITS == 4) {
-              kop = unpack8_perm(cr.kw[kb][kk]);
+              kop = unpack8_perm_b(cr.kw[kb][kk]);
             } else {
               // chunk kk: low bits in bytes 2 (kk % 2), +1 of dword kk / 2; top bits in byte kk
               const uint32_t lo16 = cr.kw[kb][kk >> 1] >> (16 * (kk & 1));
               const uint32_t top8 = BITS == 3 ? (cr.kh[kb] >> (8 * kk)) & 0xFFu : 0u;
-              kop = unpack8_lowbit<BITS>(lo16, top8);
+              kop = unpack8_lowbit_b<BITS>(lo16, top8);
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -626,6 +647,10 @@ void decode_kernel(const DecodeArgs a) {
             pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
           }
           pop[nb] = bitcast<half8v>(pw);
+          float ps = s_run[nb] * alpha;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) ps = __builtin_amdgcn_fdot2(bitcast<half2v>(pw[h]), half2v{1, 1}, ps, false);
+          s_run[nb] = ps;
           l_run[nb] = l_run[nb] * alpha + lsum;
           m_run[nb] = m_new;
           if (__ballot(alpha != 1.0f)) {
@@ -643,8 +668,8 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh) {
               const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
-              wlo[hh] = bitcast<uint32_t>(nib_lo_pair(xb));
-              whi[hh] = bitcast<uint32_t>(nib_hi_pair(xb));
+              wlo[hh] = nib_b72(xb << 4);
+              whi[hh] = nib_b72(xb);
             }
             const half8v vlo = bitcast<half8v>(wlo);
             const half8v vhi = bitcast<half8v>(whi);
@@ -660,18 +685,16 @@ void decode_kernel(const DecodeArgs a) {
           //      with top bit 4 k2 + f of their top-bit bytes)
 #pragma unroll
           for (int k2 = 0; k2 < NPB / 4; ++k2) {
-            uint32_t xb[4], zb[4];
+            uint4v pr[4];   // pr[hh][f]: field f of tokens 2 hh, 2 hh + 1 (c + lowbit_bias(f))
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh) {
-              xb[hh] = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k2);
-              zb[hh] = BITS == 3 ? pair_bytes(cr.vh[2 * hh], cr.vh[2 * hh + 1], 0) >> (4 * k2) : 0u;
+              const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k2);
+              const uint32_t zb = BITS == 3 ? pair_bytes(cr.vh[2 * hh], cr.vh[2 * hh + 1], 0) >> (4 * k2) : 0u;
+              pr[hh] = lowbit4_b<BITS>(xb, zb);
             }
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-              uint4v w;
-#pragma unroll
-              for (int hh = 0; hh < 4; ++hh)
-                w[hh] = bitcast<uint32_t>(BITS == 2 ? b2_pair(xb[hh], f) : b3_pair(xb[hh], zb[hh], f));
+              const uint4v w = {pr[0][f], pr[1][f], pr[2][f], pr[3][f]};
               const half8v vop = bitcast<half8v>(w);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb)
@@ -732,6 +755,10 @@ void decode_kernel(const DecodeArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       float l = xor_sum(l_run[nb], 16);
       l = xor_sum(l, 32);
+      float sp = xor_sum(s_run[nb], 16);
+      sp = xor_sum(sp, 32);
+#pragma unroll
+      for (int p = 0; p < NPB; ++p) o_acc[nb][p] -= vbias(p) * sp;
       if (j == 0) {
         s_m[wave][r] = m_run[nb];
         s_l[wave][r] = l;

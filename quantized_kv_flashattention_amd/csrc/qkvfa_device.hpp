@@ -137,6 +137,86 @@ __device__ __forceinline__ half8v unpack8_lowbit(uint32_t lo16, uint32_t top8) {
   return bitcast<half8v>(w);
 }
 
+// ---- Biased conversions (decode).  A code c becomes the exact fp16 value
+// c + b, with a bias b fixed by the code's position in the operand; the
+// kernel takes sum(q b) out of each score (through the accumulator's initial
+// value) and b sum(P~) out of each output (once per wave), instead of
+// subtracting b from every value: one VALU op per two codes fewer.  The
+// biases stay below 80, so the fp32 sums they ride on lose nothing that
+// matters.  An fp16 with the exponent of 64 (0x5400) has mantissa unit 1/16,
+// so bits 4-7 of a half hold an integer of weight 1; with the exponent of 16
+// (0x4C00) the unit is 1/64 and bits 6-9 do.
+
+// Nibbles in bits 4-7 and 20-23 of x (two's complement) -> fp16 pair c + 72.
+constexpr float kNibBias = 72.0f;
+__device__ __forceinline__ uint32_t nib_b72(uint32_t x) {
+  return ((x ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
+}
+
+// Eight nibbles of a dword (element i in bits 4i..4i+3) -> c + 72 in the
+// unpack8_perm order [c0, c4, c1, c5, c2, c6, c3, c7].
+__device__ __forceinline__ half8v unpack8_perm_b(uint32_t x) {
+  uint4v w;
+  w[0] = nib_b72(x << 4);   // c0, c4
+  w[1] = nib_b72(x);        // c1, c5
+  w[2] = nib_b72(x >> 4);   // c2, c6
+  w[3] = nib_b72(x >> 8);   // c3, c7
+  return bitcast<half8v>(w);
+}
+
+// 2-bit field in bits 4-5 (and 20-21) -> c + 66; in bits 6-7 (22-23) -> c + 18.
+__device__ __forceinline__ uint32_t b2_at4(uint32_t x) {
+  return ((x ^ 0x00200020u) & 0x00300030u) | 0x54005400u;
+}
+__device__ __forceinline__ uint32_t b2_at6(uint32_t x) {
+  return ((x ^ 0x00800080u) & 0x00C000C0u) | 0x4C004C00u;
+}
+// 3-bit code: its low two bits in bits 4-5 of x and its top bit at bit 6 of
+// zs (both halves alike) -> c + 68; low bits in 6-7, top bit at 8 -> c + 20.
+// The top bit enters inverted (offset binary c + 4 = low + 4 (1 - top)).
+__device__ __forceinline__ uint32_t b3_at4(uint32_t x, uint32_t zs) {
+  return ((x & 0x00300030u) | 0x54005400u) | (~zs & 0x00400040u);
+}
+__device__ __forceinline__ uint32_t b3_at6(uint32_t x, uint32_t zs) {
+  return ((x & 0x00C000C0u) | 0x4C004C00u) | (~zs & 0x01000100u);
+}
+
+// Bias of pair f (0..3) of a low-bit operand built by lowbit4_b.
+template <int BITS>
+__host__ __device__ constexpr float lowbit_bias(int f) {
+  return BITS == 2 ? ((f & 1) ? 18.0f : 66.0f) : ((f & 1) ? 20.0f : 68.0f);
+}
+
+// Four pairs of 2- or 3-bit codes: the 2-bit fields f = 0..3 of the bytes in
+// bits 0-7 and 16-23 of x (3 bits: their top bits at bits f and 16 + f of z)
+// -> w[f] = fp16 pair c + lowbit_bias(f).
+template <int BITS>
+__device__ __forceinline__ uint4v lowbit4_b(uint32_t x, uint32_t z) {
+  const uint32_t xs = x << 4;   // fields 0, 1 move to bits 4-5, 6-7
+  uint4v w;
+  if constexpr (BITS == 2) {
+    w[0] = b2_at4(xs);
+    w[1] = b2_at6(xs);
+    w[2] = b2_at4(x);
+    w[3] = b2_at6(x);
+  } else {
+    w[0] = b3_at4(xs, z << 6);
+    w[1] = b3_at6(xs, z << 7);
+    w[2] = b3_at4(x, z << 4);
+    w[3] = b3_at6(x, z << 5);
+  }
+  return w;
+}
+
+// Eight 2- or 3-bit codes -> c + bias in the unpack8_perm order.  lo16: the
+// two bytes of their low bits (elements 0-3, 4-7); top8 (3 bits only): their
+// top bits, element i at bit i.
+template <int BITS>
+__device__ __forceinline__ half8v unpack8_lowbit_b(uint32_t lo16, uint32_t top8) {
+  const uint32_t z = BITS == 3 ? (top8 | (top8 << 12)) : 0u;   // elements f, 4 + f at bits f, 16 + f
+  return bitcast<half8v>(lowbit4_b<BITS>(spread_bytes(lo16, 0), z));
+}
+
 // Raw buffer descriptor over [base, base + num_bytes): loads at offsets past
 // num_bytes return zero instead of touching memory (gfx9-family raw buffer
 // range check; the fourth descriptor word selects 32-bit data format).

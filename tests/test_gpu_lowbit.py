@@ -1,8 +1,8 @@
 """GPU parity of 2- and 3-bit rows: quantize-append byte for byte against the
 oracle quantizer, decode against the fp64 oracle, and decode of b-bit rows
-bit-identical to the int4 decode of the same codes (a 2- or 3-bit code is an
-int4 code under the same scale, and the kernels feed the matrix units the
-same fp16 values in the same order)."""
+against the int4 decode of the same codes (a 2- or 3-bit code is an int4 code
+under the same scale): equal up to fp32 rounding, since each width feeds the
+matrix units its codes plus a width-specific bias that fp32 sums remove)."""
 import numpy as np
 import pytest
 import torch
@@ -94,8 +94,10 @@ def test_decode_bits_matches_oracle_and_int4(case, bits):
     o4, l4 = qkv.decode(q_to_dev(q), _to_dev((_as_int4(kc, D, bits), ks, _as_int4(vc, D, bits), vs)), L,
                         softmax_scale=scale, num_splits=ns, return_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, o4), f"differs from the int4 decode: {float((out - o4).abs().max())}"
-    assert torch.equal(lse, l4)
+    # the same codes through the int4 kernel: equal up to fp32 rounding (the
+    # widths convert codes with different biases, removed in fp32 sums)
+    assert float((out - o4).abs().max()) <= 1e-3, f"differs from the int4 decode: {float((out - o4).abs().max())}"
+    assert float((lse - l4).abs().max()) <= 1e-3
     ro, rl = oracle.attention_bits(q, kc, ks, vc, vs, L, scale, bits)
     assert_close(out, ro, f"bits={bits} {case}")
     assert compare(lse, rl)[0] < 1e-3
