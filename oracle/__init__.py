@@ -25,7 +25,9 @@ exact arithmetic):
   of 2-bit rows and of 3-bit rows as two bit planes) and attention over them;
 * ``buffer``: the INT8 decode buffer -- universal scale from the cache's
   value range, symmetric clamped 8-bit codes, the flush to int4, and
-  attention over int4 rows followed by buffered INT8 rows.
+  attention over int4 rows followed by buffered INT8 rows;
+* ``asym``: asymmetric group-wise int4 rows (a scale and a zero point per
+  group of consecutive elements) and attention over them.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against hand
 derived examples, exact rational arithmetic, brute force on tiny inputs,
@@ -36,6 +38,7 @@ from .attention import attention, attention_partial, lse_merge
 from .buffer import buffer_scale, quantize_int8, dequantize_int8, flush_rows, attention_buffered
 from .lowbit import (row_bytes, quantize_rows_bits, unpack_bits, dequantize_rows_bits, dequantize_cache_bits,
                      attention_bits)
+from .asym import quantize_rows_asym, unpack_asym, dequantize_rows_asym, dequantize_cache_asym, attention_asym
 
 __all__ = [
     "quantize_rows",
@@ -56,4 +59,9 @@ __all__ = [
     "dequantize_rows_bits",
     "dequantize_cache_bits",
     "attention_bits",
+    "quantize_rows_asym",
+    "unpack_asym",
+    "dequantize_rows_asym",
+    "dequantize_cache_asym",
+    "attention_asym",
 ]
