@@ -38,7 +38,8 @@ from .attention import attention, attention_partial, lse_merge
 from .buffer import buffer_scale, quantize_int8, dequantize_int8, flush_rows, attention_buffered
 from .lowbit import (row_bytes, quantize_rows_bits, unpack_bits, dequantize_rows_bits, dequantize_cache_bits,
                      attention_bits)
-from .asym import quantize_rows_asym, unpack_asym, dequantize_rows_asym, dequantize_cache_asym, attention_asym
+from .asym import (quantize_rows_asym, unpack_asym, dequantize_rows_asym, dequantize_cache_asym, attention_asym,
+                   cache_order, to_cache_order, from_cache_order)
 
 __all__ = [
     "quantize_rows",
@@ -64,4 +65,7 @@ __all__ = [
     "dequantize_rows_asym",
     "dequantize_cache_asym",
     "attention_asym",
+    "cache_order",
+    "to_cache_order",
+    "from_cache_order",
 ]

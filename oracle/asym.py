@@ -23,13 +23,24 @@ Readings (no page gives the formulas):
 * dequantized value: s (u - z), exact in fp64.
 
 Storage: codes uint8 ``[..., D/2]``, scales fp16 bits ``[..., D/g]``, zero
-points uint8 ``[..., D/g]``.
+points uint8 ``[..., D/g]``.  ``quantize_rows_asym`` packs codes in element
+order (element 2i in the low nibble of byte i).  The cache stores the same
+nibbles in a fixed order inside each row, one for K rows and one for V rows
+(``cache_order``), so that each matrix-product block of the kernels reads
+elements of one group only; the order is a layout choice, not part of the
+quantization:
+
+* K rows, chunk c = 4 k + j (elements 8c .. 8c+7, k < D/32, j < 4) is stored
+  as dword (D/32) j + k, its element i in nibble i;
+* V rows, element e = 16 p + w (p < D/16, w < 16) is stored, for D = 128,
+  in nibble p of dword w; for D = 64 in nibble p + 4 (w // 8) of dword w % 8.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["quantize_rows_asym", "unpack_asym", "dequantize_rows_asym", "dequantize_cache_asym", "attention_asym"]
+__all__ = ["quantize_rows_asym", "unpack_asym", "dequantize_rows_asym", "dequantize_cache_asym", "attention_asym",
+           "cache_order", "to_cache_order", "from_cache_order"]
 
 
 def _check(D: int, group: int):
@@ -111,3 +122,44 @@ def attention_asym(q_bits, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zero
             for h in range(g * G, (g + 1) * G):
                 out[b, h], lse[b, h] = _attend(bf16_bits_to_f64(q_bits[b, h]), kd, vd, scale, causal, kv_len - Sq, 512)
     return out, lse
+
+
+def cache_order(D: int, tensor: str) -> np.ndarray:
+    """Element stored at nibble slot n (slot n = nibble n % 8 of dword n // 8 of a row)."""
+    if D not in (64, 128):
+        raise ValueError("head dim must be 64 or 128")
+    KK = D // 32
+    order = np.empty(D, np.int64)
+    for w in range(D // 8):
+        for i in range(8):
+            if tensor == "k":
+                j, k = divmod(w, KK)               # dword KK j + k holds chunk 4 k + j
+                elem = 8 * (4 * k + j) + i
+            elif tensor == "v":
+                if D == 128:
+                    elem = 16 * i + w              # nibble p = i, lane w
+                else:
+                    elem = 16 * (i % 4) + w + 8 * (i // 4)
+            else:
+                raise ValueError("tensor must be 'k' or 'v'")
+            order[8 * w + i] = elem
+    return order
+
+
+def _pack_u(u: np.ndarray) -> np.ndarray:
+    return (u[..., 0::2] | (u[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def to_cache_order(codes: np.ndarray, tensor: str) -> np.ndarray:
+    """Packed rows in element order -> the same nibbles in the cache's row order."""
+    u = unpack_asym(codes)
+    return np.ascontiguousarray(_pack_u(u[..., cache_order(u.shape[-1], tensor)]))
+
+
+def from_cache_order(codes: np.ndarray, tensor: str) -> np.ndarray:
+    """Rows in the cache's order -> packed rows in element order."""
+    u = unpack_asym(codes)
+    D = u.shape[-1]
+    out = np.empty_like(u)
+    out[..., cache_order(D, tensor)] = u
+    return np.ascontiguousarray(_pack_u(out))

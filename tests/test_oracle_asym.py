@@ -8,7 +8,8 @@
   the rounding-error bound,
 * symmetric int4 rows embedded as asymmetric rows (zero point 8, codes + 8,
   one group per row): the same values, and attention equal to the pinned
-  int4 attention oracle.
+  int4 attention oracle,
+* the cache's row orders: hand-checked slots, a permutation, a round trip.
 """
 import struct
 from fractions import Fraction
@@ -161,3 +162,32 @@ def test_attention_equals_int4_attention_on_embedded_rows(causal):
     ro, rl = attention(q, kc, ks, vc, vs, L, 0.3, causal=causal)
     np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l, rl, rtol=0, atol=1e-12)
+
+
+def test_cache_order_by_hand():
+    from oracle import cache_order
+    k128 = cache_order(128, "k").reshape(16, 8)
+    assert k128[1].tolist() == list(range(32, 40))      # dword 1 = chunk 4 (k = 1, j = 0)
+    assert k128[4].tolist() == list(range(8, 16))       # dword 4 = chunk 1 (k = 0, j = 1)
+    assert k128[15].tolist() == list(range(120, 128))
+    k64 = cache_order(64, "k").reshape(8, 8)
+    assert k64[1].tolist() == list(range(32, 40)) and k64[2].tolist() == list(range(8, 16))
+    v128 = cache_order(128, "v").reshape(16, 8)
+    assert v128[0].tolist() == [0, 16, 32, 48, 64, 80, 96, 112]
+    assert v128[5].tolist() == [5, 21, 37, 53, 69, 85, 101, 117]
+    v64 = cache_order(64, "v").reshape(8, 8)
+    assert v64[0].tolist() == [0, 16, 32, 48, 8, 24, 40, 56]
+    assert v64[7].tolist() == [7, 23, 39, 55, 15, 31, 47, 63]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("tensor", ["k", "v"])
+def test_cache_order_round_trip(D, tensor):
+    from oracle import cache_order, from_cache_order, to_cache_order
+    assert sorted(cache_order(D, tensor).tolist()) == list(range(D))
+    rng = np.random.default_rng(D)
+    c = rng.integers(0, 256, size=(5, 3, D // 2), dtype=np.uint8)
+    t = to_cache_order(c, tensor)
+    assert np.array_equal(from_cache_order(t, tensor), c)
+    # slot n of the stored row holds element cache_order[n]
+    assert np.array_equal(unpack_asym(t), unpack_asym(c)[..., cache_order(D, tensor)])
