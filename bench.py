@@ -392,6 +392,43 @@ def bench_lowbit(torch, qkv, w, steps):
     return res
 
 
+def bench_asym(torch, qkv, w, steps, int4_ms=None):
+    """Decode over asymmetric group-wise int4 caches of the same workload (groups
+    of 32, 64 and 128 elements; decode only, caches rotated past the MALL)."""
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w)
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D), 1), dtype=torch.uint8,
+                     device="cuda")
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    del k, v
+    res = {"workload": w.name}
+    for group in (32, 64, 128):
+        kv_bytes = 2 * w.B * w.Hkv * w.L * (w.D // 2 + 4 * (w.D // group))
+        n_copies = max(4, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+        c0 = qkv.AsymKVCache.empty(w.B, w.Hkv, w.L, w.D, group)
+        qkv.quantize_append_kv_asym(kt, vt, c0, 0)
+        caches = [c0] + [qkv.AsymKVCache(*(t.clone() for t in c0.tensors()), group) for _ in range(n_copies - 1)]
+
+        def run(i):
+            qkv.decode_asym(q, caches[i], w.L, softmax_scale=w.softmax_scale, out=out, workspace=ws)
+
+        for i in range(5):
+            run(i % n_copies)
+        torch.cuda.synchronize()
+        ms = region_ms(torch, run, steps, n_copies)
+        alg = kv_bytes + w.B * w.Hq * w.Sq * w.D * 6
+        r = {"ms": ms, "kv_bytes": kv_bytes, "GBps": alg / (ms * 1e-3) / 1e9,
+             "frac_hbm": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if int4_ms:
+            r["time_vs_int4"] = ms / int4_ms
+        res[f"group{group}"] = r
+        del caches, c0
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(torch, qkv, w, iters):
     from qkv_inputs import make_qkv
     q_bits, k, v = make_qkv(w)
@@ -621,6 +658,9 @@ def main():
         log("buffered:", json.dumps(secondary["int8_buffer_decode"]))
         secondary["lowbit_decode"] = bench_lowbit(torch, qkv, w3, max(args.steps, 20))
         log("lowbit:", json.dumps(secondary["lowbit_decode"]))
+        secondary["asym_group_decode"] = bench_asym(torch, qkv, w3, max(args.steps, 20),
+                                                    secondary["lowbit_decode"]["4bit"]["ms"])
+        log("asym:", json.dumps(secondary["asym_group_decode"]))
     if args.only in ("all", "prefill"):
         secondary["causal_prefill_16k"] = bench_prefill(torch, qkv, workload("causal_prefill_16k"), 10)
         log("prefill:", json.dumps(secondary["causal_prefill_16k"]))

@@ -183,6 +183,49 @@ qkv_status qkv_decode_bits(const uint16_t* q,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Asymmetric group-wise 4-bit rows (TurboAttention, arXiv 2412.08585, §2.3:
+ * a scale s and a zero point z per quantization group, value s (code - z);
+ * §3.1 keeps asymmetric INT4 groups for K and V; "Quantized Cross-Attention"
+ * §4.1: scales [b, h, seq_kv, dim/GROUP_SIZE]).  Each row (one token of one
+ * KV head) is split into groups of `group` consecutive elements (32, 64 or
+ * 128, at most D); per group, in IEEE fp32:
+ *   lo = min(0, min x), hi = max(0, max x)
+ *   s  = fp16_rne((hi - lo) / 15)
+ *   z  = clamp(rint(-lo / s), 0, 15)
+ *   u  = clamp(rint(x / s) + z, 0, 15)       (rint: half to even)
+ * and a zero s gives z = 0 and all codes 0.  Layout:
+ *   codes   uint8 [B, Hkv, C, D/2], unsigned u, nibble n of a row at bits
+ *           4 (n % 2) of byte n / 2, in a fixed order per tensor (so that
+ *           each matrix-product block of the decode reads one group):
+ *             K rows: chunk c = 4 k + j (elements 8c .. 8c+7, k < D/32,
+ *               j < 4) in dword (D/32) j + k, element 8c + i in nibble i;
+ *             V rows: element 16 p + w (p < D/16, w < 16) in nibble p of
+ *               dword w (D = 128), or in nibble p + 4 (w / 8) of dword
+ *               w % 8 (D = 64)
+ *   params  uint32 [B, Hkv, C, D/group]: s's fp16 bits in bits 0-15, z in
+ *           bits 16-19, other bits zero; 4-byte aligned
+ *   qkv_quantize_append_kv_asym: quantizes T new rows of K and V into cache
+ *     rows [pos, pos + T) (arguments as qkv_quantize_append_kv).
+ *   qkv_decode_asym: qkv_decode over such a cache (same workspace contract:
+ *     qkv_decode_workspace_bytes).  Codes enter the matrix products exactly;
+ *     scales and zero points are applied per group in fp32.
+ * Requires group in {32, 64, 128} and group <= D (QKV_ERR_UNSUPPORTED
+ * otherwise) and the requirements of the int4 calls.
+ */
+qkv_status qkv_quantize_append_kv_asym(const float* k_src, const float* v_src,
+                                       uint8_t* k_codes, uint32_t* k_params,
+                                       uint8_t* v_codes, uint32_t* v_params,
+                                       int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                                       int64_t C, int64_t pos, int group, void* stream);
+qkv_status qkv_decode_asym(const uint16_t* q,
+                           const uint8_t* k_codes, const uint32_t* k_params,
+                           const uint8_t* v_codes, const uint32_t* v_params,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                           int64_t C, int64_t D, int group, float softmax_scale, int num_splits,
+                           float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * (a)+(b) One decode step in one launch: append, then attend.  Quantizes
  * n_new new K and V rows into cache rows [pos, pos + n_new), exactly as
  * qkv_quantize_append_kv does, then computes qkv_decode over cache rows

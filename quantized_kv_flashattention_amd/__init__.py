@@ -35,6 +35,9 @@ __all__ = [
     "buffer_flush",
     "decode_buffered",
     "decode_buffered_workspace_bytes",
+    "AsymKVCache",
+    "quantize_append_kv_asym",
+    "decode_asym",
     "prefill",
     "decode_workspace_bytes",
     "decode_auto_splits",
@@ -99,6 +102,11 @@ def _load():
                                     vp, vp, vp, sz, vp]
     lib.qkv_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                 vp, vp, vp]
+    lib.qkv_quantize_append_kv_asym.restype = ci
+    lib.qkv_quantize_append_kv_asym.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.qkv_decode_asym.restype = ci
+    lib.qkv_decode_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                    vp, vp, vp, sz, vp]
     return lib
 
 
@@ -288,6 +296,75 @@ def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False,
         _check(_lib.qkv_decode_bits(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
                                     C, D, int(bits), _scale(softmax_scale, D), int(num_splits), _ptr(out),
                                     _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+@dataclasses.dataclass
+class AsymKVCache:
+    """Caller-owned asymmetric group-wise int4 KV cache of one layer: unsigned
+    nibble codes and one parameter word per group of ``group`` consecutive
+    elements (fp16 scale in bits 0-15, zero point in bits 16-19)."""
+
+    k_codes: torch.Tensor   # uint8 [B, Hkv, C, D/2]
+    k_params: torch.Tensor  # int32 [B, Hkv, C, D/group]
+    v_codes: torch.Tensor
+    v_params: torch.Tensor
+    group: int
+
+    @staticmethod
+    def empty(B: int, Hkv: int, C: int, D: int, group: int, device="cuda") -> "AsymKVCache":
+        mk = lambda: torch.empty((B, Hkv, C, D // 2), dtype=torch.uint8, device=device)
+        mp = lambda: torch.empty((B, Hkv, C, D // group), dtype=torch.int32, device=device)
+        return AsymKVCache(mk(), mp(), mk(), mp(), int(group))
+
+    def tensors(self):
+        return self.k_codes, self.k_params, self.v_codes, self.v_params
+
+
+def _asym_args(cache: AsymKVCache, device, B, Hkv, D):
+    kc, kp, vc, vp = cache.tensors()
+    for name, t, dt in (("k_codes", kc, torch.uint8), ("k_params", kp, torch.int32),
+                        ("v_codes", vc, torch.uint8), ("v_params", vp, torch.int32)):
+        _req(t, name, dt, 4)
+        if t.device != device:
+            raise ValueError("all tensors must be on one device")
+    if kc.shape[:2] != (B, Hkv) or kc.shape[3] * 2 != D or vc.shape != kc.shape or \
+            kp.shape != kc.shape[:3] + (D // max(cache.group, 1),) or vp.shape != kp.shape:
+        raise ValueError("cache shape does not match")
+    return kc, kp, vc, vp, kc.shape[2]
+
+
+def quantize_append_kv_asym(k_src: torch.Tensor, v_src: torch.Tensor, cache: AsymKVCache, pos: int):
+    """Quantize new K and V rows ``[B, Hkv, T, D]`` into rows ``[pos, pos+T)`` of an
+    asymmetric group-wise cache (one launch)."""
+    _req(k_src, "k_src", torch.float32, 4)
+    _req(v_src, "v_src", torch.float32, 4)
+    if k_src.shape != v_src.shape or k_src.device != v_src.device:
+        raise ValueError("k_src and v_src must have one shape and device")
+    B, Hkv, T, D = k_src.shape
+    kc, kp, vc, vp, C = _asym_args(cache, k_src.device, B, Hkv, D)
+    _check(_lib.qkv_quantize_append_kv_asym(_ptr(k_src), _ptr(v_src), _ptr(kc), _ptr(kp), _ptr(vc), _ptr(vp),
+                                            B, Hkv, T, D, C, int(pos), int(cache.group), _stream(k_src)))
+
+
+def decode_asym(q, cache: AsymKVCache, kv_len, softmax_scale=None, num_splits=0, return_lse=False, out=None,
+                lse=None, workspace=None):
+    """Decode attention of ``q [B, Hq, Sq, D]`` over rows ``[0, kv_len)`` of an asymmetric
+    group-wise cache."""
+    _req(q, "q", torch.bfloat16, 4)
+    if not isinstance(cache, AsymKVCache):
+        raise TypeError("cache must be an AsymKVCache")
+    B, Hq, Sq, D = q.shape
+    Hkv = int(cache.k_codes.shape[1]) if cache.k_codes.dim() == 4 else 0
+    kc, kp, vc, vp, C = _asym_args(cache, q.device, B, Hkv, D)
+    out, lse = _outputs(q, out, lse, return_lse)
+    need = decode_workspace_bytes(B, Hq, Hkv, Sq, kv_len, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, B * Hkv, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.qkv_decode_asym(_ptr(q), _ptr(kc), _ptr(kp), _ptr(vc), _ptr(vp), B, Hq, Hkv, Sq, int(kv_len),
+                                C, D, int(cache.group), _scale(softmax_scale, D), int(num_splits), _ptr(out),
+                                _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
     return (out, lse) if return_lse else out
 
 

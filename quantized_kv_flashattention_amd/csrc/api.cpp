@@ -159,7 +159,8 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
                          float softmax_scale, int num_splits, float* out, float* lse,
                          void* workspace, size_t workspace_bytes,
                          const qkvfa::DecodeAppend* append, const qkvfa::DecodeVarlen* varlen,
-                         void* stream, const char* fn, int bits = 4) {
+                         void* stream, const char* fn, int bits = 4,
+                         const qkvfa::DecodeAsym* asym = nullptr) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -184,7 +185,7 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
   return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
                                          kv_len, varlen ? varlen->page_size : C, (int)D,
                                          softmax_scale, plan, out, lse, workspace, append, varlen,
-                                         nullptr, bits, static_cast<hipStream_t>(stream)),
+                                         nullptr, bits, static_cast<hipStream_t>(stream), asym),
                     fn);
 }
 
@@ -238,6 +239,51 @@ qkv_status qkv_quantize_append_kv_bits(const float* k_src, const float* v_src, u
                                                        B * Hkv, T, (int)D, C, pos, bits,
                                                        static_cast<hipStream_t>(stream)),
                     "qkv_quantize_append_kv_bits");
+}
+
+static bool valid_group(int64_t D, int group) {
+  return (group == 32 || group == 64 || group == 128) && group <= D;
+}
+
+qkv_status qkv_quantize_append_kv_asym(const float* k_src, const float* v_src, uint8_t* k_codes,
+                                       uint32_t* k_params, uint8_t* v_codes, uint32_t* v_params,
+                                       int64_t B, int64_t Hkv, int64_t T, int64_t D, int64_t C,
+                                       int64_t pos, int group, void* stream) {
+  const char* fn = "qkv_quantize_append_kv_asym";
+  if (B < 1 || Hkv < 1 || T < 0 || C < 1)
+    return fail(QKV_ERR_INVALID_ARG, std::string(fn) + ": need B, Hkv, C >= 1 and T >= 0");
+  if (D != 64 && D != 128) return fail(QKV_ERR_UNSUPPORTED, std::string(fn) + ": head dim must be 64 or 128");
+  if (!valid_group(D, group))
+    return fail(QKV_ERR_UNSUPPORTED, std::string(fn) + ": group must be 32, 64 or 128 and at most the head dim");
+  if (pos < 0 || pos + T > C)
+    return fail(QKV_ERR_INVALID_ARG, std::string(fn) + ": need 0 <= pos and pos + T <= C");
+  if (T == 0) return QKV_OK;
+  if (!k_src || !v_src || !k_codes || !k_params || !v_codes || !v_params)
+    return fail(QKV_ERR_INVALID_ARG, std::string(fn) + ": null tensor pointer");
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_params, 4) || !aligned(v_params, 4))
+    return fail(QKV_ERR_INVALID_ARG, std::string(fn) + ": misaligned pointer");
+  if (B * Hkv > 0x3FFFFFFFll) return fail(QKV_ERR_UNSUPPORTED, std::string(fn) + ": B * Hkv too large");
+  return hip_status(qkvfa::launch_quantize_append_asym(k_src, k_codes, k_params, v_src, v_codes, v_params,
+                                                       B * Hkv, T, (int)D, C, pos, group,
+                                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+qkv_status qkv_decode_asym(const uint16_t* q, const uint8_t* k_codes, const uint32_t* k_params,
+                           const uint8_t* v_codes, const uint32_t* v_params, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D, int group,
+                           float softmax_scale, int num_splits, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_group(D, group))
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_asym: group must be 32, 64 or 128 and at most the head dim");
+  if ((k_params && !aligned(k_params, 4)) || (v_params && !aligned(v_params, 4)))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_asym: misaligned group parameters");
+  const qkvfa::DecodeAsym asym = {k_params, v_params, group};
+  return decode_common(q, k_codes, reinterpret_cast<const uint16_t*>(k_params), v_codes,
+                       reinterpret_cast<const uint16_t*>(v_params), B, Hq, Hkv, Sq, kv_len, C, D,
+                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr, nullptr,
+                       stream, "qkv_decode_asym", 4, &asym);
 }
 
 qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float* v_new,

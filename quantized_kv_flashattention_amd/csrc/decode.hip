@@ -118,6 +118,12 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   const int32_t* block_table;
   int len_cap, page_size, max_pages, num_pages;
+  // asymmetric group-wise rows (ASYM kernels): codes are unsigned nibbles,
+  // group parameters kp/vp [B, Hkv, C, ng] (fp16 scale in bits 0-15, zero
+  // point in bits 16-19) for groups of 2^gshift consecutive elements
+  const uint32_t* kp;
+  const uint32_t* vp;
+  int ng, gshift;
   // INT8 decode buffer (tail_rows > 0): the last split attends buffered rows
   // [0, tail_rows) of tk/tv [B, Hkv, buf_rows, D] after the kv_len cache
   // rows the other splits attend; rows [tail_len, tail_rows) are the call's
@@ -165,7 +171,7 @@ __device__ __forceinline__ void quantize_row_wave(const float* __restrict__ src,
   }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int NGA = 0>
 struct ChunkRegs {
   // K: the lane's D/4 elements of rows kb = 0, 1 (nibbles, or for 2/3 bits
   // the low-bit bytes: two per 8 elements); V: the lane's 8 elements of 8
@@ -177,6 +183,11 @@ struct ChunkRegs {
   uint32_t kh[BITS == 3 ? 2 : 1];
   uint32_t vh[BITS == 3 ? 8 : 1];
   uint16_t sk, sv;   // K and V scale of token (lane % 32) of the chunk
+  // asymmetric rows (NGA groups per row): parameter words lane * NPW + u of
+  // the chunk's K and V rows (word w: token w / NGA, group w % NGA)
+  static constexpr int NPW = NGA == 4 ? 2 : 1;
+  uint32_t kpw[NPW];
+  uint32_t vpw[NPW];
 };
 
 // One wave64 holds NB*32 + ~90 VGPRs.  The planner launches about one
@@ -185,10 +196,11 @@ struct ChunkRegs {
 // skips the one-chunk prefetch to stay within 256 VGPRs.
 // (3-bit rows keep a second set of top-bit registers per chunk: their one
 // row-block variant asks for three waves per SIMD instead of four.)
-template <int D, int NB, bool PAGED, int BITS>
+template <int D, int NB, bool PAGED, int BITS, int NGA>
 __global__ __launch_bounds__(64 * waves_for(NB))
-__attribute__((amdgpu_waves_per_eu(NB == 1 ? (BITS == 3 ? 3 : 4) : 1, 8)))
+__attribute__((amdgpu_waves_per_eu(NB == 1 ? ((BITS == 3 || NGA > 0) ? 3 : 4) : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
+  constexpr bool ASYM = NGA > 0;   // asymmetric group-wise rows, NGA groups per row
   constexpr int kWaves = waves_for(NB);
   constexpr bool kPrefetch = (NB <= 2);
   constexpr int KK = D / 32;    // QK MFMAs per 16-token block
@@ -199,10 +211,18 @@ void decode_kernel(const DecodeArgs a) {
   auto kbias = [](int e) { return BITS == 4 ? kNibBias : lowbit_bias<BITS>(e >> 1); };
   auto vbias = [](int p) { return BITS == 4 ? kNibBias : lowbit_bias<BITS>(p & 3); };
   static_assert(BITS == 4 || !PAGED, "the paged cache holds 4-bit rows");
+  static_assert(!ASYM || (BITS == 4 && !PAGED && (NGA == 1 || NGA == 2 || NGA == 4) && D / NGA >= 32),
+                "asymmetric rows: 4 bits, contiguous cache, groups of 32, 64 or 128 elements");
+  using Regs = ChunkRegs<D, BITS, NGA>;
+  constexpr int NPW = Regs::NPW;
   constexpr int OSTR = D + 4;   // padded LDS row stride of the merge buffer (floats)
 
   __shared__ __align__(16) _Float16 s_q[NB * 16 * D];
   __shared__ __align__(16) float s_sc[kWaves][96];   // K column scale, V scale, mask bias
+  // asymmetric rows, per wave and chunk, [group][token]: K -s x softmax scale
+  // x log2 e and 79 - z (fp32); V s and 79 - z (fp16)
+  __shared__ __align__(16) float s_ak[ASYM ? kWaves : 1][2][ASYM ? NGA : 1][32];
+  __shared__ __align__(16) _Float16 s_av[ASYM ? kWaves : 1][2][ASYM ? NGA : 1][32];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   // wave-merge buffer [kWaves][rows_o][OSTR] floats, later the split-merge
@@ -431,7 +451,7 @@ void decode_kernel(const DecodeArgs a) {
     // chunk past the split can be "loaded" unconditionally (all zeros, no
     // traffic), which keeps the prefetch branch-free: a conditional prefetch
     // makes the compiler wait for every outstanding load where the paths join.
-    auto load_chunk = [&](int c0, ChunkRegs<D, BITS>& cr, int lim, bool from_lds) {
+    auto load_chunk = [&](int c0, Regs& cr, int lim, bool from_lds) {
       // a chunk is 32 rows; with a paged cache it never straddles a page.  The
       // clamp is made scalar explicitly: computed in a vector register, the
       // descriptor would look divergent and each load would become a loop.
@@ -478,19 +498,37 @@ void decode_kernel(const DecodeArgs a) {
             cr.vh[e] = __builtin_amdgcn_raw_buffer_load_b8(rv, offv + e * ROWB + D / 4 - (r % DW), 0, 0);
         }
       }
-      cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
-      cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
+      if constexpr (ASYM) {
+        // the chunk's 32 x NGA parameter words, NPW per lane; words past the
+        // range read as zero (scale 0: the token's values are 0)
+        const rsrc_t rkp = make_rsrc(a.kp + row0 * NGA, rows_left * NGA * 4);
+        const rsrc_t rvp = make_rsrc(a.vp + row0 * NGA, rows_left * NGA * 4);
+        if constexpr (NPW == 2) {
+          const uint2v wk = __builtin_amdgcn_raw_buffer_load_b64(rkp, 8 * lane, 0, 0);
+          const uint2v wv = __builtin_amdgcn_raw_buffer_load_b64(rvp, 8 * lane, 0, 0);
+          cr.kpw[0] = wk[0];
+          cr.kpw[1] = wk[1];
+          cr.vpw[0] = wv[0];
+          cr.vpw[1] = wv[1];
+        } else {
+          cr.kpw[0] = __builtin_amdgcn_raw_buffer_load_b32(rkp, 4 * lane, 0, 0);
+          cr.vpw[0] = __builtin_amdgcn_raw_buffer_load_b32(rvp, 4 * lane, 0, 0);
+        }
+      } else {
+        cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
+        cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
+      }
     };
 
     const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
-    ChunkRegs<D, BITS> cur;
+    Regs cur;
     load_chunk(t_begin + wave * kChunk, cur, t_main, false);
 
     // ---- append mode: quantize the new rows (one wave per row and tensor,
     //      from the last wave down: with one row block the first half of the
     //      waves converts the query meanwhile), while the first chunk loads
     //      (4-bit caches only)
-    if (BITS == 4 && append) {
+    if (BITS == 4 && !ASYM && append) {
       const int ntask = 2 * max(new_hi - new_lo, 0);
       for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
         const int t = new_lo + (task >> 1);
@@ -544,6 +582,9 @@ void decode_kernel(const DecodeArgs a) {
     // Outputs: s_run sums the fp16 P~ values the PV MFMAs consumed (rescaled
     // like O), and the wave merge takes b x s_run out of each output.
     float m_run[NB], l_run[NB], s_run[NB], kinit[NB];
+    // asymmetric rows: Q_g = sum of the row's query elements in group g, and
+    // per group the sum of P~ (79 - z) the PV MFMAs consumed (rescaled like O)
+    float qg[NB][ASYM ? NGA : 1], sg[NB][ASYM ? NGA : 1];
     float4v o_acc[NB][NPB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -553,21 +594,44 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int p = 0; p < NPB; ++p) o_acc[nb][p] = float4v{0.f, 0.f, 0.f, 0.f};
       const int qrow = nb * 16 + r;
-      float qb = 0.0f;
+      if constexpr (ASYM) {
+        // the cache's K order gives block kk the elements 32 kk .. 32 kk + 31:
+        // lane j holds query chunk 4 kk + j for it
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
-        const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+        for (int gi = 0; gi < NGA; ++gi) {
+          qg[nb][gi] = 0.0f;
+          sg[nb][gi] = 0.0f;
+        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qb = fmaf((float)qop[e], kbias(e), qb);
+        for (int kk = 0; kk < KK; ++kk) {
+          const int qc = (4 * kk + j) ^ (qrow & 15 & (DW - 1));
+          const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qg[nb][kk / (KK / NGA)] += (float)qop[e];
+        }
+#pragma unroll
+        for (int gi = 0; gi < NGA; ++gi) {
+          qg[nb][gi] = xor_sum(qg[nb][gi], 16);
+          qg[nb][gi] = xor_sum(qg[nb][gi], 32);
+        }
+        kinit[nb] = 0.0f;
+      } else {
+        float qb = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int qc = (KK * j + kk) ^ (qrow & 15 & (DW - 1));
+          const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qb = fmaf((float)qop[e], kbias(e), qb);
+        }
+        qb = xor_sum(qb, 16);
+        qb = xor_sum(qb, 32);
+        kinit[nb] = -qb;
       }
-      qb = xor_sum(qb, 16);
-      qb = xor_sum(qb, 32);
-      kinit[nb] = -qb;
     }
 
     // One chunk: scores, online softmax, PV.  `cr` holds its codes and scales.
-    auto process_chunk = [&](int c0, ChunkRegs<D, BITS>& cr, int lim) {
+    auto process_chunk = [&](int c0, Regs& cr, int lim) {
         // ---- scales: each lane converts one, the wave reads its eight back.  A
         //      token at or past the split end gets bias -inf (score masked), so
         //      the score is one FMA on every chunk, full or not.
@@ -704,18 +768,157 @@ void decode_kernel(const DecodeArgs a) {
         }
     };
 
+    // One chunk of asymmetric group-wise rows.  Codes enter the MFMAs as the
+    // exact fp16 value 79 - u (one v_bitop3 per pair).  Scores: the cache's K
+    // order makes block kk the elements 32 kk .. 32 kk + 31, so a group's
+    // blocks accumulate on their own, from -(79 - z) Q_g: the result is
+    // -sum q (u - z) over the group, exact up to fp32 sums, and -s x softmax
+    // scale x log2 e (fp32) adds the group's share of the score.  Outputs: the
+    // cache's V order makes PV block p the elements 16 p .. 16 p + 15, so a
+    // group's blocks take P~_g = fp16(p s) of the group, and sg collects
+    // sum P~_g (79 - z); the wave merge forms sg - O.
+    auto process_chunk_asym = [&](int c0, Regs& cr, int lim) {
+      if constexpr (ASYM) {
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+          const int w = lane * NPW + u;   // token w / NGA, group w % NGA
+          if (w < 32 * NGA) {
+            const int t = w / NGA, gi = w % NGA;
+            const uint32_t pk = cr.kpw[u], pv = cr.vpw[u];
+            s_ak[wave][0][gi][t] = -f16bits_to_f32((uint16_t)pk) * a.qk_log2;
+            s_ak[wave][1][gi][t] = 79.0f - (float)((pk >> 16) & 15u);
+            s_av[wave][0][gi][t] = bitcast<_Float16>((uint16_t)pv);
+            s_av[wave][1][gi][t] = bitcast<_Float16>((uint16_t)(0x5400u | ((15u - ((pv >> 16) & 15u)) << 4)));
+          }
+        }
+        if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < lim) ? 0.0f : -INFINITY;
+        const float4v mb0 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j]);
+        const float4v mb1 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + 8 * j + 4]);
+
+        if constexpr (D == 64) {
+          // lanes 8..15 own nibbles 4..7 of their dword: move them down
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cr.vw[e] = (r >= 8) ? (cr.vw[e] >> 16) : cr.vw[e];
+        }
+
+        // ---- scores S^T (tokens 8 j + 4 kb + i of this lane), group by group
+        float4v xs[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          xs[nb][0] = mb0;
+          xs[nb][1] = mb1;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int gi = 0; gi < NGA; ++gi) {
+            const float4v nc = *reinterpret_cast<const float4v*>(&s_ak[wave][0][gi][8 * j + 4 * kb]);
+            const float4v bz = *reinterpret_cast<const float4v*>(&s_ak[wave][1][gi][8 * j + 4 * kb]);
+            float4v acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = bz * -qg[nb][gi];
+#pragma unroll
+            for (int kq = 0; kq < KK / NGA; ++kq) {
+              const int kk = gi * (KK / NGA) + kq;
+              const half8v kop = unpack8_n79(cr.kw[kb][kk]);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                const int qrow = nb * 16 + r;
+                const int qc = (4 * kk + j) ^ (qrow & 15 & (DW - 1));
+                const half8v qop = *reinterpret_cast<const half8v*>(&s_q[(qrow * DW + qc) * 8]);
+                acc[nb] = mfma16x16x32(kop, qop, acc[nb]);
+              }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) xs[nb][kb] += nc * acc[nb];
+          }
+        }
+
+        // ---- online softmax per row block
+        float pr[NB][8];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float mloc = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, xs[nb][e >> 2][e & 3]);
+          mloc = xor_max(mloc, 16);
+          mloc = xor_max(mloc, 32);
+          const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
+          const float alpha = fast_exp2(m_run[nb] - m_new);
+          float lsum = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pr[nb][e] = fast_exp2(xs[nb][e >> 2][e & 3] - m_new);
+            lsum += pr[nb][e];
+          }
+          l_run[nb] = l_run[nb] * alpha + lsum;
+          m_run[nb] = m_new;
+#pragma unroll
+          for (int gi = 0; gi < NGA; ++gi) sg[nb][gi] *= alpha;
+          if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
+          }
+        }
+
+        // ---- O^T += V^T P~_g^T, group by group (PV blocks 2k, 2k + 1 from byte k)
+#pragma unroll
+        for (int gi = 0; gi < NGA; ++gi) {
+          const half8v sv = *reinterpret_cast<const half8v*>(&s_av[wave][0][gi][8 * j]);
+          const uint4v bzv = *reinterpret_cast<const uint4v*>(&s_av[wave][1][gi][8 * j]);
+          half8v pop[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            uint4v pw;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              pw[h] = bitcast<uint32_t>(cvt_pk_f16(pr[nb][2 * h] * (float)sv[2 * h],
+                                                   pr[nb][2 * h + 1] * (float)sv[2 * h + 1]));
+            float ps = sg[nb][gi];
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              ps = __builtin_amdgcn_fdot2(bitcast<half2v>(pw[h]), bitcast<half2v>(bzv[h]), ps, false);
+            sg[nb][gi] = ps;
+            pop[nb] = bitcast<half8v>(pw);
+          }
+#pragma unroll
+          for (int kq = 0; kq < NPB / 2 / NGA; ++kq) {
+            const int k = gi * (NPB / 2 / NGA) + kq;
+            uint4v wlo, whi;
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+              const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
+              wlo[hh] = nib_n79(xb << 4);
+              whi[hh] = nib_n79(xb);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              o_acc[nb][2 * k] = mfma16x16x32(bitcast<half8v>(wlo), pop[nb], o_acc[nb][2 * k]);
+              o_acc[nb][2 * k + 1] = mfma16x16x32(bitcast<half8v>(whi), pop[nb], o_acc[nb][2 * k + 1]);
+            }
+          }
+        }
+      }
+    };
+    auto process = [&](int c0, Regs& cr, int lim) {
+      if constexpr (ASYM)
+        process_chunk_asym(c0, cr, lim);
+      else
+        process_chunk(c0, cr, lim);
+    };
+
     for (int c = wave; c < n_chunks; c += kWaves) {
       const int c0 = t_begin + c * kChunk;
       // Compiler-only barrier: keeps the query-operand LDS reads inside the loop
       // instead of hoisted into (NB * D / 8) live registers per lane.
       asm volatile("" ::: "memory");
       if constexpr (kPrefetch) {
-        ChunkRegs<D, BITS> nxt;
+        Regs nxt;
         load_chunk(c0 + kWaves * kChunk, nxt, t_main, true);
-        process_chunk(c0, cur, t_main);
+        process(c0, cur, t_main);
         cur = nxt;
       } else {
-        process_chunk(c0, cur, t_main);
+        process(c0, cur, t_main);
         load_chunk(c0 + kWaves * kChunk, cur, t_main, true);
       }
     }
@@ -723,10 +926,10 @@ void decode_kernel(const DecodeArgs a) {
     // ---- append mode: tail chunks [t_main, t_end).  Rows before pos come from
     //      the cache (the load range ends at pos, so no row at or past it is
     //      read), rows from pos on from the LDS copy of the new rows.
-    if constexpr (BITS == 4) if (append) {
+    if constexpr (BITS == 4 && !ASYM) if (append) {
       for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
         if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
-        ChunkRegs<D, BITS> cr;
+        Regs cr;
         load_chunk(c0, cr, max(pos_b, c0), true);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -755,16 +958,30 @@ void decode_kernel(const DecodeArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       float l = xor_sum(l_run[nb], 16);
       l = xor_sum(l, 32);
-      float sp = xor_sum(s_run[nb], 16);
-      sp = xor_sum(sp, 32);
+      if constexpr (ASYM) {
 #pragma unroll
-      for (int p = 0; p < NPB; ++p) o_acc[nb][p] -= vbias(p) * sp;
+        for (int gi = 0; gi < NGA; ++gi) {
+          float sp = xor_sum(sg[nb][gi], 16);
+          sp = xor_sum(sp, 32);
+#pragma unroll
+          for (int p = gi * (NPB / NGA); p < (gi + 1) * (NPB / NGA); ++p) o_acc[nb][p] = sp - o_acc[nb][p];
+        }
+      } else {
+        float sp = xor_sum(s_run[nb], 16);
+        sp = xor_sum(sp, 32);
+#pragma unroll
+        for (int p = 0; p < NPB; ++p) o_acc[nb][p] -= vbias(p) * sp;
+      }
       if (j == 0) {
         s_m[wave][r] = m_run[nb];
         s_l[wave][r] = l;
       }
       float* orow = s_o + (wave * rows_o + r) * OSTR;
-      if (r < rows_o) {   // rows past R are padding of the 16-row block
+      if (ASYM && r < rows_o) {
+        // the cache's V order: block p row m is head dim 16 p + m
+#pragma unroll
+        for (int p = 0; p < NPB; ++p) *reinterpret_cast<float4v*>(orow + 16 * p + 4 * j) = o_acc[nb][p];
+      } else if (r < rows_o) {   // rows past R are padding of the 16-row block
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (D == 128) {
@@ -944,15 +1161,15 @@ void decode_kernel(const DecodeArgs a) {
   merge_splits();
 }
 
-template <int D, int NB, bool PAGED, int BITS>
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0>
 hipError_t launch_kernel(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
   // this kernel the larger dynamic LDS once
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS>),
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
   if (attr != hipSuccess) return attr;
-  decode_kernel<D, NB, PAGED, BITS><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  decode_kernel<D, NB, PAGED, BITS, NGA><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -962,6 +1179,12 @@ hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, int bi
   const int R = args.G * args.Sq;
   size_t lds = merge_lds_bytes(D, waves_for(NB), R, n_split);
   if (args.tail_rows > 0 && lds < tail_lds_bytes(D, R)) lds = tail_lds_bytes(D, R);
+  if (args.kp != nullptr) {
+    if (args.ng == 1) return launch_kernel<D, NB, false, 4, 1>(args, grid, lds, stream);
+    if (args.ng == 2) return launch_kernel<D, NB, false, 4, 2>(args, grid, lds, stream);
+    if constexpr (D == 128) return launch_kernel<D, NB, false, 4, 4>(args, grid, lds, stream);
+    return hipErrorInvalidValue;
+  }
   if (bits == 2) return launch_kernel<D, NB, false, 2>(args, grid, lds, stream);
   if (bits == 3) return launch_kernel<D, NB, false, 3>(args, grid, lds, stream);
   if (args.block_table != nullptr) return launch_kernel<D, NB, true, 4>(args, grid, lds, stream);
@@ -1039,9 +1262,16 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         const DecodeTail* tail, int bits, hipStream_t stream) {
+                         const DecodeTail* tail, int bits, hipStream_t stream, const DecodeAsym* asym) {
   DecodeArgs a;
   a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
+  a.kp = nullptr; a.vp = nullptr; a.ng = 1; a.gshift = 0;
+  if (asym) {
+    a.kp = asym->k_params;
+    a.vp = asym->v_params;
+    a.ng = D / asym->group;
+    a.gshift = 31 - __builtin_clz((unsigned)asym->group);
+  }
   a.out = out; a.lse = lse;
   a.k_new = nullptr; a.v_new = nullptr;
   a.kc_w = nullptr; a.ks_w = nullptr; a.vc_w = nullptr; a.vs_w = nullptr;

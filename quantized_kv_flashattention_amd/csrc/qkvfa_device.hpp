@@ -217,6 +217,28 @@ __device__ __forceinline__ half8v unpack8_lowbit_b(uint32_t lo16, uint32_t top8)
   return bitcast<half8v>(lowbit4_b<BITS>(spread_bytes(lo16, 0), z));
 }
 
+// ---- Asymmetric group-wise rows: unsigned nibbles u.  Each enters the
+// matrix products as the exact fp16 value 79 - u: flipping all four bits
+// gives 15 - u, OR-ed into bits 4-7 of 64 (one v_bitop3).  The kernel then
+// starts each group's score accumulator at -(79 - z) Q_g and multiplies the
+// result by -s; outputs subtract their sum from the group's sum(P~ (79 - z)).
+
+// Unsigned nibbles in bits 4-7 and 20-23 of x -> fp16 pair 79 - u.
+__device__ __forceinline__ uint32_t nib_n79(uint32_t x) {
+  return ((x ^ 0x00F000F0u) & 0x00F000F0u) | 0x54005400u;
+}
+
+// Eight nibbles of a dword (element i in bits 4i..4i+3) -> 79 - u in the
+// unpack8_perm order [u0, u4, u1, u5, u2, u6, u3, u7].
+__device__ __forceinline__ half8v unpack8_n79(uint32_t x) {
+  uint4v w;
+  w[0] = nib_n79(x << 4);
+  w[1] = nib_n79(x);
+  w[2] = nib_n79(x >> 4);
+  w[3] = nib_n79(x >> 8);
+  return bitcast<half8v>(w);
+}
+
 // Raw buffer descriptor over [base, base + num_bytes): loads at offsets past
 // num_bytes return zero instead of touching memory (gfx9-family raw buffer
 // range check; the fourth descriptor word selects 32-bit data format).

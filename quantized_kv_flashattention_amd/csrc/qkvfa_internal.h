@@ -61,12 +61,31 @@ struct DecodeAppend {
   int64_t n_new;
 };
 
+// Asymmetric group-wise 4-bit rows: unsigned nibble codes in kc/vc (in the
+// cache's K and V row orders) and one parameter word per group of `group`
+// consecutive elements, k_params/v_params [B, Hkv, C, D/group] (fp16 scale in
+// bits 0-15, zero point in bits 16-19); value = scale * (code - zero).  ks/vs
+// are unused.
+struct DecodeAsym {
+  const uint32_t* k_params;
+  const uint32_t* v_params;
+  int group;   // 32, 64 or 128, dividing D
+};
+
 hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
                          const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         const DecodeTail* tail, int bits, hipStream_t stream);
+                         const DecodeTail* tail, int bits, hipStream_t stream,
+                         const DecodeAsym* asym = nullptr);
+
+// Quantize-append of asymmetric group-wise 4-bit K and V rows (codes and
+// parameter words as in DecodeAsym) into cache rows [pos, pos + T).
+hipError_t launch_quantize_append_asym(const float* src, uint8_t* codes, uint32_t* params,
+                                       const float* src2, uint8_t* codes2, uint32_t* params2,
+                                       int64_t BH, int64_t T, int D, int64_t C, int64_t pos, int group,
+                                       hipStream_t stream);
 
 // Quantize-append of K and V rows at 2, 3 or 4 bits (4: launch_quantize_append's
 // arithmetic and layout).

@@ -158,6 +158,104 @@ hipError_t launch_quantize_append_bits(const float* src, uint8_t* codes, uint16_
   return hipGetLastError();
 }
 
+// Asymmetric group-wise rows (TurboAttention §2.3: a scale and a zero point;
+// "Quantized Cross-Attention" §4.1: one scale per group of consecutive
+// elements).  Per group of g elements: lo = min(0, min x), hi = max(0, max x),
+// scale = fp16((hi - lo) / 15), zero = clamp(rint(-lo / scale), 0, 15),
+// code = clamp(rint(x / scale) + zero, 0, 15), all in IEEE fp32; a zero scale
+// gives zero point 0 and zero codes.  The g/8 lanes of a group reduce its
+// range; its first lane writes the parameter word (scale in bits 0-15, zero
+// point in bits 16-19).  Codes are stored in the cache's row orders (the
+// decode reads each matrix-product block from one group): a K row keeps
+// chunk c = 4 k + j (elements 8c .. 8c+7) in dword (D/32) j + k; a V row keeps
+// element 16 p + w in nibble p of dword w (D = 128), or in nibble
+// p + 4 (w / 8) of dword w % 8 (D = 64).
+struct AsymTarget {
+  const float* src;
+  uint8_t* codes;
+  uint32_t* params;
+  int v_order;   // 1: the V row order, 0: the K row order
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_append_asym_kernel(AsymTarget t0, AsymTarget t1, uint32_t nblk,
+                                                                   int64_t T, int64_t C, int64_t pos,
+                                                                   uint32_t tblocks, int lpg) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const bool second = blockIdx.x >= nblk;
+  const uint32_t blk = second ? blockIdx.x - nblk : blockIdx.x;
+  const AsymTarget& tg = second ? t1 : t0;
+  const uint32_t bh = blk / tblocks;
+  const uint32_t tb = blk - bh * tblocks;
+  const int sub = threadIdx.x % TPR;
+  const int64_t t = (int64_t)tb * RPB + threadIdx.x / TPR;
+  if (t >= T) return;  // whole TPR-lane groups leave together
+  const float4* p = reinterpret_cast<const float4*>(tg.src + ((int64_t)bh * T + t) * D) + 2 * sub;
+  const float4 a = p[0];
+  const float4 b = p[1];
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+  for (int o = 1; o < lpg; o <<= 1) {   // the group's lanes are an aligned block of lpg
+    lo = fminf(lo, __shfl_xor(lo, o, TPR));
+    hi = fmaxf(hi, __shfl_xor(hi, o, TPR));
+  }
+  const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
+  const float s = (float)s16;
+  uint32_t packed = 0, z = 0;
+  if (s != 0.0f) {
+    const float zf = fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f);
+    z = (uint32_t)zf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= (uint32_t)fminf(fmaxf(rintf(x[i] / s) + zf, 0.0f), 15.0f) << (4 * i);
+  }
+  const int64_t row = (int64_t)bh * C + pos + t;
+  uint32_t* out = reinterpret_cast<uint32_t*>(tg.codes + row * (D / 2));
+  if (tg.v_order) {
+    // dword sub gathers nibble p from the lane holding element 16 p + sub
+    // (D = 128) or 16 (p % 4) + 8 (p / 4) + sub (D = 64)
+    uint32_t word = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int src = D == 128 ? 2 * p + (sub >> 3) : 2 * (p & 3) + (p >> 2);
+      const int nib = D == 128 ? (sub & 7) : sub;
+      const uint32_t w = (uint32_t)__shfl((int)packed, src, TPR);
+      word |= ((w >> (4 * nib)) & 15u) << (4 * p);
+    }
+    out[sub] = word;
+  } else {
+    out[(D / 32) * (sub & 3) + (sub >> 2)] = packed;   // chunk sub = 4 k + j -> dword (D/32) j + k
+  }
+  if ((sub & (lpg - 1)) == 0) tg.params[row * (D / (8 * lpg)) + sub / lpg] = (uint32_t)bitcast<uint16_t>(s16) | (z << 16);
+}
+
+hipError_t launch_quantize_append_asym(const float* src, uint8_t* codes, uint32_t* params,
+                                       const float* src2, uint8_t* codes2, uint32_t* params2,
+                                       int64_t BH, int64_t T, int D, int64_t C, int64_t pos, int group,
+                                       hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int rpb = 256 / (D / 8);
+  const int64_t tblocks = (T + rpb - 1) / rpb;
+  const int64_t nblk = BH * tblocks;
+  const int ntensors = src2 ? 2 : 1;
+  if (nblk * ntensors > 0x7FFFFFFF || tblocks > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  const AsymTarget t0 = {src, codes, params, 0};
+  const AsymTarget t1 = src2 ? AsymTarget{src2, codes2, params2, 1} : t0;
+  const dim3 grid((uint32_t)(nblk * ntensors));
+  if (D == 128)
+    quantize_append_asym_kernel<128><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, C, pos,
+                                                                     (uint32_t)tblocks, group / 8);
+  else
+    quantize_append_asym_kernel<64><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, C, pos,
+                                                                    (uint32_t)tblocks, group / 8);
+  return hipGetLastError();
+}
+
 // Flush of the INT8 decode buffer (TurboAttention §3.3: a full buffer is
 // compressed to the low-bit cache format): buffered rows [0, T) of every
 // (batch, KV head), dequantized as the fp32 product s8 * code, are quantized

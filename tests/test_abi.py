@@ -48,7 +48,9 @@ def test_every_declared_symbol_is_exported(lib):
                           "qkv_buffer_scale", "qkv_buffer_flush", "qkv_decode_buffered",
                           "qkv_decode_buffered_workspace_bytes", "qkv_prefill",
                           "qkv_quantize_append_kv", "qkv_decode_workspace_bytes",
-                          "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version"}
+                          "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version",
+                          "qkv_quantize_append_kv_bits", "qkv_decode_bits", "qkv_quantize_append_kv_asym",
+                          "qkv_decode_asym"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -283,3 +285,32 @@ def test_lowbit_argument_errors(lib):
     assert db(L=129) == 1
     assert db(ns=2) == 3
     assert b"qkv_decode_bits" in lib.qkv_last_error()
+
+
+def test_asym_argument_errors(lib):
+    i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    lib.qkv_quantize_append_kv_asym.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.qkv_decode_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                    vp, vp, vp, sz, vp]
+    qa = lambda **kw: lib.qkv_quantize_append_kv_asym(P, P, P, kw.get("kp", P), P, P, 1, 1, kw.get("T", 4),
+                                                      kw.get("D", 64), 8, kw.get("pos", 0), kw.get("g", 32), None)
+    assert qa(g=16) == 2
+    assert qa(g=128) == 2        # group larger than the head dim
+    assert qa(g=48) == 2
+    assert qa(D=96) == 2
+    assert qa(pos=5) == 1
+    assert qa(kp=None) == 1
+    assert qa(kp=P + 2) == 1     # parameter words are 4-byte aligned
+    assert qa(T=0) == 0
+    assert b"qkv_quantize_append_kv_asym" in lib.qkv_last_error()
+    da = lambda **kw: lib.qkv_decode_asym(P, P, kw.get("kp", P), P, P, 1, 4, 2, 1, kw.get("L", 100), 128,
+                                          kw.get("D", 128), kw.get("g", 64), 0.1, kw.get("ns", 0), P, None, None, 0,
+                                          None)
+    assert da(g=256) == 2
+    assert da(D=64, g=128) == 2
+    assert da(D=80) == 2
+    assert da(L=129) == 1
+    assert da(kp=None) == 1
+    assert da(kp=P + 2) == 1
+    assert da(ns=2) == 3         # two splits need a workspace
+    assert b"qkv_decode_asym" in lib.qkv_last_error()
