@@ -183,6 +183,41 @@ qkv_status qkv_decode_bits(const uint16_t* q,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Per-head bit widths (TurboAttention, arXiv 2412.08585, §3.2: a layer keeps
+ * some KV heads at 2 bits and the rest at 4).  A layer's cache is split by
+ * width: one cache per width, each holding a subset of the layer's Hkv KV
+ * heads, listed by kv_heads (int32 [Hkv_sub], device, 4-byte aligned; ids
+ * are clamped into [0, Hkv); each KV head of the layer belongs to one cache).
+ *   qkv_quantize_append_kv_heads: quantizes rows [pos, pos + T) of the
+ *     listed heads of k_src, v_src (float [B, Hkv, T, D], device) into a
+ *     b-bit cache of Hkv_sub heads (k_codes, v_codes uint8
+ *     [B, Hkv_sub, C, D*bits/8]; k_scales, v_scales fp16 [B, Hkv_sub, C]);
+ *     cache head i takes source head kv_heads[i].
+ *   qkv_decode_heads: qkv_decode for the query heads of the listed KV heads
+ *     (query head h uses KV head h / (Hq/Hkv) of the layer): q, out, lse are
+ *     the layer's [B, Hq, Sq, D] / [B, Hq, Sq]; only the rows of the listed
+ *     heads' query heads are written.  One call per width covers the layer.
+ *     Workspace: qkv_decode_workspace_bytes(B, (Hq/Hkv)*Hkv_sub, Hkv_sub, Sq,
+ *     kv_len, D, num_splits), same ticket contract as qkv_decode.
+ * Requires bits in {2, 3, 4}, 1 <= Hkv_sub <= Hkv (QKV_ERR_INVALID_ARG
+ * otherwise), and the requirements of the int4 calls.
+ */
+qkv_status qkv_quantize_append_kv_heads(const float* k_src, const float* v_src,
+                                        const int32_t* kv_heads, int64_t Hkv_sub,
+                                        uint8_t* k_codes, uint16_t* k_scales,
+                                        uint8_t* v_codes, uint16_t* v_scales,
+                                        int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                                        int64_t C, int64_t pos, int bits, void* stream);
+qkv_status qkv_decode_heads(const uint16_t* q,
+                            const uint8_t* k_codes, const uint16_t* k_scales,
+                            const uint8_t* v_codes, const uint16_t* v_scales,
+                            const int32_t* kv_heads, int64_t Hkv_sub,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                            int64_t C, int64_t D, int bits, float softmax_scale, int num_splits,
+                            float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Asymmetric group-wise 4-bit rows (TurboAttention, arXiv 2412.08585, §2.3:
  * a scale s and a zero point z per quantization group, value s (code - z);
  * §3.1 keeps asymmetric INT4 groups for K and V; "Quantized Cross-Attention"

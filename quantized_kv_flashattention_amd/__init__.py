@@ -35,6 +35,9 @@ __all__ = [
     "buffer_flush",
     "decode_buffered",
     "decode_buffered_workspace_bytes",
+    "quantize_append_kv_heads",
+    "decode_heads",
+    "decode_mixed",
     "AsymKVCache",
     "quantize_append_kv_asym",
     "decode_asym",
@@ -104,6 +107,12 @@ def _load():
                                 vp, vp, vp]
     lib.qkv_quantize_append_kv_asym.restype = ci
     lib.qkv_quantize_append_kv_asym.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.qkv_quantize_append_kv_heads.restype = ci
+    lib.qkv_quantize_append_kv_heads.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
+                                                 vp]
+    lib.qkv_decode_heads.restype = ci
+    lib.qkv_decode_heads.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                     vp, vp, vp, sz, vp]
     lib.qkv_decode_asym.restype = ci
     lib.qkv_decode_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
                                     vp, vp, vp, sz, vp]
@@ -296,6 +305,85 @@ def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False,
         _check(_lib.qkv_decode_bits(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
                                     C, D, int(bits), _scale(softmax_scale, D), int(num_splits), _ptr(out),
                                     _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def _heads_arg(kv_heads, device):
+    _req(kv_heads, "kv_heads", torch.int32, 1)
+    if kv_heads.device != device:
+        raise ValueError("kv_heads must be on the tensors' device")
+    return kv_heads
+
+
+def quantize_append_kv_heads(k_src: torch.Tensor, v_src: torch.Tensor, cache: "KVCache", kv_heads: torch.Tensor,
+                             pos: int, bits: int = 4):
+    """Quantize rows ``[pos, pos+T)`` of the KV heads ``kv_heads`` (int32, device) of a layer's
+    ``k_src``/``v_src [B, Hkv, T, D]`` into a ``bits``-bit cache holding those heads
+    (cache head i = layer head kv_heads[i])."""
+    _req(k_src, "k_src", torch.float32, 4)
+    _req(v_src, "v_src", torch.float32, 4)
+    if k_src.shape != v_src.shape or k_src.device != v_src.device:
+        raise ValueError("k_src and v_src must have one shape and device")
+    B, Hkv, T, D = k_src.shape
+    kv_heads = _heads_arg(kv_heads, k_src.device)
+    Hs = kv_heads.numel()
+    kc, ks, vc, vs = cache.tensors()
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+        if t.device != k_src.device:
+            raise ValueError("all tensors must be on one device")
+    if kc.shape[:2] != (B, Hs) or kc.shape[3] * 8 != D * bits or vc.shape != kc.shape or \
+            ks.shape != kc.shape[:3] or vs.shape != ks.shape:
+        raise ValueError("cache shape does not match src and kv_heads")
+    _check(_lib.qkv_quantize_append_kv_heads(_ptr(k_src), _ptr(v_src), _ptr(kv_heads), Hs, _ptr(kc), _ptr(ks),
+                                             _ptr(vc), _ptr(vs), B, Hkv, T, D, kc.shape[2], int(pos), int(bits),
+                                             _stream(k_src)))
+
+
+def decode_heads(q, cache: "KVCache", kv_heads: torch.Tensor, Hkv: int, kv_len, out, lse=None, softmax_scale=None,
+                 num_splits=0, workspace=None, bits=4):
+    """Decode for the query heads of the layer's KV heads ``kv_heads`` (int32, device) over a
+    ``bits``-bit cache holding those heads; writes their rows of ``out`` (and ``lse``) only.
+    ``q``/``out`` are the layer's ``[B, Hq, Sq, D]``; ``Hkv`` is the layer's KV head count."""
+    _req(q, "q", torch.bfloat16, 4)
+    B, Hq, Sq, D = q.shape
+    kv_heads = _heads_arg(kv_heads, q.device)
+    Hs = kv_heads.numel()
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    tensors = cache.tensors()
+    kc, ks, vc, vs = tensors
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    if kc.shape[:2] != (B, Hs) or kc.shape[3] * 8 != D * bits or vc.shape != kc.shape or \
+            ks.shape != kc.shape[:3] or vs.shape != ks.shape:
+        raise ValueError("cache shape does not match q and kv_heads")
+    out, lse = _outputs(q, out, lse, False)
+    G = Hq // Hkv
+    need = decode_workspace_bytes(B, G * Hs, Hs, Sq, kv_len, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, B * Hs, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.qkv_decode_heads(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), _ptr(kv_heads), Hs, B, Hq, Hkv,
+                                 Sq, int(kv_len), kc.shape[2], D, int(bits), _scale(softmax_scale, D),
+                                 int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_mixed(q, parts, Hkv: int, kv_len, softmax_scale=None, num_splits=0, return_lse=False, out=None,
+                 lse=None):
+    """Decode of a layer whose KV heads are kept at different widths: ``parts`` is a list of
+    ``(cache, kv_heads, bits)``, one per width, whose head lists cover the layer's ``Hkv`` KV
+    heads once (one launch per part, all on the current stream)."""
+    if sum(int(h.numel()) for _, h, _ in parts) != Hkv:
+        raise ValueError("the parts' head lists must cover the layer's KV heads once")
+    out, lse = _outputs(q, out, lse, return_lse)
+    for cache, heads, bits in parts:
+        decode_heads(q, cache, heads, Hkv, kv_len, out, lse, softmax_scale, num_splits, bits=bits)
     return (out, lse) if return_lse else out
 
 

@@ -160,7 +160,8 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
                          void* workspace, size_t workspace_bytes,
                          const qkvfa::DecodeAppend* append, const qkvfa::DecodeVarlen* varlen,
                          void* stream, const char* fn, int bits = 4,
-                         const qkvfa::DecodeAsym* asym = nullptr) {
+                         const qkvfa::DecodeAsym* asym = nullptr, const int32_t* kv_heads = nullptr,
+                         int64_t Hkv_sub = 0) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -169,23 +170,26 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
     return fail(QKV_ERR_UNSUPPORTED, f + ": (Hq/Hkv) * Sq must be <= 64; use qkv_prefill");
   if (num_splits < 0 || num_splits > 1024)
     return fail(QKV_ERR_INVALID_ARG, f + ": num_splits must be in [0, 1024]");
-  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus(),
+  // the KV heads this call's cache holds (all of them without a head map)
+  const int64_t Hc = kv_heads ? Hkv_sub : Hkv;
+  const int64_t rows = B * Hc * (Hq / Hkv) * Sq;
+  const qkvfa::DecodePlan plan = qkvfa::plan_decode(B, Hc, rows, kv_len, (int)D, num_splits, current_cus(),
                                                      varlen != nullptr && varlen->kv_lens != nullptr);
-  // one-dimensional grid: (splits x B x Hkv) workgroups of up to 512 threads,
+  // one-dimensional grid: (splits x B x heads) workgroups of up to 512 threads,
   // whose thread count must fit 32 bits
-  if ((int64_t)plan.n_split * B * Hkv > ((int64_t)1 << 32) / 512)
+  if ((int64_t)plan.n_split * B * Hc > ((int64_t)1 << 32) / 512)
     return fail(QKV_ERR_UNSUPPORTED, f + ": too many workgroups (num_splits * B * Hkv)");
-  const size_t need = qkvfa::decode_workspace_bytes(B * Hq * Sq, B * Hkv, (int)D, plan.n_split);
+  const size_t need = qkvfa::decode_workspace_bytes(rows, B * Hc, (int)D, plan.n_split);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(QKV_ERR_WORKSPACE, f + ": workspace smaller than qkv_decode_workspace_bytes()");
     if (!aligned(workspace, 16))
       return fail(QKV_ERR_INVALID_ARG, f + ": workspace must be 16-byte aligned");
   }
-  return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
+  return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hc, Sq,
                                          kv_len, varlen ? varlen->page_size : C, (int)D,
                                          softmax_scale, plan, out, lse, workspace, append, varlen,
-                                         nullptr, bits, static_cast<hipStream_t>(stream), asym),
+                                         nullptr, bits, static_cast<hipStream_t>(stream), asym, kv_heads, Hkv),
                     fn);
 }
 
@@ -284,6 +288,47 @@ qkv_status qkv_decode_asym(const uint16_t* q, const uint8_t* k_codes, const uint
                        reinterpret_cast<const uint16_t*>(v_params), B, Hq, Hkv, Sq, kv_len, C, D,
                        softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr, nullptr,
                        stream, "qkv_decode_asym", 4, &asym);
+}
+
+qkv_status qkv_quantize_append_kv_heads(const float* k_src, const float* v_src, const int32_t* kv_heads,
+                                        int64_t Hkv_sub, uint8_t* k_codes, uint16_t* k_scales,
+                                        uint8_t* v_codes, uint16_t* v_scales, int64_t B, int64_t Hkv,
+                                        int64_t T, int64_t D, int64_t C, int64_t pos, int bits, void* stream) {
+  const char* fn = "qkv_quantize_append_kv_heads";
+  const std::string f(fn);
+  if (bits != 2 && bits != 3 && bits != 4) return fail(QKV_ERR_UNSUPPORTED, f + ": bits must be 2, 3 or 4");
+  if (B < 1 || Hkv < 1 || T < 0 || C < 1)
+    return fail(QKV_ERR_INVALID_ARG, f + ": need B, Hkv, C >= 1 and T >= 0");
+  if (Hkv_sub < 1 || Hkv_sub > Hkv) return fail(QKV_ERR_INVALID_ARG, f + ": need 1 <= Hkv_sub <= Hkv");
+  if (D != 64 && D != 128) return fail(QKV_ERR_UNSUPPORTED, f + ": head dim must be 64 or 128");
+  if (pos < 0 || pos + T > C) return fail(QKV_ERR_INVALID_ARG, f + ": need 0 <= pos and pos + T <= C");
+  if (T == 0) return QKV_OK;
+  if (!k_src || !v_src || !kv_heads || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(QKV_ERR_INVALID_ARG, f + ": null pointer");
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 2) || !aligned(v_scales, 2) || !aligned(kv_heads, 4))
+    return fail(QKV_ERR_INVALID_ARG, f + ": misaligned pointer");
+  if (B * Hkv > 0x3FFFFFFFll) return fail(QKV_ERR_UNSUPPORTED, f + ": B * Hkv too large");
+  return hip_status(qkvfa::launch_quantize_append_bits(k_src, k_codes, k_scales, v_src, v_codes, v_scales,
+                                                       B * Hkv_sub, T, (int)D, C, pos, bits,
+                                                       static_cast<hipStream_t>(stream), kv_heads, (int)Hkv_sub,
+                                                       (int)Hkv),
+                    fn);
+}
+
+qkv_status qkv_decode_heads(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                            const uint8_t* v_codes, const uint16_t* v_scales, const int32_t* kv_heads,
+                            int64_t Hkv_sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                            int64_t C, int64_t D, int bits, float softmax_scale, int num_splits, float* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (bits != 2 && bits != 3 && bits != 4)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_decode_heads: bits must be 2, 3 or 4");
+  if (Hkv_sub < 1 || Hkv_sub > Hkv) return fail(QKV_ERR_INVALID_ARG, "qkv_decode_heads: need 1 <= Hkv_sub <= Hkv");
+  if (!kv_heads || !aligned(kv_heads, 4))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_decode_heads: null or misaligned kv_heads");
+  return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
+                       num_splits, out, lse, workspace, workspace_bytes, nullptr, nullptr, stream,
+                       "qkv_decode_heads", bits, nullptr, kv_heads, Hkv_sub);
 }
 
 qkv_status qkv_decode_append(const uint16_t* q, const float* k_new, const float* v_new,

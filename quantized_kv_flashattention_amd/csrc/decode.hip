@@ -124,6 +124,10 @@ struct DecodeArgs {
   const uint32_t* kp;
   const uint32_t* vp;
   int ng, gshift;
+  // head map (kv_heads != nullptr): KV head g of this call's cache is KV head
+  // kv_heads[g] of a layer with Hkv_all KV heads (Hq, G count the layer)
+  const int32_t* kv_heads;
+  int Hkv_all;
   // INT8 decode buffer (tail_rows > 0): the last split attends buffered rows
   // [0, tail_rows) of tk/tv [B, Hkv, buf_rows, D] after the kv_len cache
   // rows the other splits attend; rows [tail_len, tail_rows) are the call's
@@ -253,6 +257,10 @@ void decode_kernel(const DecodeArgs a) {
   const int g = unit % a.Hkv;
   const int b = unit / a.Hkv;
   const int G = a.G, Sq = a.Sq;
+  // head map: this call's cache holds KV heads kv_heads[0 .. Hkv) of a layer
+  // of Hkv_all KV heads (ids clamped into range); their query rows are
+  // written, other rows of q / out / lse are not touched
+  const int gq = a.kv_heads ? min(max(__builtin_amdgcn_readfirstlane(a.kv_heads[g]), 0), a.Hkv_all - 1) : g;
   const int R = G * Sq;
   const int rows_o = min(16, R);   // rows per wave in the merge buffer
   const bool append = a.k_new != nullptr;
@@ -264,9 +272,12 @@ void decode_kernel(const DecodeArgs a) {
     pos_b = lb;
     L_b = lb + (append ? a.n_new : 0);
   }
-  // Query row `row` of this group (head g G + row / Sq, position row % Sq)
-  // is row grow0 + row of q, out and lse: heads of a group are adjacent.
-  const int64_t grow0 = ((int64_t)b * a.Hq + (int64_t)g * G) * Sq;
+  // Query row `row` of this group (head gq G + row / Sq, position row % Sq)
+  // is row grow0 + row of q, out and lse: heads of a group are adjacent.  Its
+  // split partials are row prow0 + row of the workspace, which numbers the
+  // rows of this call's (batch, KV head) units only (= grow0 without a map).
+  const int64_t grow0 = ((int64_t)b * a.Hq + (int64_t)gq * G) * Sq;
+  const int64_t prow0 = ((int64_t)b * a.Hkv + g) * G * Sq;
   const int t_begin = split * a.split_len;
   const int t_end = min(L_b, t_begin + a.split_len);   // <= t_begin: nothing to attend here
 
@@ -351,7 +362,7 @@ void decode_kernel(const DecodeArgs a) {
                    : float4v{0.f, 0.f, 0.f, 0.f};
     };
     auto item_off = [&](int idx) -> uint32_t {
-      return (uint32_t)((item_grow(idx) * n_split * D + 4 * (idx % (D / 4))) * 4);
+      return (uint32_t)(((prow0 + idx / (D / 4)) * n_split * D + 4 * (idx % (D / 4))) * 4);
     };
     // (0) the partial outputs of this thread's first item (first kPre splits),
     //     issued now: their round trip overlaps the LSE loads'
@@ -377,8 +388,7 @@ void decode_kernel(const DecodeArgs a) {
           v[u] = -INFINITY;
           if (idx < total) {
             const int row = idx / n_live;
-            const int64_t grow = grow0 + row;
-            v[u] = __hip_atomic_load(a.part_lse + grow * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
+            v[u] = __hip_atomic_load(a.part_lse + (prow0 + row) * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
           }
         }
@@ -1026,9 +1036,10 @@ void decode_kernel(const DecodeArgs a) {
         } else {
           // device-coherent stores (sc1): visible to every XCD without an L2 writeback
           __builtin_amdgcn_raw_buffer_store_b128(
-              acc * inv, rpart, (uint32_t)(((grow * a.n_split + split) * D + d) * 4), 0, kCoherent);
+              acc * inv, rpart, (uint32_t)((((prow0 + nb * 16 + rr) * a.n_split + split) * D + d) * 4), 0,
+              kCoherent);
           if (d == 0)   // log2 units
-            __hip_atomic_store(a.part_lse + grow * a.n_split + split, lse2, __ATOMIC_RELAXED,
+            __hip_atomic_store(a.part_lse + (prow0 + nb * 16 + rr) * a.n_split + split, lse2, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -1134,10 +1145,11 @@ void decode_kernel(const DecodeArgs a) {
         *reinterpret_cast<float4v*>(a.out + grow * D + d) = o;
         if (d == 0 && a.lse) a.lse[grow] = lse2 * kLn2;
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(o, rpart, (uint32_t)(((grow * a.n_split + split) * D + d) * 4), 0,
+        const int64_t prow = prow0 + r;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rpart, (uint32_t)(((prow * a.n_split + split) * D + d) * 4), 0,
                                                kCoherent);
         if (d == 0)
-          __hip_atomic_store(a.part_lse + grow * a.n_split + split, lse2, __ATOMIC_RELAXED,
+          __hip_atomic_store(a.part_lse + prow * a.n_split + split, lse2, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -1262,8 +1274,11 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
-                         const DecodeTail* tail, int bits, hipStream_t stream, const DecodeAsym* asym) {
+                         const DecodeTail* tail, int bits, hipStream_t stream, const DecodeAsym* asym,
+                         const int32_t* kv_heads, int64_t Hkv_all) {
   DecodeArgs a;
+  a.kv_heads = kv_heads;
+  a.Hkv_all = (int)(kv_heads ? Hkv_all : Hkv);
   a.q = q; a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.kp = nullptr; a.vp = nullptr; a.ng = 1; a.gshift = 0;
   if (asym) {
@@ -1308,7 +1323,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
   }
   a.part_o = nullptr; a.part_lse = nullptr; a.tickets = nullptr; a.part_bytes = 0;
   if (plan.n_split > 1) {
-    const int64_t rows = B * Hq * Sq;
+    const int64_t rows = B * Hkv * (Hq / a.Hkv_all) * Sq;   // this call's query rows
     char* w = static_cast<char*>(workspace);
     const size_t t = align256((size_t)B * Hkv * sizeof(uint32_t));
     const size_t o = align256((size_t)rows * plan.n_split * D * sizeof(float));
@@ -1318,7 +1333,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
     a.part_bytes = (int)((size_t)rows * plan.n_split * D * sizeof(float));
   }
   a.C = C;
-  a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv); a.Sq = (int)Sq; a.kv_len = (int)kv_len;
+  a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / a.Hkv_all); a.Sq = (int)Sq; a.kv_len = (int)kv_len;
   a.split_len = plan.split_len; a.n_split = plan.n_split;
   a.qk_log2 = softmax_scale * kLog2e;
   if (D == 128) return launch_d<128>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);

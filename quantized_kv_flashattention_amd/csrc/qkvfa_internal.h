@@ -8,10 +8,14 @@
 namespace qkvfa {
 
 // Quantize one tensor (src2 == nullptr) or two tensors of the same shape in one launch.
+// Head map (heads != nullptr): the cache holds h_cache heads per batch entry,
+// and cache head h takes the source rows of head heads[h] of the h_src heads
+// per batch entry of src (BH = B * h_cache).
 hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,
                                   const float* src2, uint8_t* codes2, uint16_t* scales2,
                                   int64_t BH, int64_t T, int D, int64_t C, int64_t pos,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const int32_t* heads = nullptr, int h_cache = 0,
+                                  int h_src = 0);
 
 struct DecodePlan {
   int n_split;     // number of KV ranges
@@ -78,7 +82,8 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
                          const DecodeTail* tail, int bits, hipStream_t stream,
-                         const DecodeAsym* asym = nullptr);
+                         const DecodeAsym* asym = nullptr, const int32_t* kv_heads = nullptr,
+                         int64_t Hkv_all = 0);
 
 // Quantize-append of asymmetric group-wise 4-bit K and V rows (codes and
 // parameter words as in DecodeAsym) into cache rows [pos, pos + T).
@@ -92,7 +97,8 @@ hipError_t launch_quantize_append_asym(const float* src, uint8_t* codes, uint32_
 hipError_t launch_quantize_append_bits(const float* src, uint8_t* codes, uint16_t* scales,
                                        const float* src2, uint8_t* codes2, uint16_t* scales2,
                                        int64_t BH, int64_t T, int D, int64_t C, int64_t pos, int bits,
-                                       hipStream_t stream);
+                                       hipStream_t stream, const int32_t* heads = nullptr, int h_cache = 0,
+                                       int h_src = 0);
 
 hipError_t launch_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scales, float* k_s8, float* v_s8,
                                int64_t BH, int64_t L, int64_t C, hipStream_t stream);

@@ -28,7 +28,19 @@ struct QuantTarget {
   const float* src;
   uint8_t* codes;
   uint16_t* scales;
+  // head map (heads != nullptr): cache head h of the h_cache heads per batch
+  // entry takes the source rows of head heads[h] of h_src (ids clamped)
+  const int32_t* heads;
+  int h_cache, h_src;
 };
+
+// Row index of (batch x cache head) bh in the source tensor.
+__device__ __forceinline__ int64_t src_bh(const QuantTarget& t, uint32_t bh) {
+  if (t.heads == nullptr) return bh;
+  const int64_t b = bh / (uint32_t)t.h_cache;
+  const int h = (int)(bh - b * t.h_cache);
+  return b * t.h_src + min(max(t.heads[h], 0), t.h_src - 1);
+}
 
 // The TPR = D/8 lanes of one row, each holding 8 consecutive elements x:
 // the row's absmax (cross-lane), its fp16 scale, and this lane's dword of codes.
@@ -60,16 +72,17 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantTarget t0, Qu
   constexpr int RPB = 256 / TPR;      // rows per block
   const bool second = blockIdx.x >= nblk;
   const uint32_t blk = second ? blockIdx.x - nblk : blockIdx.x;
-  const float* __restrict__ src = second ? t1.src : t0.src;
-  uint8_t* __restrict__ codes = second ? t1.codes : t0.codes;
-  uint16_t* __restrict__ scales = second ? t1.scales : t0.scales;
+  const QuantTarget& tg = second ? t1 : t0;
+  const float* __restrict__ src = tg.src;
+  uint8_t* __restrict__ codes = tg.codes;
+  uint16_t* __restrict__ scales = tg.scales;
   const uint32_t bh = blk / tblocks;
   const uint32_t tb = blk - bh * tblocks;
   const int sub = threadIdx.x % TPR;
   const int64_t t = (int64_t)tb * RPB + threadIdx.x / TPR;
   if (t >= T) return;  // whole TPR-lane groups leave together
 
-  const float4* p = reinterpret_cast<const float4*>(src + ((int64_t)bh * T + t) * D) + 2 * sub;
+  const float4* p = reinterpret_cast<const float4*>(src + (src_bh(tg, bh) * T + t) * D) + 2 * sub;
   const float4 a = p[0];
   const float4 b = p[1];
   const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(256) void quantize_append_lowbit_kernel(QuantTarget
   const int sub = threadIdx.x % TPR;
   const int64_t t = (int64_t)tb * RPB + threadIdx.x / TPR;
   if (t >= T) return;  // whole TPR-lane groups leave together
-  const float4* p = reinterpret_cast<const float4*>(tg.src + ((int64_t)bh * T + t) * D) + 2 * sub;
+  const float4* p = reinterpret_cast<const float4*>(tg.src + (src_bh(tg, bh) * T + t) * D) + 2 * sub;
   const float4 a = p[0];
   const float4 b = p[1];
   const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -134,17 +147,18 @@ __global__ __launch_bounds__(256) void quantize_append_lowbit_kernel(QuantTarget
 hipError_t launch_quantize_append_bits(const float* src, uint8_t* codes, uint16_t* scales,
                                        const float* src2, uint8_t* codes2, uint16_t* scales2,
                                        int64_t BH, int64_t T, int D, int64_t C, int64_t pos, int bits,
-                                       hipStream_t stream) {
+                                       hipStream_t stream, const int32_t* heads, int h_cache, int h_src) {
   if (bits == 4)
-    return launch_quantize_append(src, codes, scales, src2, codes2, scales2, BH, T, D, C, pos, stream);
+    return launch_quantize_append(src, codes, scales, src2, codes2, scales2, BH, T, D, C, pos, stream, heads,
+                                  h_cache, h_src);
   if (T == 0) return hipSuccess;
   const int rpb = 256 / (D / 8);
   const int64_t tblocks = (T + rpb - 1) / rpb;
   const int64_t nblk = BH * tblocks;
   const int ntensors = src2 ? 2 : 1;
   if (nblk * ntensors > 0x7FFFFFFF || tblocks > 0xFFFFFFFFll) return hipErrorInvalidValue;
-  const QuantTarget t0 = {src, codes, scales};
-  const QuantTarget t1 = src2 ? QuantTarget{src2, codes2, scales2} : t0;
+  const QuantTarget t0 = {src, codes, scales, heads, h_cache, h_src};
+  const QuantTarget t1 = src2 ? QuantTarget{src2, codes2, scales2, heads, h_cache, h_src} : t0;
   const dim3 grid((uint32_t)(nblk * ntensors));
   const uint32_t nb = (uint32_t)nblk, tbk = (uint32_t)tblocks;
   if (D == 128 && bits == 2)
@@ -361,15 +375,15 @@ hipError_t launch_buffer_scale(const uint16_t* k_scales, const uint16_t* v_scale
 hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* scales,
                                   const float* src2, uint8_t* codes2, uint16_t* scales2,
                                   int64_t BH, int64_t T, int D, int64_t C, int64_t pos,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const int32_t* heads, int h_cache, int h_src) {
   if (T == 0) return hipSuccess;
   const int rpb = 256 / (D / 8);
   const int64_t tblocks = (T + rpb - 1) / rpb;
   const int64_t nblk = BH * tblocks;
   const int ntensors = src2 ? 2 : 1;
   if (nblk * ntensors > 0x7FFFFFFF || tblocks > 0xFFFFFFFFll) return hipErrorInvalidValue;
-  const QuantTarget t0 = {src, codes, scales};
-  const QuantTarget t1 = src2 ? QuantTarget{src2, codes2, scales2} : t0;
+  const QuantTarget t0 = {src, codes, scales, heads, h_cache, h_src};
+  const QuantTarget t1 = src2 ? QuantTarget{src2, codes2, scales2, heads, h_cache, h_src} : t0;
   const dim3 grid((uint32_t)(nblk * ntensors));
   if (D == 128) {
     quantize_append_kernel<128><<<grid, dim3(256), 0, stream>>>(t0, t1, (uint32_t)nblk, T, C, pos,

@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "qkv_quantize_append_kv", "qkv_decode_workspace_bytes",
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version",
                           "qkv_quantize_append_kv_bits", "qkv_decode_bits", "qkv_quantize_append_kv_asym",
-                          "qkv_decode_asym"}
+                          "qkv_decode_asym", "qkv_quantize_append_kv_heads", "qkv_decode_heads"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -314,3 +314,32 @@ def test_asym_argument_errors(lib):
     assert da(kp=P + 2) == 1
     assert da(ns=2) == 3         # two splits need a workspace
     assert b"qkv_decode_asym" in lib.qkv_last_error()
+
+
+def test_head_map_argument_errors(lib):
+    i64, vp, f32, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    lib.qkv_quantize_append_kv_heads.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
+                                                 vp]
+    lib.qkv_decode_heads.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                     vp, vp, vp, sz, vp]
+    qh = lambda **kw: lib.qkv_quantize_append_kv_heads(P, P, kw.get("heads", P), kw.get("hs", 2), P, P, P, P, 1,
+                                                       kw.get("H", 4), kw.get("T", 4), 64, 8, kw.get("pos", 0),
+                                                       kw.get("bits", 4), None)
+    assert qh(bits=5) == 2
+    assert qh(hs=0) == 1
+    assert qh(hs=5) == 1          # more heads than the layer has
+    assert qh(heads=None) == 1
+    assert qh(heads=P + 2) == 1
+    assert qh(pos=6) == 1
+    assert qh(T=0) == 0
+    assert b"qkv_quantize_append_kv_heads" in lib.qkv_last_error()
+    dh = lambda **kw: lib.qkv_decode_heads(P, P, P, P, P, kw.get("heads", P), kw.get("hs", 2), 1, 8, 4, 1,
+                                           kw.get("L", 100), 128, 128, kw.get("bits", 2), 0.1, kw.get("ns", 0), P,
+                                           None, None, 0, None)
+    assert dh(bits=1) == 2
+    assert dh(hs=0) == 1
+    assert dh(hs=5) == 1
+    assert dh(heads=None) == 1
+    assert dh(L=129) == 1
+    assert dh(ns=2) == 3
+    assert b"qkv_decode_heads" in lib.qkv_last_error()
