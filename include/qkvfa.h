@@ -407,6 +407,17 @@ qkv_status qkv_prefill(const uint16_t* q,
                        int64_t C, int64_t D, float softmax_scale, int causal,
                        float* out, float* lse, void* stream);
 
+/* qkv_prefill over b-bit rows (the 2/3-bit layout of qkv_decode_bits; bits =
+ * 4 is qkv_prefill).  Codes are converted exactly once per key tile and
+ * workgroup, as for int4.  Requires bits in {2, 3, 4} (QKV_ERR_UNSUPPORTED
+ * otherwise) and the qkv_prefill requirements. */
+qkv_status qkv_prefill_bits(const uint16_t* q,
+                            const uint8_t* k_codes, const uint16_t* k_scales,
+                            const uint8_t* v_codes, const uint16_t* v_scales,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                            int64_t C, int64_t D, int bits, float softmax_scale, int causal,
+                            float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -113,6 +113,8 @@ def _load():
     lib.qkv_decode_heads.restype = ci
     lib.qkv_decode_heads.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
                                      vp, vp, vp, sz, vp]
+    lib.qkv_prefill_bits.restype = ci
+    lib.qkv_prefill_bits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
     lib.qkv_decode_asym.restype = ci
     lib.qkv_decode_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
                                     vp, vp, vp, sz, vp]
@@ -659,13 +661,19 @@ def decode_buffered(q, cache, kv_len, buf: "DecodeBuffer", k_new=None, v_new=Non
     return (out, lse) if return_lse else out
 
 
-def prefill(q, cache, kv_len, causal, softmax_scale=None, return_lse=False, out=None, lse=None):
-    """Prefill attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)``."""
+def prefill(q, cache, kv_len, causal, softmax_scale=None, return_lse=False, out=None, lse=None, bits=4):
+    """Prefill attention of ``q [B, Hq, Sq, D]`` over cache rows ``[0, kv_len)``;
+    ``bits`` = 2, 3 or 4 is the width of the cache's codes."""
     tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
-    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len)
+    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len, bits)
     out, lse = _outputs(q, out, lse, return_lse)
     kc, ks, vc, vs = tensors
-    _check(_lib.qkv_prefill(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
-                            C, D, _scale(softmax_scale, D), int(bool(causal)), _ptr(out), _ptr(lse),
-                            _stream(q)))
+    if bits == 4:
+        _check(_lib.qkv_prefill(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                                C, D, _scale(softmax_scale, D), int(bool(causal)), _ptr(out), _ptr(lse),
+                                _stream(q)))
+    else:
+        _check(_lib.qkv_prefill_bits(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                                     C, D, int(bits), _scale(softmax_scale, D), int(bool(causal)), _ptr(out),
+                                     _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out

@@ -511,24 +511,44 @@ qkv_status qkv_decode_buffered(const uint16_t* q, const float* k_new, const floa
                     "qkv_decode_buffered");
 }
 
+static qkv_status prefill_common(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                                 const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                                 int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
+                                 float softmax_scale, int causal, float* out, float* lse, void* stream, int bits,
+                                 const char* fn) {
+  const std::string f(fn);
+  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
+                                  C, D, out, lse, fn);
+  if (st != QKV_OK) return st;
+  if (causal != 0 && causal != 1) return fail(QKV_ERR_INVALID_ARG, f + ": causal must be 0 or 1");
+  if (causal && Sq > kv_len)
+    return fail(QKV_ERR_INVALID_ARG, f + ": causal attention needs Sq <= kv_len");
+  if ((Sq + 127) / 128 > 0xFFFF)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": too many query blocks");
+  if (kv_len * (D * bits / 8) > 0x7FFFFFFFll)
+    return fail(QKV_ERR_UNSUPPORTED, f + ": kv_len * D * bits / 8 must stay below 2^31 bytes");
+  return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
+                                          kv_len, C, (int)D, softmax_scale, causal, out, lse,
+                                          static_cast<hipStream_t>(stream), bits),
+                    fn);
+}
+
 qkv_status qkv_prefill(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
                        const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
                        int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
                        float softmax_scale, int causal, float* out, float* lse, void* stream) {
-  qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
-                                  C, D, out, lse, "qkv_prefill");
-  if (st != QKV_OK) return st;
-  if (causal != 0 && causal != 1) return fail(QKV_ERR_INVALID_ARG, "qkv_prefill: causal must be 0 or 1");
-  if (causal && Sq > kv_len)
-    return fail(QKV_ERR_INVALID_ARG, "qkv_prefill: causal attention needs Sq <= kv_len");
-  if ((Sq + 127) / 128 > 0xFFFF)
-    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill: too many query blocks");
-  if (kv_len * (D / 2) > 0x7FFFFFFFll)
-    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill: kv_len * D / 2 must stay below 2^31 bytes");
-  return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
-                                          kv_len, C, (int)D, softmax_scale, causal, out, lse,
-                                          static_cast<hipStream_t>(stream)),
-                    "qkv_prefill");
+  return prefill_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
+                        causal, out, lse, stream, 4, "qkv_prefill");
+}
+
+qkv_status qkv_prefill_bits(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                            const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D, int bits,
+                            float softmax_scale, int causal, float* out, float* lse, void* stream) {
+  if (bits != 2 && bits != 3 && bits != 4)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill_bits: bits must be 2, 3 or 4");
+  return prefill_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
+                        causal, out, lse, stream, bits, "qkv_prefill_bits");
 }
 
 }  // extern "C"

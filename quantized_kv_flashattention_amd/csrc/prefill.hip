@@ -94,7 +94,7 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
   return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, int BITS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
@@ -104,12 +104,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int KS = D / 16;   // QK k-steps
   constexpr int NDB = D / 32;  // PV output blocks
   constexpr int NCH = D / 8;   // K chunk planes
-  constexpr int ROWB = D / 2;  // bytes per packed row
+  constexpr int ROWB = D * BITS / 8;  // bytes per packed row (R: 4-bit nibbles; 2/3 bits: bit planes)
   constexpr int KPL = BN * 8;  // halves per K chunk plane
   constexpr int VPL = D * 8;   // halves per V 8-token plane
   constexpr int KBUF = NCH * KPL;
   constexpr int VBUF = 8 * VPL;
-  constexpr int KDW = ROWB / (4 * NW);   // K code dwords per thread and tile
+  constexpr int KDW = D / (8 * NW);      // K chunks of 8 codes per thread and tile (one int4 dword each)
   constexpr int VT = D / (8 * NW);       // V tokens (x one code dword) per thread
   static_assert(KDW >= 1 && KDW <= 4 && (VT == 2 || VT == 4), "unsupported D / NW");
 
@@ -180,7 +180,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // dims) per thread, mapped so that every conversion write instruction of a
   // wave covers distinct banks.  Scales: wave 0 lane t loads the K scale of
   // token t, wave 1 the V scale.
-  const uint32_t k_voff = (uint32_t)(lane * ROWB + wave * (ROWB / NW));
+  // (2/3 bits: the chunks' low-bit bytes, 2 per chunk, and top-bit bytes, 1 per chunk at D/4)
+  const uint32_t k_voff = (uint32_t)(lane * ROWB + wave * (BITS == 4 ? ROWB / NW : 2 * KDW));
+  const uint32_t k_toff = (uint32_t)(lane * ROWB + D / 4 + wave * KDW);
   int v_dp, v_tok0;
   if constexpr (D == 128 && NW == 4) {
     const int t = lane >> 4;
@@ -195,7 +197,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     v_dp = lane & 7;
     v_tok0 = 2 * (8 * wave + (lane >> 3));
   }
-  const uint32_t v_voff = (uint32_t)(v_tok0 * ROWB + 4 * v_dp);
+  const uint32_t v_voff = (uint32_t)(v_tok0 * ROWB + (BITS == 4 ? 4 : 2) * v_dp);
+  const uint32_t v_toff = (uint32_t)(v_tok0 * ROWB + D / 4 + v_dp);
   // V store position: plane P and half h of the token unit, row slot base.
   int v_st;
   {
@@ -210,10 +213,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   uint32_t kw[KDW];
   uint32_t vw[VT];
+  uint32_t ktop = 0;        // 3 bits: the K chunks' top-bit bytes
+  uint32_t vt[VT] = {};     // 3 bits: the V tokens' top-bit bytes
   uint16_t sc = 0;
 
   auto load_tile = [&](int t0) {
     const int so = t0 * ROWB;
+    if constexpr (BITS != 4) {
+      // chunk i's low bits in bits 16 (i % 2) of kw[i / 2]; V tokens' in bits 0-15
+      if constexpr (KDW == 4) {
+        const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, k_voff, so, 0);
+        kw[0] = w[0];
+        kw[1] = w[1];
+        if constexpr (BITS == 3) ktop = __builtin_amdgcn_raw_buffer_load_b32(rk, k_toff, so, 0);
+      } else {
+        kw[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, k_voff, so, 0);
+        if constexpr (BITS == 3) ktop = __builtin_amdgcn_raw_buffer_load_b16(rk, k_toff, so, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VT; ++i) {
+        vw[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, v_voff + i * ROWB, so, 0);
+        if constexpr (BITS == 3) vt[i] = __builtin_amdgcn_raw_buffer_load_b8(rv, v_toff + i * ROWB, so, 0);
+      }
+      if (wave < 2) sc = __builtin_amdgcn_raw_buffer_load_b16(rsc, (uint32_t)(lane * 2), t0 * 2, 0);
+      return;
+    }
     if constexpr (KDW == 4) {
       const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff, so, 0);
 #pragma unroll
@@ -238,15 +262,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int i = 0; i < KDW; ++i) {
       const int c = KDW * wave + i;
-      *reinterpret_cast<half8v*>(sk_ + c * KPL + lane * 8) = unpack8_perm(kw[i]);
+      half8v kop;
+      if constexpr (BITS == 4)
+        kop = unpack8_perm(kw[i]);
+      else
+        kop = unpack8_lowbit<BITS>(kw[i >> 1] >> (16 * (i & 1)), (ktop >> (8 * i)) & 0xFFu);
+      *reinterpret_cast<half8v*>(sk_ + c * KPL + lane * 8) = kop;
     }
+    // V element n of tokens (0, 1) [and (2, 3)] -> exact fp16 pair
+    auto vpair = [&](int t, int n) -> half2v {
+      if constexpr (BITS == 4)
+        return nib_pair2(vw[t], vw[t + 1], n);
+      else
+        return lowbit_pair2<BITS>(vw[t], vw[t + 1], vt[t], vt[t + 1], n);
+    };
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       // row slot (8 v_dp + n) ^ sig = v_st's slot with n xor-ed into bits 0-2
       _Float16* dst = sv_ + (v_st ^ (n * 8));
-      const half2v a = nib_pair2(vw[0], vw[1], n);
+      const half2v a = vpair(0, n);
       if constexpr (VT == 4) {
-        const half2v c = nib_pair2(vw[2], vw[3], n);
+        const half2v c = vpair(2, n);
         const uint2v w = {bitcast<uint32_t>(a), bitcast<uint32_t>(c)};
         *reinterpret_cast<uint2v*>(dst) = w;
       } else {
@@ -440,18 +476,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+template <int D, int NW, bool CAUSAL, int BITS>
+hipError_t launch1(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
+                   const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                   int64_t kv_len, int64_t C, float qk_log2, float* out, float* lse,
+                   hipStream_t stream) {
+  constexpr int BM = 32 * NW;
+  const int nqb = (int)((Sq + BM - 1) / BM);
+  dim3 grid((uint32_t)Hq, (uint32_t)nqb, (uint32_t)B);
+  prefill_kernel<D, NW, CAUSAL, BITS><<<grid, dim3(64 * NW), 0, stream>>>(
+      q, kc, ks, vc, vs, (int)Hq, (int)Hkv, (int)(Hq / Hkv), (int)Sq, (int)kv_len, C, qk_log2, nqb,
+      out, lse);
+  return hipGetLastError();
+}
+
 template <int D, int NW, bool CAUSAL>
 hipError_t launch(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
                   const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                   int64_t kv_len, int64_t C, float qk_log2, float* out, float* lse,
-                  hipStream_t stream) {
-  constexpr int BM = 32 * NW;
-  const int nqb = (int)((Sq + BM - 1) / BM);
-  dim3 grid((uint32_t)Hq, (uint32_t)nqb, (uint32_t)B);
-  prefill_kernel<D, NW, CAUSAL><<<grid, dim3(64 * NW), 0, stream>>>(
-      q, kc, ks, vc, vs, (int)Hq, (int)Hkv, (int)(Hq / Hkv), (int)Sq, (int)kv_len, C, qk_log2, nqb,
-      out, lse);
-  return hipGetLastError();
+                  hipStream_t stream, int bits) {
+  if (bits == 2)
+    return launch1<D, NW, CAUSAL, 2>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
+  if (bits == 3)
+    return launch1<D, NW, CAUSAL, 3>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
+  return launch1<D, NW, CAUSAL, 4>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
 }
 
 }  // namespace
@@ -460,20 +508,20 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                           float softmax_scale, int causal, float* out, float* lse,
-                          hipStream_t stream) {
+                          hipStream_t stream, int bits) {
   const float qk_log2 = softmax_scale * kLog2e;
   if (D == 128) {
     if (causal)
       return launch<128, 8, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2,
-                                         out, lse, stream);
+                                  out, lse, stream, bits);
     return launch<128, 8, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2,
-                                        out, lse, stream);
+                                 out, lse, stream, bits);
   }
   if (causal)
     return launch<64, 4, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
-                               stream);
+                               stream, bits);
   return launch<64, 4, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
-                              stream);
+                              stream, bits);
 }
 
 }  // namespace qkvfa

@@ -137,6 +137,20 @@ __device__ __forceinline__ half8v unpack8_lowbit(uint32_t lo16, uint32_t top8) {
   return bitcast<half8v>(w);
 }
 
+// Element n (0..7) of eight 2- or 3-bit codes of two tokens a and b -> exact
+// fp16 pair (a's, b's).  lo_a / lo_b: the tokens' two low-bit bytes in bits
+// 0-15; top_a / top_b (3 bits only): their top-bit bytes in bits 0-7.
+template <int BITS>
+__device__ __forceinline__ half2v lowbit_pair2(uint32_t lo_a, uint32_t lo_b, uint32_t top_a, uint32_t top_b, int n) {
+  const uint32_t x = pair_bytes(lo_a, lo_b, n >> 2);
+  if constexpr (BITS == 2) {
+    return b2_pair(x, n & 3);
+  } else {
+    const uint32_t z = pair_bytes(top_a, top_b, 0) >> (4 * (n >> 2));   // elements 4 (n/4) + f at f, 16 + f
+    return b3_pair(x, z, n & 3);
+  }
+}
+
 // ---- Biased conversions (decode).  A code c becomes the exact fp16 value
 // c + b, with a bias b fixed by the code's position in the operand; the
 // kernel takes sum(q b) out of each score (through the accumulator's initial

@@ -112,6 +112,6 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                           float softmax_scale, int causal, float* out, float* lse,
-                          hipStream_t stream);
+                          hipStream_t stream, int bits = 4);
 
 }  // namespace qkvfa

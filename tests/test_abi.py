@@ -50,7 +50,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "qkv_quantize_append_kv", "qkv_decode_workspace_bytes",
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version",
                           "qkv_quantize_append_kv_bits", "qkv_decode_bits", "qkv_quantize_append_kv_asym",
-                          "qkv_decode_asym", "qkv_quantize_append_kv_heads", "qkv_decode_heads"}
+                          "qkv_decode_asym", "qkv_quantize_append_kv_heads", "qkv_decode_heads",
+                          "qkv_prefill_bits"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -343,3 +344,18 @@ def test_head_map_argument_errors(lib):
     assert dh(L=129) == 1
     assert dh(ns=2) == 3
     assert b"qkv_decode_heads" in lib.qkv_last_error()
+
+
+def test_prefill_bits_argument_errors(lib):
+    i64, vp, f32, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.qkv_prefill_bits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
+    pb = lambda **kw: lib.qkv_prefill_bits(P, P, P, P, P, 1, 4, 2, kw.get("Sq", 10), kw.get("L", 100), 128,
+                                           kw.get("D", 64), kw.get("bits", 2), 0.1, kw.get("causal", 1), P, None,
+                                           None)
+    assert pb(bits=1) == 2
+    assert pb(bits=8) == 2
+    assert pb(D=96) == 2
+    assert pb(causal=2) == 1
+    assert pb(Sq=101) == 1        # causal needs Sq <= kv_len
+    assert pb(L=129) == 1
+    assert b"qkv_prefill_bits" in lib.qkv_last_error()

@@ -48,14 +48,15 @@ def test_quantize_append_matches_oracle(bits, D, T, C, pos):
         assert np.all(c[:, :, :pos] == fc) and np.all(c[:, :, pos + T:] == fc)
 
 
-def _lowbit_case(seed, B, Hq, Hkv, Sq, L, C, D, bits):
+def _lowbit_case(seed, B, Hq, Hkv, Sq, L, C, D, bits, v_outliers=True):
     rng = np.random.default_rng(seed)
     q = f32_to_bf16_bits(rng.standard_normal((B, Hq, Sq, D)).astype(np.float32))
     out = []
-    for scale in (1.0, 1.5):
+    for scale, outl in ((1.0, True), (1.5, v_outliers)):
         x = (rng.standard_normal((B, Hkv, C, D)) * scale).astype(np.float32)
         ch = rng.choice(D, size=2, replace=False)
-        x[:, :, :, ch] *= 8.0                            # outlier channels
+        if outl:
+            x[:, :, :, ch] *= 8.0                        # outlier channels
         out += list(oracle.quantize_rows_bits(x, bits))
     return q, out
 
@@ -111,3 +112,57 @@ def test_decode_bits_length_edges(bits, L):
     torch.cuda.synchronize()
     ro, _ = oracle.attention_bits(q, *arrs, L, 0.125, bits)
     assert_close(out, ro, f"bits={bits} L={L}")
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, Sq, L, C, D, causal
+    (1, 8, 2, 300, 300, 320, 128, True),
+    (2, 4, 4, 197, 197, 197, 64, False),
+    (1, 8, 2, 100, 700, 700, 128, True),      # Sq < kv_len: bottom-right aligned
+    (1, 4, 1, 513, 600, 640, 64, True),
+    (1, 4, 2, 70, 1000, 1024, 128, False),
+]
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(c) for c in PREFILL_CASES])
+def test_prefill_bits_matches_oracle(case, bits):
+    B, Hq, Hkv, Sq, L, C, D, causal = case
+    # outlier channels in K only: with few visible keys (early causal rows) the
+    # fp16 rounding of P~ = p s_V bounds the error by max|v| 2^-11, which
+    # V values of magnitude ~40 would take past the tolerance
+    q, (kc, ks, vc, vs) = _lowbit_case(sum(case) + bits, B, Hq, Hkv, Sq, L, C, D, bits, v_outliers=False)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = torch.full((B, Hq, Sq, D), float("nan"), device=DEV)
+    out, lse = qkv.prefill(q_to_dev(q), _to_dev((kc, ks, vc, vs)), L, causal, softmax_scale=scale,
+                           return_lse=True, out=out, bits=bits)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_bits(q, kc, ks, vc, vs, L, scale, bits, causal=causal)
+    assert_close(out, ro, f"prefill bits={bits} {case}")
+    assert compare(lse, rl)[0] < 1e-3
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_prefill_bits_causal_16k_sampled(bits):
+    """The causal prefill workload's shape (32/8 heads, D 128, 16384 tokens) over
+    b-bit rows, checked on sampled query rows of every head."""
+    B, Hq, Hkv, L, D = 1, 32, 8, 16384, 128
+    rng = np.random.default_rng(40 + bits)
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, L, D)).astype(np.float32))
+    k = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    cache = qkv.KVCache.empty(B, Hkv, L, D, device=DEV, bits=bits)
+    qkv.quantize_append_kv(torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV), cache, 0, bits=bits)
+    out = qkv.prefill(q_to_dev(q), cache, L, True, bits=bits)
+    torch.cuda.synchronize()
+    kc, ks = oracle.quantize_rows_bits(k, bits)
+    vc, vs = oracle.quantize_rows_bits(v, bits)
+    rows = np.array([0, 1, 63, 64, 4095, 8191, 12000, L - 1])
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    errs = []
+    for r in rows:
+        qr = q[:, :, r:r + 1]
+        ro, _ = oracle.attention_bits(qr, kc, ks, vc, vs, r + 1, scale, bits)   # row r sees keys [0, r]
+        errs.append(np.abs(out[:, :, r:r + 1].cpu().double().numpy() - ro))
+    e = np.concatenate([x.ravel() for x in errs])
+    assert e.max() <= 4e-3 and e.mean() <= 4e-4, (e.max(), e.mean())
