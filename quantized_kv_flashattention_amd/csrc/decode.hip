@@ -58,6 +58,10 @@ namespace {
 // (256 per lane with eight waves) do not fit; it keeps four waves and gets
 // the whole register file of its SIMD slot.
 __host__ __device__ constexpr int waves_for(int NB) { return NB >= 4 ? 4 : 8; }
+template <int N>
+struct IntTag {
+  static constexpr int value = N;
+};
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
@@ -66,11 +70,12 @@ constexpr int kMaxTail = 64;                // rows of the INT8 decode buffer on
 constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (floats)
 
 // Dynamic LDS of a decode launch: the wave-merge buffer (waves x min(16, R)
-// rows x (D + 4) floats), reused for the split-merge weights (R x n_split).
+// rows x (D + 4) floats), reused by the split merge for its weights
+// (R x n_split) and one float4 per thread of per-part sums.
 inline size_t merge_lds_bytes(int D, int waves, int R, int n_split) {
   const size_t wave_merge = (size_t)waves * (size_t)(R < 16 ? R : 16) * (size_t)(D + 4);
-  const size_t weights = (size_t)R * (size_t)n_split;
-  return 4 * (wave_merge > weights ? wave_merge : weights);
+  const size_t split_merge = (size_t)R * (size_t)n_split + 4 + (size_t)4 * 64 * waves;
+  return 4 * (wave_merge > split_merge ? wave_merge : split_merge);
 }
 
 // Dynamic LDS of the buffer split: the buffered K and V rows (int8) and the
@@ -81,8 +86,9 @@ inline size_t tail_lds_bytes(int D, int R) {
 
 template <int D, int NB>
 constexpr size_t max_merge_lds_bytes() {   // largest dynamic LDS of a kernel variant
-  const size_t merge = 4 * ((size_t)waves_for(NB) * 16 * (D + 4) > (size_t)kMaxMergeLse
-                                ? (size_t)waves_for(NB) * 16 * (D + 4) : (size_t)kMaxMergeLse);
+  const size_t wave_merge = (size_t)waves_for(NB) * 16 * (D + 4);
+  const size_t split_merge = (size_t)kMaxMergeLse + 4 + (size_t)4 * 64 * waves_for(NB);
+  const size_t merge = 4 * (wave_merge > split_merge ? wave_merge : split_merge);
   const size_t tail = (size_t)2 * kMaxTail * D + (size_t)4 * 64 * kMaxTail;
   return merge > tail ? merge : tail;
 }
@@ -350,103 +356,144 @@ void decode_kernel(const DecodeArgs a) {
     const int n_live = a.tail_rows > 0 ? n_split : min(n_split, (L_b + a.split_len - 1) / a.split_len);
     // item idx: four output values (query row idx / (D/4), dims 4 (idx % (D/4)) + 0..3)
     const int n_items = R * (D / 4);
-    auto item_grow = [&](int idx) -> int64_t {
-      const int row = idx / (D / 4);
-      return grow0 + row;
-    };
-    auto load16 = [&](uint32_t off0, int s0, float4v (&o)[16]) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        o[u] = (s0 + u < n_live)
-                   ? __builtin_amdgcn_raw_buffer_load_b128(rpart, off0 + (uint32_t)((s0 + u) * D * 4), 0, kCoherent)
-                   : float4v{0.f, 0.f, 0.f, 0.f};
-    };
     auto item_off = [&](int idx) -> uint32_t {
       return (uint32_t)(((prow0 + idx / (D / 4)) * n_split * D + 4 * (idx % (D / 4))) * 4);
     };
-    // (0) the partial outputs of this thread's first item (first kPre splits),
-    //     issued now: their round trip overlaps the LSE loads'
-    constexpr int kPre = 8;
-    float4v pre[kPre];
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      pre[u] = float4v{0.f, 0.f, 0.f, 0.f};
-      if ((int)threadIdx.x < n_items && u < n_live)
-        pre[u] = __builtin_amdgcn_raw_buffer_load_b128(rpart, item_off(threadIdx.x) + (uint32_t)(u * D * 4), 0,
-                                                       kCoherent);
-    }
-    // (1) every live split's LSE of this group -> LDS (the wave-merge buffer is free
-    //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
-    float* s_w = s_o;
-    {
-      const int total = R * n_live;
-      for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int idx = base + u * 64 * kWaves;
-          v[u] = -INFINITY;
-          if (idx < total) {
-            const int row = idx / n_live;
-            v[u] = __hip_atomic_load(a.part_lse + (prow0 + row) * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+    // Steps (0)-(3), instantiated for 4 or 16 splits per task loaded ahead
+    // (loads of splits past the live ones still pass the memory pipeline)
+    auto merge_with = [&](auto pre_tag) {
+      // Work unit "task" = (item, part): part p of an item sums its splits p,
+      // p + tpi, p + 2 tpi, ...  With few items (few query rows) and many splits,
+      // several threads share an item (tpi > 1) so that every partial load is in
+      // flight at once; their sums meet in LDS and are added in part order.
+      constexpr int kNthr = 64 * kWaves;
+      constexpr int kPre = decltype(pre_tag)::value;   // splits of a task loaded before the weights are known
+      int tpi = 1;
+      while (tpi * kPre < n_live && 2 * tpi * n_items <= kNthr) tpi *= 2;
+      const int n_tasks = n_items * tpi;
+      // loads of splits part + tpi (u0 + u), u < n.  Branch-free: a split past
+      // the live ones (a thread without a task asks for part n_live) is read at an offset
+      // past the descriptor's range, which returns zeros without a memory
+      // access (loads under divergent branches make the compiler wait for them
+      // at the join, serializing this prefetch with the LSE loads)
+      auto load_n = [&](int item, int part, int u0, auto& o) {
+        const uint32_t off0 = item_off(item);
+        constexpr int n = sizeof(o) / sizeof(o[0]);
+  #pragma unroll
+        for (int u = 0; u < n; ++u) {
+          const int sp = part + tpi * (u0 + u);
+          const uint32_t off = sp < n_live ? off0 + (uint32_t)(sp * D * 4) : 0x80000000u;
+          o[u] = __builtin_amdgcn_raw_buffer_load_b128(rpart, off, 0, kCoherent);
+        }
+      };
+      // acc += sum_u w[part + tpi (u0 + u)] o[u], in blocks of four weights read
+      // together; an index past the live splits is clamped (its o[u] is zero)
+      auto accumulate = [&](const float* wr, int part, int u0, const auto& o, float4v& acc) {
+        constexpr int n = sizeof(o) / sizeof(o[0]);
+  #pragma unroll
+        for (int blk = 0; blk < n / 4; ++blk) {
+          if (tpi * (u0 + 4 * blk) < n_live) {   // uniform
+            float wv[4];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = wr[min(part + tpi * (u0 + 4 * blk + i), n_live - 1)];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) acc += wv[i] * o[4 * blk + i];
           }
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
+      };
+      // (0) the partial outputs of this thread's first task (its first kPre
+      //     splits), issued now: their round trip overlaps the LSE loads'
+      float4v pre[kPre];
+      {
+        const int t0 = min((int)threadIdx.x, n_tasks - 1);
+        load_n(t0 % n_items, (int)threadIdx.x < n_tasks ? t0 / n_items : n_live, 0, pre);
       }
-    }
-    __syncthreads();
-    // (2) per row: max, weights 2^(lse_s - max) (in place), their sum -- one wave per row
-    for (int row = wave; row < R; row += kWaves) {
-      float* wr = s_w + row * n_live;
-      float M = -INFINITY;
-      for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
-      float den = 0.0f;
-      for (int s = lane; s < n_live; s += 64) {
-        const float w = fast_exp2(wr[s] - M);
-        wr[s] = w;
-        den += w;
+      // (1) every live split's LSE of this group -> LDS (the wave-merge buffer is free
+      //     now; the planner keeps R * n_split <= kMaxMergeLse), loads in flight together
+      float* s_w = s_o;
+      {
+        const int total = R * n_live;
+        for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
+          float v[8];
+  #pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int idx = base + u * 64 * kWaves;
+            v[u] = -INFINITY;
+            if (idx < total) {
+              const int row = idx / n_live;
+              v[u] = __hip_atomic_load(a.part_lse + (prow0 + row) * n_split + (idx - row * n_live), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+  #pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
+        }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
-      if (lane == 0) {
-        s_den[row] = den;
-        const int64_t grow = grow0 + row;
-        if (a.lse) a.lse[grow] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+      __syncthreads();
+      // (2) per row: max, weights 2^(lse_s - max) (in place), their sum -- one wave per row
+      for (int row = wave; row < R; row += kWaves) {
+        float* wr = s_w + row * n_live;
+        float M = -INFINITY;
+        for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
+  #pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
+        float den = 0.0f;
+        for (int s = lane; s < n_live; s += 64) {
+          const float w = fast_exp2(wr[s] - M);
+          wr[s] = w;
+          den += w;
+        }
+  #pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
+        if (lane == 0) {
+          s_den[row] = den;
+          const int64_t grow = grow0 + row;
+          if (a.lse) a.lse[grow] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+        }
       }
-    }
-    __syncthreads();
-    // (3) O = sum_s w_s O_s / sum_s w_s, sixteen partial loads in flight per
-    //     thread; the first item starts from its prefetched splits
-    auto finish_item = [&](int idx, bool first) {
-      const int row = idx / (D / 4);
-      const int d = 4 * (idx - row * (D / 4));
-      const float* wr = s_w + row * n_live;
-      const uint32_t off0 = item_off(idx);
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-      int s0 = 0;
-      if (first) {
-#pragma unroll
-        for (int u = 0; u < kPre; ++u)
-          if (u < n_live) acc += wr[u] * pre[u];
-        s0 = kPre;
+      __syncthreads();
+      // (3) O = sum_s w_s O_s / sum_s w_s: each task sums its splits (sixteen
+      //     partial loads in flight per thread; the first task starts from its
+      //     prefetched splits), then the parts of an item are added in order
+      float4v* s_part = reinterpret_cast<float4v*>(s_w + ((R * n_live + 3) & ~3));   // tpi > 1: [tpi][n_items]
+      auto finish = [&](int item, const float4v& acc) {
+        const int row = item / (D / 4);
+        const float den = s_den[row];
+        *reinterpret_cast<float4v*>(a.out + (grow0 + row) * D + 4 * (item - row * (D / 4))) =
+            acc * (den > 0.0f ? 1.0f / den : 0.0f);
+      };
+      auto task = [&](int t, bool first) {
+        const int item = t % n_items;
+        const int part = t / n_items;
+        const float* wr = s_w + (item / (D / 4)) * n_live;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        int u0 = 0;
+        if (first) {
+          accumulate(wr, part, 0, pre, acc);
+          u0 = kPre;
+        }
+        for (; tpi * u0 < n_live; u0 += 16) {   // uniform
+          float4v o[16];
+          load_n(item, part, u0, o);
+          accumulate(wr, part, u0, o, acc);
+        }
+        if (tpi == 1) finish(item, acc);
+        else s_part[t] = acc;
+      };
+      if ((int)threadIdx.x < n_tasks) task(threadIdx.x, true);
+      for (int t = threadIdx.x + kNthr; t < n_tasks; t += kNthr) task(t, false);
+      if (tpi > 1) {
+        __syncthreads();
+        for (int item = threadIdx.x; item < n_items; item += kNthr) {
+          float4v acc = s_part[item];
+          for (int p = 1; p < tpi; ++p) acc += s_part[p * n_items + item];
+          finish(item, acc);
+        }
       }
-      for (; s0 < n_live; s0 += 16) {
-        float4v o[16];
-        load16(off0, s0, o);
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (s0 + u < n_live) acc += wr[s0 + u] * o[u];
-      }
-      const float den = s_den[row];
-      *reinterpret_cast<float4v*>(a.out + item_grow(idx) * D + d) = acc * (den > 0.0f ? 1.0f / den : 0.0f);
     };
-    if ((int)threadIdx.x < n_items) finish_item(threadIdx.x, true);
-    for (int idx = threadIdx.x + 64 * kWaves; idx < n_items; idx += 64 * kWaves) finish_item(idx, false);
+    if (n_live <= 4) merge_with(IntTag<4>{});
+    else merge_with(IntTag<16>{});
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 

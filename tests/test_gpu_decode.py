@@ -116,6 +116,28 @@ def test_workspace_reuse_across_shapes():
         assert int((ws[:8] != 0).sum()) == 0, "tickets not returned to zero"
 
 
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, Sq, L, D, num_splits
+    (1, 1, 1, 1, 20000, 64, 200),     # one query row, 157 splits: 16 threads per output item
+    (1, 2, 1, 1, 20000, 128, 200),    # 8 threads per item, more than 16 splits each
+    (2, 4, 2, 3, 9000, 128, 40),      # 2 threads per item, 18 splits each
+    (1, 8, 2, 8, 5000, 128, 40),      # 32 rows: one thread per item, loads in rounds
+])
+def test_merge_of_many_splits(case):
+    """The merging workgroup spreads each output item's splits over several
+    threads when there are few rows and many splits; every split's partial
+    still counts once, and repeated calls agree bit for bit."""
+    B, Hq, Hkv, Sq, L, D, ns = case
+    q, kc, ks, vc, vs = random_case(sum(case), B, Hq, Hkv, Sq, L, D)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, lse = _run(q, (kc, ks, vc, vs), L, scale, ns)
+    again, _ = _run(q, (kc, ks, vc, vs), L, scale, ns)
+    assert torch.equal(out, again)
+    ro, rl = oracle.attention(q, kc, ks, vc, vs, L, scale)
+    assert_close(out, ro, f"{case}")
+    assert compare(lse, rl)[0] < 1e-3
+
+
 @pytest.mark.parametrize("case", [(16, 32, 8, 1, 8192, 128, 0), (1, 64, 8, 1, 20000, 128, 0), (2, 8, 2, 4, 3000, 64, 11)])
 def test_split_merge_sees_fresh_partials(case):
     """The last workgroup of a group merges partials written by workgroups on
