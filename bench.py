@@ -429,11 +429,15 @@ def bench_asym(torch, qkv, w, steps, int4_ms=None):
     return res
 
 
-def bench_prefill(torch, qkv, w, iters, bits=4):
-    """Prefill over a cache of ``bits``-bit rows (4: the int4 path)."""
+def bench_prefill(torch, qkv, w, iters, bits=4, group=0):
+    """Prefill over a cache of ``bits``-bit rows (4: the int4 path), or of
+    asymmetric group-wise int4 rows with groups of ``group`` elements."""
     from qkv_inputs import make_qkv
     q_bits, k, v = make_qkv(w)
-    if bits == 4:
+    if group:
+        cache = qkv.AsymKVCache.empty(w.B, w.Hkv, w.L, w.D, group)
+        qkv.quantize_append_kv_asym(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), cache, 0)
+    elif bits == 4:
         cache = upload_cache(torch, qkv, k, v, 1)[0]
     else:
         cache = qkv.KVCache.empty(w.B, w.Hkv, w.L, w.D, bits=bits)
@@ -443,13 +447,17 @@ def bench_prefill(torch, qkv, w, iters, bits=4):
     out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
 
     def run(_):
-        qkv.prefill(q, cache, w.L, w.causal, softmax_scale=w.softmax_scale, out=out, bits=bits)
+        if group:
+            qkv.prefill_asym(q, cache, w.L, w.causal, softmax_scale=w.softmax_scale, out=out)
+        else:
+            qkv.prefill(q, cache, w.L, w.causal, softmax_scale=w.softmax_scale, out=out, bits=bits)
 
     for i in range(2):
         run(i)
     avg_ms, med_ms = per_launch_ms(torch, run, iters, 1)
     fl = prefill_flops(w)
-    res = {"workload": w.name, "bits": bits, "avg_ms": avg_ms, "median_ms": med_ms, "flops": fl,
+    res = {"workload": w.name, "bits": bits, "group": group or None, "avg_ms": avg_ms, "median_ms": med_ms,
+           "flops": fl,
            "TFLOPs": fl / (avg_ms * 1e-3) / 1e12}
     res["frac_mfma"] = res["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
     del cache, q, out
@@ -674,6 +682,9 @@ def main():
         secondary["causal_prefill_16k_lowbit"] = {
             f"{b}bit": bench_prefill(torch, qkv, workload("causal_prefill_16k"), 6, bits=b) for b in (2, 3)}
         log("prefill lowbit:", json.dumps(secondary["causal_prefill_16k_lowbit"]))
+        secondary["causal_prefill_16k_asym"] = {
+            f"group{g}": bench_prefill(torch, qkv, workload("causal_prefill_16k"), 6, group=g) for g in (128, 64, 32)}
+        log("prefill asym:", json.dumps(secondary["causal_prefill_16k_asym"]))
     if args.only == "all":
         secondary["quantize_append"] = bench_quantize(torch, qkv, w3, 20)
         log("quantize:", json.dumps(secondary["quantize_append"]))

@@ -418,6 +418,23 @@ qkv_status qkv_prefill_bits(const uint16_t* q,
                             int64_t C, int64_t D, int bits, float softmax_scale, int causal,
                             float* out, float* lse, void* stream);
 
+/* qkv_prefill over asymmetric group-wise 4-bit rows (the layout and parameter
+ * words of qkv_decode_asym; TurboAttention §2.3 and §3.1).  Codes enter LDS
+ * as exact fp16 code - z; with one group per row the K scale multiplies
+ * score columns and the V scale is folded into P as for int4 rows; with
+ * several, each group's QK products are accumulated apart and scaled by the
+ * group's K scale in fp32, and each 32-head-dim output block takes its
+ * group's P~ = fp16(p s_V).  Requires group in {32, 64, 128}, group <= D
+ * (QKV_ERR_UNSUPPORTED otherwise), k_params / v_params aligned to
+ * 4 * (D / group) bytes, kv_len * (D / group) * 4 < 2^31, and the
+ * qkv_prefill requirements. */
+qkv_status qkv_prefill_asym(const uint16_t* q,
+                            const uint8_t* k_codes, const uint32_t* k_params,
+                            const uint8_t* v_codes, const uint32_t* v_params,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                            int64_t C, int64_t D, int group, float softmax_scale, int causal,
+                            float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -115,6 +115,8 @@ def _load():
                                      vp, vp, vp, sz, vp]
     lib.qkv_prefill_bits.restype = ci
     lib.qkv_prefill_bits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
+    lib.qkv_prefill_asym.restype = ci
+    lib.qkv_prefill_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
     lib.qkv_decode_asym.restype = ci
     lib.qkv_decode_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
                                     vp, vp, vp, sz, vp]
@@ -455,6 +457,23 @@ def decode_asym(q, cache: AsymKVCache, kv_len, softmax_scale=None, num_splits=0,
     _check(_lib.qkv_decode_asym(_ptr(q), _ptr(kc), _ptr(kp), _ptr(vc), _ptr(vp), B, Hq, Hkv, Sq, int(kv_len),
                                 C, D, int(cache.group), _scale(softmax_scale, D), int(num_splits), _ptr(out),
                                 _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def prefill_asym(q, cache: AsymKVCache, kv_len, causal, softmax_scale=None, return_lse=False, out=None,
+                 lse=None):
+    """Prefill attention of ``q [B, Hq, Sq, D]`` over rows ``[0, kv_len)`` of an
+    asymmetric group-wise cache (causal: bottom-right aligned, as ``prefill``)."""
+    _req(q, "q", torch.bfloat16, 4)
+    if not isinstance(cache, AsymKVCache):
+        raise TypeError("cache must be an AsymKVCache")
+    B, Hq, Sq, D = q.shape
+    Hkv = int(cache.k_codes.shape[1]) if cache.k_codes.dim() == 4 else 0
+    kc, kp, vc, vp, C = _asym_args(cache, q.device, B, Hkv, D)
+    out, lse = _outputs(q, out, lse, return_lse)
+    _check(_lib.qkv_prefill_asym(_ptr(q), _ptr(kc), _ptr(kp), _ptr(vc), _ptr(vp), B, Hq, Hkv, Sq, int(kv_len),
+                                 C, D, int(cache.group), _scale(softmax_scale, D), int(bool(causal)), _ptr(out),
+                                 _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
 
 

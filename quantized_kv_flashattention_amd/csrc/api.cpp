@@ -511,11 +511,12 @@ qkv_status qkv_decode_buffered(const uint16_t* q, const float* k_new, const floa
                     "qkv_decode_buffered");
 }
 
+// group > 0: asymmetric rows, k_scales / v_scales are their parameter words
 static qkv_status prefill_common(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
                                  const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
                                  int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
                                  float softmax_scale, int causal, float* out, float* lse, void* stream, int bits,
-                                 const char* fn) {
+                                 const char* fn, int group = 0) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -527,6 +528,15 @@ static qkv_status prefill_common(const uint16_t* q, const uint8_t* k_codes, cons
     return fail(QKV_ERR_UNSUPPORTED, f + ": too many query blocks");
   if (kv_len * (D * bits / 8) > 0x7FFFFFFFll)
     return fail(QKV_ERR_UNSUPPORTED, f + ": kv_len * D * bits / 8 must stay below 2^31 bytes");
+  if (group > 0) {
+    if (kv_len * (D / group) * 4 > 0x7FFFFFFFll)
+      return fail(QKV_ERR_UNSUPPORTED, f + ": kv_len * (D / group) * 4 must stay below 2^31 bytes");
+    return hip_status(qkvfa::launch_prefill_asym(q, k_codes, reinterpret_cast<const uint32_t*>(k_scales), v_codes,
+                                                 reinterpret_cast<const uint32_t*>(v_scales), B, Hq, Hkv, Sq,
+                                                 kv_len, C, (int)D, group, softmax_scale, causal, out, lse,
+                                                 static_cast<hipStream_t>(stream)),
+                      fn);
+  }
   return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
                                           kv_len, C, (int)D, softmax_scale, causal, out, lse,
                                           static_cast<hipStream_t>(stream), bits),
@@ -549,6 +559,21 @@ qkv_status qkv_prefill_bits(const uint16_t* q, const uint8_t* k_codes, const uin
     return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill_bits: bits must be 2, 3 or 4");
   return prefill_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
                         causal, out, lse, stream, bits, "qkv_prefill_bits");
+}
+
+qkv_status qkv_prefill_asym(const uint16_t* q, const uint8_t* k_codes, const uint32_t* k_params,
+                            const uint8_t* v_codes, const uint32_t* v_params, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D, int group,
+                            float softmax_scale, int causal, float* out, float* lse, void* stream) {
+  if (D != 64 && D != 128) return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill_asym: head dim must be 64 or 128");
+  if (!valid_group(D, group))
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill_asym: group must be 32, 64 or 128 and at most the head dim");
+  const int64_t wbytes = 4 * (D / group);   // parameter words of one row
+  if ((k_params && !aligned(k_params, wbytes)) || (v_params && !aligned(v_params, wbytes)))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_prefill_asym: parameter words must be 4 * (D / group)-byte aligned");
+  return prefill_common(q, k_codes, reinterpret_cast<const uint16_t*>(k_params), v_codes,
+                        reinterpret_cast<const uint16_t*>(v_params), B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
+                        causal, out, lse, stream, 4, "qkv_prefill_asym", group);
 }
 
 }  // extern "C"

@@ -94,12 +94,25 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
   return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
 }
 
-template <int D, int NW, bool CAUSAL, int BITS>
+template <int D, int NW, bool CAUSAL, int BITS, int NGA>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-    const uint16_t* __restrict__ vs, int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C,
+    const uint16_t* __restrict__ vs, const uint32_t* __restrict__ kp, const uint32_t* __restrict__ vp,
+    int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C,
     float qk_log2, int nqb, float* __restrict__ out, float* __restrict__ lse_out) {
+  // Asymmetric group-wise rows (NGA groups per row): unsigned nibbles in the
+  // cache's K and V row orders and parameter words kp/vp [B, Hkv, C, NGA]
+  // (fp16 scale in bits 0-15, zero point in bits 16-19).  Codes enter LDS as
+  // exact fp16 u - z.  With one group the scales act as the int4 rows' do;
+  // with several, each group's QK products accumulate apart and join the
+  // score under the group's K scale (PRESCALED scores), and each PV output
+  // block (32 head dims, inside one group) takes its group's P~ = p s_V.
+  constexpr bool ASYM = NGA > 0;
+  constexpr bool PRESCALED = NGA > 1;
+  constexpr int NG = ASYM ? NGA : 1;  // scale (and zero point) groups per row
+  constexpr int GS = D / NG;          // elements per group
+  static_assert(!ASYM || (BITS == 4 && GS >= 32 && D % GS == 0), "asymmetric rows: 4 bits, groups of >= 32");
   constexpr int BM = 32 * NW;  // query rows per workgroup
   constexpr int KS = D / 16;   // QK k-steps
   constexpr int NDB = D / 32;  // PV output blocks
@@ -115,8 +128,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   __shared__ __align__(16) _Float16 s_k[2 * KBUF];
   __shared__ __align__(16) _Float16 s_v[2 * VBUF];
-  __shared__ __align__(16) float s_csk[2][BN];     // K scale x qk_log2
-  __shared__ __align__(16) _Float16 s_svh[2][BN];  // V scale, [j][tb][vq][i]
+  __shared__ __align__(16) float s_csk[2][NG][BN];     // K scale x qk_log2 (per group)
+  __shared__ __align__(16) _Float16 s_svh[2][NG][BN];  // V scale (per group), [j][tb][vq][i]
   __shared__ float s_cmax[2];                      // max |csk| of the tile
   __shared__ __align__(16) float s_ones[BN];
 
@@ -174,6 +187,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const rsrc_t rk = make_rsrc(kc + kvrow0 * ROWB, kv_len * ROWB);
   const rsrc_t rv = make_rsrc(vc + kvrow0 * ROWB, kv_len * ROWB);
   const rsrc_t rsc = make_rsrc((wave == 0 ? ks : vs) + kvrow0, kv_len * 2);
+  // asymmetric rows: parameter words (NG per token)
+  const rsrc_t rkp = make_rsrc(ASYM ? kp + kvrow0 * NG : nullptr, ASYM ? kv_len * NG * 4 : 0);
+  const rsrc_t rvp = make_rsrc(ASYM ? vp + kvrow0 * NG : nullptr, ASYM ? kv_len * NG * 4 : 0);
 
   // Loader roles.  K: lane = token, wave = which ROWB / NW bytes of the row
   // (chunk planes KDW wave ..).  V: VT consecutive tokens x one dword (8 head
@@ -216,6 +232,35 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   uint32_t ktop = 0;        // 3 bits: the K chunks' top-bit bytes
   uint32_t vt[VT] = {};     // 3 bits: the V tokens' top-bit bytes
   uint16_t sc = 0;
+  // asymmetric rows: the parameter word of each K chunk's group (token lane)
+  // and the V tokens' words (all groups); for the scale tables, waves
+  // [0, NG) load the K word of group `wave` of token lane and waves
+  // [NW/2, NW/2 + NG) the V word of group wave - NW/2
+  static_assert(!ASYM || NG <= NW / 2, "one wave per group and tensor");
+  uint32_t kpw[ASYM ? KDW : 1] = {};
+  uint32_t vpw[ASYM ? VT : 1][NG] = {};
+  uint32_t spw = 0;
+  const bool sp_k = wave < NG;
+  const bool sp_v = wave >= NW / 2 && wave < NW / 2 + NG;
+  const int sp_g = sp_k ? wave : wave - NW / 2;
+  // K chunk (head dims 8c..8c+7) held by dword w of an asymmetric row
+  auto asym_kchunk = [](int w) { return 4 * (w % (D / 32)) + w / (D / 32); };
+  // head dim held by nibble n of dword w of an asymmetric V row
+  auto asym_vdim = [](int w, int n) { return D == 128 ? 16 * n + w : 16 * (n & 3) + w + 8 * (n >> 2); };
+  // NG consecutive parameter words at byte offset off (+ soff)
+  auto load_words = [&](const rsrc_t& rs, uint32_t off, int soff, uint32_t (&o)[NG]) {
+    if constexpr (NG == 4) {
+      const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rs, off, soff, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = w[i];
+    } else if constexpr (NG == 2) {
+      const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, soff, 0);
+      o[0] = w[0];
+      o[1] = w[1];
+    } else {
+      o[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, soff, 0);
+    }
+  };
 
   auto load_tile = [&](int t0) {
     const int so = t0 * ROWB;
@@ -252,7 +297,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int i = 0; i < VT; ++i)
       vw[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_voff + i * ROWB, so, 0);
-    if (wave < 2) sc = __builtin_amdgcn_raw_buffer_load_b16(rsc, (uint32_t)(lane * 2), t0 * 2, 0);
+    if constexpr (ASYM) {
+      const int po = t0 * NG * 4;
+#pragma unroll
+      for (int i = 0; i < KDW; ++i) {
+        const int gi = 8 * asym_kchunk(KDW * wave + i) / GS;
+        kpw[i] = __builtin_amdgcn_raw_buffer_load_b32(rkp, (uint32_t)((lane * NG + gi) * 4), po, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VT; ++i) load_words(rvp, (uint32_t)((v_tok0 + i) * NG * 4), po, vpw[i]);
+      if (sp_k || sp_v)
+        spw = __builtin_amdgcn_raw_buffer_load_b32(sp_k ? rkp : rvp, (uint32_t)((lane * NG + sp_g) * 4), po, 0);
+    } else {
+      if (wave < 2) sc = __builtin_amdgcn_raw_buffer_load_b16(rsc, (uint32_t)(lane * 2), t0 * 2, 0);
+    }
   };
 
   // Exact codes to LDS (no scale applied), scales to their tables.
@@ -261,9 +319,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     _Float16* sv_ = s_v + buf * VBUF;
 #pragma unroll
     for (int i = 0; i < KDW; ++i) {
-      const int c = KDW * wave + i;
+      const int c = ASYM ? asym_kchunk(KDW * wave + i) : KDW * wave + i;
       half8v kop;
-      if constexpr (BITS == 4)
+      if constexpr (ASYM)
+        kop = unpack8_uz(kw[i], (kpw[i] >> 16) & 0xFu);
+      else if constexpr (BITS == 4)
         kop = unpack8_perm(kw[i]);
       else
         kop = unpack8_lowbit<BITS>(kw[i >> 1] >> (16 * (i & 1)), (ktop >> (8 * i)) & 0xFFu);
@@ -278,24 +338,47 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      // row slot (8 v_dp + n) ^ sig = v_st's slot with n xor-ed into bits 0-2
-      _Float16* dst = sv_ + (v_st ^ (n * 8));
-      const half2v a = vpair(0, n);
+      _Float16* dst;
+      half2v a, c2;
+      if constexpr (ASYM) {
+        // nibble n of dword v_dp holds head dim d (row slot d ^ ((d >> 4) & 7))
+        const int d = asym_vdim(v_dp, n);
+        const int gi = d / GS;
+        dst = sv_ + (v_st & ~(VPL - 1)) + (v_st & 7) + ((d ^ ((d >> 4) & 7)) * 8);
+        auto zt = [&](int t) { return (vpw[t][gi] >> 16) & 0xFu; };
+        a = uz_pair2(vw[0], vw[1], n, zt(0), zt(1));
+        if constexpr (VT == 4) c2 = uz_pair2(vw[2], vw[3], n, zt(2), zt(3));
+      } else {
+        // row slot (8 v_dp + n) ^ sig = v_st's slot with n xor-ed into bits 0-2
+        dst = sv_ + (v_st ^ (n * 8));
+        a = vpair(0, n);
+        if constexpr (VT == 4) c2 = vpair(2, n);
+      }
       if constexpr (VT == 4) {
-        const half2v c = vpair(2, n);
-        const uint2v w = {bitcast<uint32_t>(a), bitcast<uint32_t>(c)};
+        const uint2v w = {bitcast<uint32_t>(a), bitcast<uint32_t>(c2)};
         *reinterpret_cast<uint2v*>(dst) = w;
       } else {
         *reinterpret_cast<uint32_t*>(dst) = bitcast<uint32_t>(a);
       }
     }
-    if (wave == 0) {
+    if constexpr (ASYM) {
+      if (sp_k) {
+        const float f = f16bits_to_f32((uint16_t)(spw & 0xFFFFu)) * qk_log2;
+        s_csk[buf][sp_g][lane] = f;
+        if constexpr (!PRESCALED) {
+          const float m = wave_max_nonneg(fabsf(f));
+          if (lane == 0) s_cmax[buf] = m;
+        }
+      } else if (sp_v) {
+        s_svh[buf][sp_g][sv_slot] = bitcast<_Float16>((uint16_t)(spw & 0xFFFFu));
+      }
+    } else if (wave == 0) {
       const float f = f16bits_to_f32(sc) * qk_log2;
-      s_csk[buf][lane] = f;
+      s_csk[buf][0][lane] = f;
       const float m = wave_max_nonneg(fabsf(f));
       if (lane == 0) s_cmax[buf] = m;
     } else if (wave == 1) {
-      s_svh[buf][sv_slot] = bitcast<_Float16>(sc);
+      s_svh[buf][0][sv_slot] = bitcast<_Float16>(sc);
     }
   };
 
@@ -323,7 +406,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int buf = kt & 1;
     const _Float16* sk_ = s_k + buf * KBUF;
     const _Float16* sv_ = s_v + buf * VBUF;
-    const float* csk_ = s_csk[buf];
+    const float* csk_ = &s_csk[buf][0][0];
+    // column factors of the softmax: the K scale column, or ones when the
+    // scores already carry their (per-group) K scales
+    const float* cbase = PRESCALED ? s_ones : csk_;
     const bool need = ALL_FULL || (wave_active && (!CAUSAL || t0 <= wrow_hi + off));
 
     // Convert the next tile into the other buffer and fetch the one after.
@@ -332,15 +418,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     float16v st[2];
     if (need) {
       // ---- S^T = K Q^T for two 32-token blocks
+      if constexpr (PRESCALED) {
+        // group by group (k-steps 16 s .. 16 s + 15 lie in group 16 s / GS);
+        // each group's products scaled by its K scale column
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float16v acc = float16v{};
+        for (int tb = 0; tb < 2; ++tb) {
+          st[tb] = float16v{};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const half8v a = *reinterpret_cast<const half8v*>(sk_ + k_rd + 2 * s * KPL + tb * 256);
-          acc = mfma32x32x16(a, qop[s], acc);
+          for (int gi = 0; gi < NG; ++gi) {
+            float16v acc = float16v{};
+#pragma unroll
+            for (int s = gi * (KS / NG); s < (gi + 1) * (KS / NG); ++s) {
+              const half8v a = *reinterpret_cast<const half8v*>(sk_ + k_rd + 2 * s * KPL + tb * 256);
+              acc = mfma32x32x16(a, qop[s], acc);
+            }
+#pragma unroll
+            for (int vq = 0; vq < 4; ++vq) {
+              const float4v c = *reinterpret_cast<const float4v*>(csk_ + gi * BN + 32 * tb + 8 * vq + 4 * j);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) st[tb][4 * vq + i] = fmaf(acc[4 * vq + i], c[i], st[tb][4 * vq + i]);
+            }
+          }
         }
-        st[tb] = acc;
+        // the folded scores are complete here: without this pin the compiler
+        // sinks the fold below the conversion of the next tile, keeping every
+        // group's products and scale columns live across it
+        asm volatile("" : "+v"(st[0]), "+v"(st[1]));
+      } else {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          float16v acc = float16v{};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const half8v a = *reinterpret_cast<const half8v*>(sk_ + k_rd + 2 * s * KPL + tb * 256);
+            acc = mfma32x32x16(a, qop[s], acc);
+          }
+          st[tb] = acc;
+        }
       }
       store_tile(buf ^ 1);
       load_tile(t0 + 2 * BN);
@@ -353,7 +467,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // ---- online softmax; lane's tokens: 32 tb + 8 (v/4) + 4 j + v%4
       const bool full = ALL_FULL || ((t0 + BN <= kv_len) && (!CAUSAL || t0 + BN - 1 <= wrow_lo + off));
       auto csk4 = [&](int tb, int vq) {
-        return *reinterpret_cast<const float4v*>(csk_ + 32 * tb + 8 * vq + 4 * j);
+        return *reinterpret_cast<const float4v*>(cbase + 32 * tb + 8 * vq + 4 * j);
       };
       // Exponent p = exp2(st * c - m_use): with c = csk and raw scores st on
       // full tiles, with c = 1 and exact masked scores st on the others.
@@ -386,8 +500,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fabsf(st[tb][v]));
         }
-        mx *= s_cmax[buf];
-        ctab = csk_;
+        if constexpr (!PRESCALED) mx *= s_cmax[buf];
+        ctab = cbase;
       }
       if (__builtin_amdgcn_ballot_w64(mx > m_ref + kTau)) {
         // some row of the wave may rise above its reference: move the
@@ -413,37 +527,72 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o_acc[db] *= alpha;
       }
-      half8v pop[2][2];
-      const half8v* svh = reinterpret_cast<const half8v*>(&s_svh[buf][32 * j]);
+      if constexpr (PRESCALED) {
+        // per 32-token block: probabilities once, then for each group its
+        // P~_g = fp16(p s_V,g) and the PV products of the group's output blocks
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < 2; ++tb) {
+          float pr[2][8];
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          const half8v sv = svh[2 * tb + kp];  // tokens 32 tb + 8 (2 kp + e/4) + 4 j + e%4
+          for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            // v = 4 vq + i = 8 kp + e  ->  vq = 2 kp + e/4, i = e%4
-            const int vq = 2 * kp + (e >> 2);
-            const int i = e & 3;
-            const float c = ctab[32 * tb + 8 * vq + 4 * j + i];
-            const float p = fast_exp2(fmaf(st[tb][8 * kp + e], c, -m_use));
-            l_run += p;
-            // P~ = fp16(p x s_V): one rounding of the exact product
-            pop[tb][kp][e] = (_Float16)fmaf(p, (float)sv[e], 0.0f);
+            for (int e = 0; e < 8; ++e) {
+              const float p = fast_exp2(st[tb][8 * kp + e] - m_use);
+              l_run += p;
+              pr[kp][e] = p;
+            }
+          }
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) {
+            const half8v* svh = reinterpret_cast<const half8v*>(&s_svh[buf][gi][32 * j]);
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+              const half8v sv = svh[2 * tb + kp];
+              half8v pg;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pg[e] = (_Float16)fmaf(pr[kp][e], (float)sv[e], 0.0f);
+#pragma unroll
+              for (int db = gi * (NDB / NG); db < (gi + 1) * (NDB / NG); ++db) {
+                const half8v a =
+                    *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
+                o_acc[db] = mfma32x32x16(a, pg, o_acc[db]);
+              }
+            }
           }
         }
-      }
+      } else {
+        half8v pop[2][2];
+        const half8v* svh = reinterpret_cast<const half8v*>(&s_svh[buf][0][32 * j]);
+  #pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+  #pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            const half8v sv = svh[2 * tb + kp];  // tokens 32 tb + 8 (2 kp + e/4) + 4 j + e%4
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              // v = 4 vq + i = 8 kp + e  ->  vq = 2 kp + e/4, i = e%4
+              const int vq = 2 * kp + (e >> 2);
+              const int i = e & 3;
+              const float c = ctab[32 * tb + 8 * vq + 4 * j + i];
+              const float p = fast_exp2(fmaf(st[tb][8 * kp + e], c, -m_use));
+              l_run += p;
+              // P~ = fp16(p x s_V): one rounding of the exact product
+              pop[tb][kp][e] = (_Float16)fmaf(p, (float)sv[e], 0.0f);
+            }
+          }
+        }
 
-      // ---- O^T += V^T P^T; k = 8 j + e <-> token 32 tb + 16 kp + 8 (e/4) + 4 j + e%4
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const half8v a =
-                *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
-            o_acc[db] = mfma32x32x16(a, pop[tb][kp], o_acc[db]);
+        // ---- O^T += V^T P^T; k = 8 j + e <-> token 32 tb + 16 kp + 8 (e/4) + 4 j + e%4
+  #pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+  #pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+  #pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const half8v a =
+                  *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
+              o_acc[db] = mfma32x32x16(a, pop[tb][kp], o_acc[db]);
+            }
           }
         }
       }
@@ -476,30 +625,52 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-template <int D, int NW, bool CAUSAL, int BITS>
-hipError_t launch1(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
-                   const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
-                   int64_t kv_len, int64_t C, float qk_log2, float* out, float* lse,
-                   hipStream_t stream) {
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint8_t* kc;
+  const uint16_t* ks;
+  const uint8_t* vc;
+  const uint16_t* vs;
+  const uint32_t* kp;   // asymmetric rows: parameter words
+  const uint32_t* vp;
+  int64_t B, Hq, Hkv, Sq, kv_len, C;
+  float qk_log2;
+  float* out;
+  float* lse;
+};
+
+template <int D, int NW, bool CAUSAL, int BITS, int NGA = 0>
+hipError_t launch1(const PrefillArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * NW;
-  const int nqb = (int)((Sq + BM - 1) / BM);
-  dim3 grid((uint32_t)Hq, (uint32_t)nqb, (uint32_t)B);
-  prefill_kernel<D, NW, CAUSAL, BITS><<<grid, dim3(64 * NW), 0, stream>>>(
-      q, kc, ks, vc, vs, (int)Hq, (int)Hkv, (int)(Hq / Hkv), (int)Sq, (int)kv_len, C, qk_log2, nqb,
-      out, lse);
+  const int nqb = (int)((a.Sq + BM - 1) / BM);
+  dim3 grid((uint32_t)a.Hq, (uint32_t)nqb, (uint32_t)a.B);
+  prefill_kernel<D, NW, CAUSAL, BITS, NGA><<<grid, dim3(64 * NW), 0, stream>>>(
+      a.q, a.kc, a.ks, a.vc, a.vs, a.kp, a.vp, (int)a.Hq, (int)a.Hkv, (int)(a.Hq / a.Hkv), (int)a.Sq,
+      (int)a.kv_len, a.C, a.qk_log2, nqb, a.out, a.lse);
   return hipGetLastError();
 }
 
+// bits 2, 3, 4 (symmetric rows), or asymmetric rows with ng groups per row (ng > 0)
 template <int D, int NW, bool CAUSAL>
-hipError_t launch(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
-                  const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
-                  int64_t kv_len, int64_t C, float qk_log2, float* out, float* lse,
-                  hipStream_t stream, int bits) {
-  if (bits == 2)
-    return launch1<D, NW, CAUSAL, 2>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
-  if (bits == 3)
-    return launch1<D, NW, CAUSAL, 3>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
-  return launch1<D, NW, CAUSAL, 4>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse, stream);
+hipError_t launch(const PrefillArgs& a, hipStream_t stream, int bits, int ng) {
+  if (ng == 1) return launch1<D, NW, CAUSAL, 4, 1>(a, stream);
+  if (ng == 2) return launch1<D, NW, CAUSAL, 4, 2>(a, stream);
+  if (ng == 4) {
+    if constexpr (D == 128) return launch1<D, NW, CAUSAL, 4, 4>(a, stream);
+    return hipErrorInvalidValue;
+  }
+  if (bits == 2) return launch1<D, NW, CAUSAL, 2>(a, stream);
+  if (bits == 3) return launch1<D, NW, CAUSAL, 3>(a, stream);
+  return launch1<D, NW, CAUSAL, 4>(a, stream);
+}
+
+hipError_t launch_any(const PrefillArgs& a, int D, int causal, hipStream_t stream, int bits, int ng) {
+  if (D == 128) {
+    if (causal) return launch<128, 8, true>(a, stream, bits, ng);
+    return launch<128, 8, false>(a, stream, bits, ng);
+  }
+  if (causal) return launch<64, 4, true>(a, stream, bits, ng);
+  return launch<64, 4, false>(a, stream, bits, ng);
 }
 
 }  // namespace
@@ -509,19 +680,19 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                           float softmax_scale, int causal, float* out, float* lse,
                           hipStream_t stream, int bits) {
-  const float qk_log2 = softmax_scale * kLog2e;
-  if (D == 128) {
-    if (causal)
-      return launch<128, 8, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2,
-                                  out, lse, stream, bits);
-    return launch<128, 8, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2,
-                                 out, lse, stream, bits);
-  }
-  if (causal)
-    return launch<64, 4, true>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
-                               stream, bits);
-  return launch<64, 4, false>(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, qk_log2, out, lse,
-                              stream, bits);
+  const PrefillArgs a = {q, kc, ks, vc, vs, nullptr, nullptr, B, Hq, Hkv, Sq, kv_len, C,
+                         softmax_scale * kLog2e, out, lse};
+  return launch_any(a, D, causal, stream, bits, 0);
+}
+
+hipError_t launch_prefill_asym(const uint16_t* q, const uint8_t* kc, const uint32_t* kp,
+                               const uint8_t* vc, const uint32_t* vp, int64_t B, int64_t Hq,
+                               int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D, int group,
+                               float softmax_scale, int causal, float* out, float* lse,
+                               hipStream_t stream) {
+  const PrefillArgs a = {q, kc, nullptr, vc, nullptr, kp, vp, B, Hq, Hkv, Sq, kv_len, C,
+                         softmax_scale * kLog2e, out, lse};
+  return launch_any(a, D, causal, stream, 4, D / group);
 }
 
 }  // namespace qkvfa

@@ -253,6 +253,34 @@ __device__ __forceinline__ half8v unpack8_n79(uint32_t x) {
   return bitcast<half8v>(w);
 }
 
+// Unsigned nibbles u of asymmetric rows -> exact fp16 u - z.  Bits 0x6400 | u
+// are the fp16 1024 + u and bits 0x5400 | u << 4 are 64 + u, so subtracting
+// 1024 + z (bits 0x6400 | z) or 64 + z (bits 0x5400 | z << 4) leaves u - z
+// exactly.  Eight nibbles of a dword with one zero point z, in the
+// unpack8_perm order [u0, u4, u1, u5, u2, u6, u3, u7] (minus z).
+__device__ __forceinline__ half8v unpack8_uz(uint32_t x, uint32_t z) {
+  const half2v blo = bitcast<half2v>((0x6400u | z) * 0x00010001u);
+  const half2v bhi = bitcast<half2v>((0x5400u | (z << 4)) * 0x00010001u);
+  uint4v w;
+  w[0] = bitcast<uint32_t>(bitcast<half2v>((x & 0x000F000Fu) | 0x64006400u) - blo);
+  w[1] = bitcast<uint32_t>(bitcast<half2v>((x & 0x00F000F0u) | 0x54005400u) - bhi);
+  w[2] = bitcast<uint32_t>(bitcast<half2v>(((x >> 8) & 0x000F000Fu) | 0x64006400u) - blo);
+  w[3] = bitcast<uint32_t>(bitcast<half2v>(((x >> 8) & 0x00F000F0u) | 0x54005400u) - bhi);
+  return bitcast<half8v>(w);
+}
+
+// Nibble `nib` (0..7) of dwords a and b (unsigned codes) -> fp16 pair
+// (u_a - za, u_b - zb), exact.
+__device__ __forceinline__ half2v uz_pair2(uint32_t a, uint32_t b, int nib, uint32_t za, uint32_t zb) {
+  const uint32_t x = pair_bytes(a, b, nib >> 1);
+  if (nib & 1) {
+    const uint32_t bias = (0x5400u | (za << 4)) | ((0x5400u | (zb << 4)) << 16);
+    return bitcast<half2v>((x & 0x00F000F0u) | 0x54005400u) - bitcast<half2v>(bias);
+  }
+  const uint32_t bias = (0x6400u | za) | ((0x6400u | zb) << 16);
+  return bitcast<half2v>((x & 0x000F000Fu) | 0x64006400u) - bitcast<half2v>(bias);
+}
+
 // Raw buffer descriptor over [base, base + num_bytes): loads at offsets past
 // num_bytes return zero instead of touching memory (gfx9-family raw buffer
 // range check; the fourth descriptor word selects 32-bit data format).

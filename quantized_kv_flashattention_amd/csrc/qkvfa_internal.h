@@ -114,4 +114,12 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           float softmax_scale, int causal, float* out, float* lse,
                           hipStream_t stream, int bits = 4);
 
+// Prefill over asymmetric group-wise 4-bit rows (codes and parameter words as
+// in DecodeAsym, groups of 32, 64 or 128 elements dividing D).
+hipError_t launch_prefill_asym(const uint16_t* q, const uint8_t* kc, const uint32_t* kp,
+                               const uint8_t* vc, const uint32_t* vp, int64_t B, int64_t Hq,
+                               int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D, int group,
+                               float softmax_scale, int causal, float* out, float* lse,
+                               hipStream_t stream);
+
 }  // namespace qkvfa

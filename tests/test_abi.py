@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version",
                           "qkv_quantize_append_kv_bits", "qkv_decode_bits", "qkv_quantize_append_kv_asym",
                           "qkv_decode_asym", "qkv_quantize_append_kv_heads", "qkv_decode_heads",
-                          "qkv_prefill_bits"}
+                          "qkv_prefill_bits", "qkv_prefill_asym"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -359,3 +359,21 @@ def test_prefill_bits_argument_errors(lib):
     assert pb(Sq=101) == 1        # causal needs Sq <= kv_len
     assert pb(L=129) == 1
     assert b"qkv_prefill_bits" in lib.qkv_last_error()
+
+
+def test_prefill_asym_argument_errors(lib):
+    i64, vp, f32, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.qkv_prefill_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
+    pa = lambda **kw: lib.qkv_prefill_asym(P, P, kw.get("kp", P), P, P, 1, 4, 2, kw.get("Sq", 10), kw.get("L", 100),
+                                           128, kw.get("D", 128), kw.get("g", 32), 0.1, kw.get("causal", 1), P, None,
+                                           None)
+    assert pa(g=16) == 2
+    assert pa(D=64, g=128) == 2   # group larger than the head dim
+    assert pa(D=96) == 2
+    assert pa(kp=None) == 1
+    assert pa(kp=P + 4) == 1      # four words per row: 16-byte aligned
+    assert pa(g=64, kp=P + 4) == 1   # two words: 8-byte aligned
+    assert pa(causal=2) == 1
+    assert pa(Sq=101) == 1        # causal needs Sq <= kv_len
+    assert pa(L=129) == 1
+    assert b"qkv_prefill_asym" in lib.qkv_last_error()

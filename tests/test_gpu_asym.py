@@ -170,3 +170,106 @@ def test_quantize_then_decode_end_to_end():
     vq = oracle.quantize_rows_asym(v, group)
     ro, _ = oracle.attention_asym(q, *kq, *vq, L, float(np.float32(1 / np.sqrt(D))), group)
     assert_close(out, ro, "quantize + decode")
+
+
+def _prefill_case(seed, B, Hq, Hkv, Sq, L, C, D, group):
+    """K with outlier channels and an offset (zero points matter); V offset
+    without outliers: with few visible keys (early causal rows) the fp16
+    rounding of P~ = p s_V bounds the error by max|v| 2^-11, which outlier
+    channels of magnitude ~40 would take past the tolerance."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, Sq, D)).astype(np.float32))
+    out = []
+    for shift, outl in ((0.4, True), (0.7, False)):
+        x = (rng.standard_normal((B, Hkv, C, D)) + shift).astype(np.float32)
+        if outl:
+            x[:, :, :, rng.choice(D, size=2, replace=False)] *= 8.0
+        c, s, z = oracle.quantize_rows_asym(x, group)
+        c[:, :, L:] = rng.integers(0, 256, size=c[:, :, L:].shape, dtype=np.uint8)   # garbage past kv_len
+        s[:, :, L:] = rng.integers(0, 0x7800, size=s[:, :, L:].shape, dtype=np.uint16)
+        z[:, :, L:] = rng.integers(0, 16, size=z[:, :, L:].shape, dtype=np.uint8)
+        out += [c, s, z]
+    return q, out
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, Sq, L, C, D, group, causal
+    (1, 8, 2, 300, 300, 320, 128, 32, True),
+    (1, 8, 2, 300, 300, 320, 128, 64, True),
+    (1, 8, 2, 300, 300, 320, 128, 128, True),
+    (2, 4, 4, 197, 197, 197, 64, 32, False),
+    (2, 4, 4, 197, 197, 197, 64, 64, False),
+    (1, 8, 2, 100, 700, 700, 128, 32, True),     # Sq < kv_len: bottom-right aligned
+    (1, 4, 1, 513, 600, 640, 64, 32, True),
+    (1, 4, 2, 70, 1000, 1024, 128, 64, False),
+    (1, 8, 8, 33, 33, 40, 128, 32, True),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(c) for c in PREFILL_CASES])
+def test_prefill_asym_matches_oracle(case):
+    B, Hq, Hkv, Sq, L, C, D, group, causal = case
+    q, arrs = _prefill_case(sum(case), B, Hq, Hkv, Sq, L, C, D, group)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = torch.full((B, Hq, Sq, D), float("nan"), device=DEV)
+    out, lse = qkv.prefill_asym(q_to_dev(q), _to_dev(arrs, group), L, causal, softmax_scale=scale,
+                                return_lse=True, out=out)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_asym(q, *arrs, L, scale, group, causal=causal)
+    assert_close(out, ro, f"prefill asym {case}")
+    assert compare(lse, rl)[0] < 1e-3
+
+
+@pytest.mark.parametrize("D,group", [(64, 64), (128, 128), (128, 32)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_symmetric_rows_embedded(D, group, causal):
+    """Symmetric int4 rows as asymmetric rows (codes + 8, zero point 8, the
+    row's scale for every group): the same fp16 operands, so with one group
+    per row the asymmetric prefill equals the int4 prefill bit for bit; with
+    several, the per-group scaling changes only the fp32 rounding order."""
+    B, Hq, Hkv, Sq, L = 1, 8, 2, 200, 260
+    q, kc, ks, vc, vs = random_case(9 + D + group, B, Hq, Hkv, Sq, L, D)
+    emb = lambda c: (c.astype(np.int64) ^ 0x88).astype(np.uint8)
+    ng = D // group
+    z = np.full((B, Hkv, L, ng), 8, np.uint8)
+    rep = lambda s_: np.repeat(s_[..., None], ng, axis=-1)
+    cache = qkv.AsymKVCache(*(torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (
+        oracle.to_cache_order(emb(kc), "k"), _params(rep(ks), z),
+        oracle.to_cache_order(emb(vc), "v"), _params(rep(vs), z))), group=group)
+    sym = qkv.KVCache(*(torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (
+        kc, ks.view(np.float16), vc, vs.view(np.float16))))
+    oa = qkv.prefill_asym(q_to_dev(q), cache, L, causal)
+    os_ = qkv.prefill(q_to_dev(q), sym, L, causal)
+    torch.cuda.synchronize()
+    if ng == 1:
+        assert torch.equal(oa, os_)
+    else:
+        d = (oa - os_).abs()
+        assert float(d.max()) < 1e-4 and float(d.mean()) < 1e-5
+    ro, _ = oracle.attention(q, kc, ks, vc, vs, L, float(np.float32(1 / np.sqrt(D))), causal=causal)
+    assert_close(oa, ro, "embedded symmetric rows")
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_prefill_asym_causal_16k_sampled(group):
+    """The causal prefill workload's shape (32/8 heads, D 128, 16384 tokens)
+    over asymmetric rows quantized on the GPU, checked on sampled query rows
+    of every head."""
+    B, Hq, Hkv, L, D = 1, 32, 8, 16384, 128
+    rng = np.random.default_rng(60 + group)
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, L, D)).astype(np.float32))
+    k = (rng.standard_normal((B, Hkv, L, D)) + 0.3).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    cache = qkv.AsymKVCache.empty(B, Hkv, L, D, group, device=DEV)
+    qkv.quantize_append_kv_asym(torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV), cache, 0)
+    out = qkv.prefill_asym(q_to_dev(q), cache, L, True)
+    torch.cuda.synchronize()
+    kq = oracle.quantize_rows_asym(k, group)
+    vq = oracle.quantize_rows_asym(v, group)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    errs = []
+    for r in [0, 1, 63, 64, 4095, 8191, 12000, L - 1]:
+        ro, _ = oracle.attention_asym(q[:, :, r:r + 1], *kq, *vq, r + 1, scale, group)   # row r sees keys [0, r]
+        errs.append(np.abs(out[:, :, r:r + 1].cpu().double().numpy() - ro))
+    e = np.concatenate([x.ravel() for x in errs])
+    assert e.max() <= 4e-3 and e.mean() <= 4e-4, (e.max(), e.mean())
