@@ -418,6 +418,22 @@ qkv_status qkv_prefill_bits(const uint16_t* q,
                             int64_t C, int64_t D, int bits, float softmax_scale, int causal,
                             float* out, float* lse, void* stream);
 
+/* qkv_prefill for the query heads of the listed KV heads (the per-head widths
+ * of qkv_decode_heads: a cache of Hkv_sub heads at `bits` bits, cache head i
+ * being KV head kv_heads[i] of a layer of Hkv KV heads; ids outside [0, Hkv)
+ * are clamped).  q, out, lse are the layer's [B, Hq, Sq, D] / [B, Hq, Sq];
+ * only the rows of the listed heads' query heads are written, so one call
+ * per width covers the layer.  Requires bits in {2, 3, 4}
+ * (QKV_ERR_UNSUPPORTED otherwise), 1 <= Hkv_sub <= Hkv, kv_heads non-null and
+ * 4-byte aligned (QKV_ERR_INVALID_ARG), and the qkv_prefill requirements. */
+qkv_status qkv_prefill_heads(const uint16_t* q,
+                             const uint8_t* k_codes, const uint16_t* k_scales,
+                             const uint8_t* v_codes, const uint16_t* v_scales,
+                             const int32_t* kv_heads, int64_t Hkv_sub,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                             int64_t C, int64_t D, int bits, float softmax_scale, int causal,
+                             float* out, float* lse, void* stream);
+
 /* qkv_prefill over asymmetric group-wise 4-bit rows (the layout and parameter
  * words of qkv_decode_asym; TurboAttention §2.3 and §3.1).  Codes enter LDS
  * as exact fp16 code - z; with one group per row the K scale multiplies

@@ -38,9 +38,12 @@ __all__ = [
     "quantize_append_kv_heads",
     "decode_heads",
     "decode_mixed",
+    "prefill_heads",
+    "prefill_mixed",
     "AsymKVCache",
     "quantize_append_kv_asym",
     "decode_asym",
+    "prefill_asym",
     "prefill",
     "decode_workspace_bytes",
     "decode_auto_splits",
@@ -115,6 +118,9 @@ def _load():
                                      vp, vp, vp, sz, vp]
     lib.qkv_prefill_bits.restype = ci
     lib.qkv_prefill_bits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
+    lib.qkv_prefill_heads.restype = ci
+    lib.qkv_prefill_heads.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                      vp, vp, vp]
     lib.qkv_prefill_asym.restype = ci
     lib.qkv_prefill_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci, vp, vp, vp]
     lib.qkv_decode_asym.restype = ci
@@ -388,6 +394,44 @@ def decode_mixed(q, parts, Hkv: int, kv_len, softmax_scale=None, num_splits=0, r
     out, lse = _outputs(q, out, lse, return_lse)
     for cache, heads, bits in parts:
         decode_heads(q, cache, heads, Hkv, kv_len, out, lse, softmax_scale, num_splits, bits=bits)
+    return (out, lse) if return_lse else out
+
+
+def prefill_heads(q, cache: "KVCache", kv_heads: torch.Tensor, Hkv: int, kv_len, causal, out, lse=None,
+                  softmax_scale=None, bits=4):
+    """Prefill for the query heads of the layer's KV heads ``kv_heads`` (int32, device) over a
+    ``bits``-bit cache holding those heads; writes their rows of ``out`` (and ``lse``) only.
+    ``q``/``out`` are the layer's ``[B, Hq, Sq, D]``; ``Hkv`` is the layer's KV head count."""
+    _req(q, "q", torch.bfloat16, 4)
+    B, Hq, Sq, D = q.shape
+    kv_heads = _heads_arg(kv_heads, q.device)
+    Hs = kv_heads.numel()
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    kc, ks, vc, vs = cache.tensors()
+    for name, t, dt, nd in (("k_codes", kc, torch.uint8, 4), ("k_scales", ks, torch.float16, 3),
+                            ("v_codes", vc, torch.uint8, 4), ("v_scales", vs, torch.float16, 3)):
+        _req(t, name, dt, nd)
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    if kc.shape[:2] != (B, Hs) or kc.shape[3] * 8 != D * bits or vc.shape != kc.shape or \
+            ks.shape != kc.shape[:3] or vs.shape != ks.shape:
+        raise ValueError("cache shape does not match q and kv_heads")
+    out, lse = _outputs(q, out, lse, False)
+    _check(_lib.qkv_prefill_heads(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), _ptr(kv_heads), Hs, B, Hq, Hkv,
+                                  Sq, int(kv_len), kc.shape[2], D, int(bits), _scale(softmax_scale, D),
+                                  int(bool(causal)), _ptr(out), _ptr(lse), _stream(q)))
+    return out
+
+
+def prefill_mixed(q, parts, Hkv: int, kv_len, causal, softmax_scale=None, return_lse=False, out=None, lse=None):
+    """Prefill of a layer whose KV heads are kept at different widths: ``parts`` is a list of
+    ``(cache, kv_heads, bits)`` covering the layer's ``Hkv`` KV heads once (one launch per part)."""
+    if sum(int(h.numel()) for _, h, _ in parts) != Hkv:
+        raise ValueError("the parts' head lists must cover the layer's KV heads once")
+    out, lse = _outputs(q, out, lse, return_lse)
+    for cache, heads, bits in parts:
+        prefill_heads(q, cache, heads, Hkv, kv_len, causal, out, lse, softmax_scale, bits=bits)
     return (out, lse) if return_lse else out
 
 

@@ -516,7 +516,8 @@ static qkv_status prefill_common(const uint16_t* q, const uint8_t* k_codes, cons
                                  const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
                                  int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
                                  float softmax_scale, int causal, float* out, float* lse, void* stream, int bits,
-                                 const char* fn, int group = 0) {
+                                 const char* fn, int group = 0, const int32_t* kv_heads = nullptr,
+                                 int64_t Hkv_sub = 0) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -537,9 +538,9 @@ static qkv_status prefill_common(const uint16_t* q, const uint8_t* k_codes, cons
                                                  static_cast<hipStream_t>(stream)),
                       fn);
   }
-  return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq,
-                                          kv_len, C, (int)D, softmax_scale, causal, out, lse,
-                                          static_cast<hipStream_t>(stream), bits),
+  return hip_status(qkvfa::launch_prefill(q, k_codes, k_scales, v_codes, v_scales, B, Hq,
+                                          kv_heads ? Hkv_sub : Hkv, Sq, kv_len, C, (int)D, softmax_scale, causal,
+                                          out, lse, static_cast<hipStream_t>(stream), bits, kv_heads, Hkv),
                     fn);
 }
 
@@ -559,6 +560,20 @@ qkv_status qkv_prefill_bits(const uint16_t* q, const uint8_t* k_codes, const uin
     return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill_bits: bits must be 2, 3 or 4");
   return prefill_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
                         causal, out, lse, stream, bits, "qkv_prefill_bits");
+}
+
+qkv_status qkv_prefill_heads(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                             const uint8_t* v_codes, const uint16_t* v_scales, const int32_t* kv_heads,
+                             int64_t Hkv_sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                             int64_t C, int64_t D, int bits, float softmax_scale, int causal, float* out,
+                             float* lse, void* stream) {
+  if (bits != 2 && bits != 3 && bits != 4)
+    return fail(QKV_ERR_UNSUPPORTED, "qkv_prefill_heads: bits must be 2, 3 or 4");
+  if (Hkv_sub < 1 || Hkv_sub > Hkv) return fail(QKV_ERR_INVALID_ARG, "qkv_prefill_heads: need 1 <= Hkv_sub <= Hkv");
+  if (!kv_heads || !aligned(kv_heads, 4))
+    return fail(QKV_ERR_INVALID_ARG, "qkv_prefill_heads: null or misaligned kv_heads");
+  return prefill_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
+                        causal, out, lse, stream, bits, "qkv_prefill_heads", 0, kv_heads, Hkv_sub);
 }
 
 qkv_status qkv_prefill_asym(const uint16_t* q, const uint8_t* k_codes, const uint32_t* k_params,

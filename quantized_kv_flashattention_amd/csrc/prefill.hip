@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
     const uint16_t* __restrict__ vs, const uint32_t* __restrict__ kp, const uint32_t* __restrict__ vp,
-    int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C,
+    const int32_t* __restrict__ kv_heads, int Hkv_all, int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C,
     float qk_log2, int nqb, float* __restrict__ out, float* __restrict__ lse_out) {
   // Asymmetric group-wise rows (NGA groups per row): unsigned nibbles in the
   // cache's K and V row orders and parameter words kp/vp [B, Hkv, C, NGA]
@@ -133,10 +133,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ float s_cmax[2];                      // max |csk| of the tile
   __shared__ __align__(16) float s_ones[BN];
 
-  const int h = blockIdx.x;
+  const int h = blockIdx.x;   // query head of this call: KV head h / G of the cache
   const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.y) : (int)blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / G;
+  // head map (kv_heads != nullptr): the cache holds KV heads kv_heads[0 ..
+  // Hkv) of a layer of Hkv_all (ids clamped into range); q, out and lse are
+  // the layer's, and this workgroup's query head there is hq
+  const int hq = kv_heads ? min(max(__builtin_amdgcn_readfirstlane(kv_heads[g]), 0), Hkv_all - 1) * G + (h - g * G)
+                          : h;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31;
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // 8 (2 s + j) + perm8(e), matching K chunk plane 2 s + j.
   half8v qop[KS];
   if (qrow < Sq) {
-    const uint16_t* qr = q + (((int64_t)b * Hq + h) * Sq + qrow) * D;
+    const uint16_t* qr = q + (((int64_t)b * Hq + hq) * Sq + qrow) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const uint4v w = *reinterpret_cast<const uint4v*>(qr + 8 * (2 * s + j));
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float l = xor_sum(l_run, 32);
   if (qrow < Sq) {
     const float inv = 1.0f / l;
-    float* orow = out + (((int64_t)b * Hq + h) * Sq + qrow) * D;
+    float* orow = out + (((int64_t)b * Hq + hq) * Sq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
     if (j == 0 && lse_out)
-      lse_out[((int64_t)b * Hq + h) * Sq + qrow] = (m_ref + log2f(l)) * kLn2;
+      lse_out[((int64_t)b * Hq + hq) * Sq + qrow] = (m_ref + log2f(l)) * kLn2;
   }
 }
 
@@ -633,6 +638,8 @@ struct PrefillArgs {
   const uint16_t* vs;
   const uint32_t* kp;   // asymmetric rows: parameter words
   const uint32_t* vp;
+  const int32_t* kv_heads;   // head map (or nullptr): the cache's Hkv heads among the layer's Hkv_all
+  int64_t Hkv_all;
   int64_t B, Hq, Hkv, Sq, kv_len, C;
   float qk_log2;
   float* out;
@@ -643,10 +650,11 @@ template <int D, int NW, bool CAUSAL, int BITS, int NGA = 0>
 hipError_t launch1(const PrefillArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * NW;
   const int nqb = (int)((a.Sq + BM - 1) / BM);
-  dim3 grid((uint32_t)a.Hq, (uint32_t)nqb, (uint32_t)a.B);
+  const int64_t G = a.Hq / a.Hkv_all;
+  dim3 grid((uint32_t)(a.Hkv * G), (uint32_t)nqb, (uint32_t)a.B);
   prefill_kernel<D, NW, CAUSAL, BITS, NGA><<<grid, dim3(64 * NW), 0, stream>>>(
-      a.q, a.kc, a.ks, a.vc, a.vs, a.kp, a.vp, (int)a.Hq, (int)a.Hkv, (int)(a.Hq / a.Hkv), (int)a.Sq,
-      (int)a.kv_len, a.C, a.qk_log2, nqb, a.out, a.lse);
+      a.q, a.kc, a.ks, a.vc, a.vs, a.kp, a.vp, a.kv_heads, (int)a.Hkv_all, (int)a.Hq, (int)a.Hkv, (int)G,
+      (int)a.Sq, (int)a.kv_len, a.C, a.qk_log2, nqb, a.out, a.lse);
   return hipGetLastError();
 }
 
@@ -679,9 +687,9 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                           float softmax_scale, int causal, float* out, float* lse,
-                          hipStream_t stream, int bits) {
-  const PrefillArgs a = {q, kc, ks, vc, vs, nullptr, nullptr, B, Hq, Hkv, Sq, kv_len, C,
-                         softmax_scale * kLog2e, out, lse};
+                          hipStream_t stream, int bits, const int32_t* kv_heads, int64_t Hkv_all) {
+  const PrefillArgs a = {q, kc, ks, vc, vs, nullptr, nullptr, kv_heads, kv_heads ? Hkv_all : Hkv, B, Hq, Hkv, Sq,
+                         kv_len, C, softmax_scale * kLog2e, out, lse};
   return launch_any(a, D, causal, stream, bits, 0);
 }
 
@@ -690,7 +698,7 @@ hipError_t launch_prefill_asym(const uint16_t* q, const uint8_t* kc, const uint3
                                int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D, int group,
                                float softmax_scale, int causal, float* out, float* lse,
                                hipStream_t stream) {
-  const PrefillArgs a = {q, kc, nullptr, vc, nullptr, kp, vp, B, Hq, Hkv, Sq, kv_len, C,
+  const PrefillArgs a = {q, kc, nullptr, vc, nullptr, kp, vp, nullptr, Hkv, B, Hq, Hkv, Sq, kv_len, C,
                          softmax_scale * kLog2e, out, lse};
   return launch_any(a, D, causal, stream, 4, D / group);
 }

@@ -112,7 +112,8 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           const uint8_t* vc, const uint16_t* vs, int64_t B, int64_t Hq,
                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                           float softmax_scale, int causal, float* out, float* lse,
-                          hipStream_t stream, int bits = 4);
+                          hipStream_t stream, int bits = 4, const int32_t* kv_heads = nullptr,
+                          int64_t Hkv_all = 0);
 
 // Prefill over asymmetric group-wise 4-bit rows (codes and parameter words as
 // in DecodeAsym, groups of 32, 64 or 128 elements dividing D).

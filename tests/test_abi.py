@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "qkv_decode_auto_splits", "qkv_last_error", "qkv_status_string", "qkv_version",
                           "qkv_quantize_append_kv_bits", "qkv_decode_bits", "qkv_quantize_append_kv_asym",
                           "qkv_decode_asym", "qkv_quantize_append_kv_heads", "qkv_decode_heads",
-                          "qkv_prefill_bits", "qkv_prefill_asym"}
+                          "qkv_prefill_bits", "qkv_prefill_asym", "qkv_prefill_heads"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -377,3 +377,21 @@ def test_prefill_asym_argument_errors(lib):
     assert pa(Sq=101) == 1        # causal needs Sq <= kv_len
     assert pa(L=129) == 1
     assert b"qkv_prefill_asym" in lib.qkv_last_error()
+
+
+def test_prefill_heads_argument_errors(lib):
+    i64, vp, f32, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.qkv_prefill_heads.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, ci, f32, ci,
+                                      vp, vp, vp]
+    ph = lambda **kw: lib.qkv_prefill_heads(P, P, P, P, P, kw.get("heads", P), kw.get("hs", 2), 1, 8, 4,
+                                            kw.get("Sq", 10), kw.get("L", 100), 128, 128, kw.get("bits", 2), 0.1,
+                                            kw.get("causal", 1), P, None, None)
+    assert ph(bits=1) == 2
+    assert ph(hs=0) == 1
+    assert ph(hs=5) == 1          # more heads than the layer has
+    assert ph(heads=None) == 1
+    assert ph(heads=P + 2) == 1
+    assert ph(causal=2) == 1
+    assert ph(Sq=101) == 1        # causal needs Sq <= kv_len
+    assert ph(L=129) == 1
+    assert b"qkv_prefill_heads" in lib.qkv_last_error()

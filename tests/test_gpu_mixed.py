@@ -125,3 +125,69 @@ def test_other_heads_untouched():
     assert torch.all(out[:, others] == 7.0) and torch.all(lse[:, others] == 7.0)
     qi, o, _ = _oracle_part(q, k, v, ids, 2, L, float(np.float32(1 / np.sqrt(D))), G)
     assert_close(out[:, qi], o, "head subset")
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, Sq, L, D, low-bit heads, low bits, causal
+    (1, 32, 8, 300, 300, 128, [1, 4, 6], 2, True),
+    (2, 8, 4, 197, 197, 64, [2], 3, False),
+    (1, 16, 8, 100, 500, 128, [7, 0], 2, True),      # Sq < kv_len
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(c) for c in PREFILL_CASES])
+def test_mixed_prefill_matches_oracle(case):
+    B, Hq, Hkv, Sq, L, D, lo_ids, lo_bits, causal = case
+    G = Hq // Hkv
+    q, k, v = _layer(sum(case[:6]), B, Hq, Hkv, Sq, L, D)
+    hi_ids = [h for h in range(Hkv) if h not in lo_ids]
+    scale = float(np.float32(1 / np.sqrt(D)))
+    parts, want_o, want_l = [], np.full((B, Hq, Sq, D), np.nan), np.full((B, Hq, Sq), np.nan)
+    for ids, bits in ((lo_ids, lo_bits), (hi_ids, 4)):
+        cache = qkv.KVCache.empty(B, len(ids), L, D, device=DEV, bits=bits)
+        qkv.quantize_append_kv_heads(_dev(k), _dev(v), cache, _heads(ids), 0, bits=bits)
+        parts.append((cache, _heads(ids), bits))
+        qi = [h * G + i for h in ids for i in range(G)]
+        kc, ks = oracle.quantize_rows_bits(k[:, ids], bits)
+        vc, vs = oracle.quantize_rows_bits(v[:, ids], bits)
+        want_o[:, qi], want_l[:, qi] = oracle.attention_bits(q[:, qi], kc, ks, vc, vs, L, scale, bits, causal=causal)
+    out = torch.full((B, Hq, Sq, D), float("nan"), device=DEV)
+    out, lse = qkv.prefill_mixed(q_to_dev(q), parts, Hkv, L, causal, softmax_scale=scale, return_lse=True, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "a query row was not written"
+    assert_close(out, want_o, f"mixed prefill {case}")
+    assert compare(lse, want_l)[0] < 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_head_map_is_plain_prefill(causal):
+    B, Hq, Hkv, Sq, L, D = 1, 16, 4, 250, 250, 128
+    q, k, v = _layer(5 + causal, B, Hq, Hkv, Sq, L, D)
+    plain = qkv.KVCache.empty(B, Hkv, L, D, device=DEV)
+    qkv.quantize_append_kv(_dev(k), _dev(v), plain, 0)
+    out = torch.empty((B, Hq, Sq, D), device=DEV)
+    lse = torch.empty((B, Hq, Sq), device=DEV)
+    qkv.prefill_heads(q_to_dev(q), plain, _heads(list(range(Hkv))), Hkv, L, causal, out, lse=lse)
+    ro, rl = qkv.prefill(q_to_dev(q), plain, L, causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ro) and torch.equal(lse, rl)
+
+
+def test_prefill_other_heads_untouched():
+    B, Hq, Hkv, Sq, L, D = 1, 16, 8, 130, 130, 64
+    q, k, v = _layer(6, B, Hq, Hkv, Sq, L, D)
+    ids = [5, 2]
+    cache = qkv.KVCache.empty(B, 2, L, D, device=DEV, bits=3)
+    qkv.quantize_append_kv_heads(_dev(k), _dev(v), cache, _heads(ids), 0, bits=3)
+    out = torch.full((B, Hq, Sq, D), 7.0, device=DEV)
+    lse = torch.full((B, Hq, Sq), 7.0, device=DEV)
+    qkv.prefill_heads(q_to_dev(q), cache, _heads(ids), Hkv, L, True, out, lse=lse, bits=3)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    mine = [h * G + i for h in ids for i in range(G)]
+    others = [h for h in range(Hq) if h not in mine]
+    assert torch.all(out[:, others] == 7.0) and torch.all(lse[:, others] == 7.0)
+    kc, ks = oracle.quantize_rows_bits(k[:, ids], 3)
+    vc, vs = oracle.quantize_rows_bits(v[:, ids], 3)
+    o, _ = oracle.attention_bits(q[:, mine], kc, ks, vc, vs, L, float(np.float32(1 / np.sqrt(D))), 3, causal=True)
+    assert_close(out[:, mine], o, "head subset")
