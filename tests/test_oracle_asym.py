@@ -191,3 +191,48 @@ def test_cache_order_round_trip(D, tensor):
     assert np.array_equal(from_cache_order(t, tensor), c)
     # slot n of the stored row holds element cache_order[n]
     assert np.array_equal(unpack_asym(t), unpack_asym(c)[..., cache_order(D, tensor)])
+
+
+def _py_asym_row(codes_row, scale_bits, zeros, group):
+    """One packed row in element order -> its values, scalar Python (s (u - z) per group)."""
+    from test_oracle_attention import _py_f16
+    us = []
+    for byte in codes_row:
+        us += [int(byte) & 0xF, int(byte) >> 4]
+    return [_py_f16(scale_bits[e // group]) * (u - int(zeros[e // group])) for e, u in enumerate(us)]
+
+
+@pytest.mark.parametrize("group", [4, 8])
+@pytest.mark.parametrize("Hq,Hkv,Sq,L,causal", [(4, 2, 3, 12, False), (4, 2, 5, 12, True), (6, 3, 2, 9, True)])
+def test_attention_asym_brute_force(group, Hq, Hkv, Sq, L, causal):
+    """Several groups per row (D = 16): pure-Python scalar loops (math.exp,
+    math.fsum, struct-decoded fp16 scales and bf16 queries) against the oracle."""
+    import math
+    from test_oracle_attention import _py_bf16
+    rng = np.random.default_rng(group * 100 + Hq + Sq + L + causal)
+    B, D = 2, 16
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, Sq, D)).astype(np.float32))
+    k = (rng.standard_normal((B, Hkv, L + 2, D)) * rng.uniform(0.2, 3.0, size=(1, 1, 1, D)) + 0.5).astype(np.float32)
+    v = (rng.standard_normal((B, Hkv, L + 2, D)) - 0.3).astype(np.float32)
+    kc, ks, kz = quantize_rows_asym(k, group)
+    vc, vs, vz = quantize_rows_asym(v, group)
+    assert len(set(kz.ravel().tolist())) > 1 and len(set(ks[0, 0, 0].tolist())) > 1   # zero points and scales vary
+    scale = float(np.float32(0.41))
+    o, l = attention_asym(q, kc, ks, kz, vc, vs, vz, L, scale, group, causal=causal)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            K = [_py_asym_row(kc[b, g, j], ks[b, g, j], kz[b, g, j], group) for j in range(L)]
+            V = [_py_asym_row(vc[b, g, j], vs[b, g, j], vz[b, g, j], group) for j in range(L)]
+            for i in range(Sq):
+                qi = [_py_bf16(q[b, h, i, d]) for d in range(D)]
+                vis = [j for j in range(L) if (not causal) or j <= i + L - Sq]
+                sc = [math.fsum(qi[d] * K[j][d] for d in range(D)) * scale for j in vis]
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                den = math.fsum(e)
+                for d in range(D):
+                    want = math.fsum(e[t] * V[j][d] for t, j in enumerate(vis)) / den
+                    assert abs(o[b, h, i, d] - want) < 1e-12
+                assert abs(l[b, h, i] - (m + math.log(den))) < 1e-12
