@@ -143,6 +143,7 @@ CASES = [
     (1, 4, 1, 16, (700,), 128, 32, 16, 0),                   # 64 rows per group; new rows cross a page
     (3, 8, 2, 1, (0, 0, 40), 64, 32, 2, 5),                  # appends into empty sequences
     (2, 8, 8, 1, (20000, 17), 64, 32, 0, 1),                 # one split over 625 pages
+    (4, 8, 2, 1, (50, 700, 2500, 9000), 128, 64, 1, 40),    # 1, 3, 10, 36 live splits: both merge forms
 ]
 
 
