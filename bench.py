@@ -465,6 +465,32 @@ def bench_prefill(torch, qkv, w, iters, bits=4, group=0):
     return res
 
 
+def bench_hbm_context(torch, iters=10):
+    """Achievable-HBM context (not the headline's peak, which stays nominal):
+    a read-only reduction over 1 GiB and a 512 MiB device-to-device copy,
+    torch's own kernels, back to back with events around the batch."""
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("read_1GiB_sum", lambda: x.sum(), 1 << 30),
+                             ("copy_512MiB", lambda: y.copy_(x[: n // 2]), 2 * (1 << 29))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        res[name] = {"ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_quantize(torch, qkv, w, iters):
     from qkv_inputs import make_qkv
     _, k, _ = make_qkv(w)
@@ -686,6 +712,8 @@ def main():
             f"group{g}": bench_prefill(torch, qkv, workload("causal_prefill_16k"), 6, group=g) for g in (128, 64, 32)}
         log("prefill asym:", json.dumps(secondary["causal_prefill_16k_asym"]))
     if args.only == "all":
+        secondary["hbm_context"] = bench_hbm_context(torch)
+        log("hbm context:", json.dumps(secondary["hbm_context"]))
         secondary["quantize_append"] = bench_quantize(torch, qkv, w3, 20)
         log("quantize:", json.dumps(secondary["quantize_append"]))
 
