@@ -273,3 +273,18 @@ def test_prefill_asym_causal_16k_sampled(group):
         errs.append(np.abs(out[:, :, r:r + 1].cpu().double().numpy() - ro))
     e = np.concatenate([x.ravel() for x in errs])
     assert e.max() <= 4e-3 and e.mean() <= 4e-4, (e.max(), e.mean())
+
+
+@pytest.mark.parametrize("D,group", [(64, 32), (128, 64), (128, 32)])
+@pytest.mark.parametrize("L,Sq,causal", [(1, 1, True), (1, 1, False), (63, 63, True), (64, 64, True),
+                                         (65, 65, True), (129, 129, False), (200, 1, True)])
+def test_prefill_asym_length_edges(D, group, L, Sq, causal):
+    """A single key, lengths at and around the 64-token tile, and one query row
+    against a longer cache (causal: it sees every key)."""
+    B, Hq, Hkv = 1, 4, 2
+    q, arrs = _prefill_case(L * 7 + Sq + D + group + causal, B, Hq, Hkv, Sq, L, L + 5, D, group)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = qkv.prefill_asym(q_to_dev(q), _to_dev(arrs, group), L, causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    ro, _ = oracle.attention_asym(q, *arrs, L, scale, group, causal=causal)
+    assert_close(out, ro, f"asym prefill L={L} Sq={Sq} causal={causal} D={D} g={group}")
