@@ -62,6 +62,15 @@ template <int N>
 struct IntTag {
   static constexpr int value = N;
 };
+
+// DPP move of a float inside 16-lane rows: lanes of the banks in BANK (bit k:
+// lanes 4k..4k+3 of each row) take src from the lane CTRL names, the others
+// keep old.  CTRL: 0x100 + n = row_shl:n (from lane + n), 0x110 + n =
+// row_shr:n (from lane - n), 0x120 + n = row_ror:n.
+template <int CTRL, int BANK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+  return bitcast<float>(__builtin_amdgcn_update_dpp(bitcast<int>(old), bitcast<int>(src), CTRL, 0xF, BANK, false));
+}
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
@@ -269,6 +278,9 @@ void decode_kernel(const DecodeArgs a) {
   const int gq = a.kv_heads ? min(max(__builtin_amdgcn_readfirstlane(a.kv_heads[g]), 0), a.Hkv_all - 1) : g;
   const int R = G * Sq;
   const int rows_o = min(16, R);   // rows per wave in the merge buffer
+  // At most 4 query rows in the one 16-row block: the softmax runs on packed
+  // scores (2 per lane instead of 8, the other 48 lanes' rows being padding)
+  const bool packed_sm = !ASYM && NB == 1 && R <= 4;
   const bool append = a.k_new != nullptr;
   // rows this sequence attends, and where its new rows start (append mode)
   int pos_b = a.pos;
@@ -379,7 +391,7 @@ void decode_kernel(const DecodeArgs a) {
       auto load_n = [&](int item, int part, int u0, auto& o) {
         const uint32_t off0 = item_off(item);
         constexpr int n = sizeof(o) / sizeof(o[0]);
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < n; ++u) {
           const int sp = part + tpi * (u0 + u);
           const uint32_t off = sp < n_live ? off0 + (uint32_t)(sp * D * 4) : 0x80000000u;
@@ -390,13 +402,13 @@ void decode_kernel(const DecodeArgs a) {
       // together; an index past the live splits is clamped (its o[u] is zero)
       auto accumulate = [&](const float* wr, int part, int u0, const auto& o, float4v& acc) {
         constexpr int n = sizeof(o) / sizeof(o[0]);
-  #pragma unroll
+#pragma unroll
         for (int blk = 0; blk < n / 4; ++blk) {
           if (tpi * (u0 + 4 * blk) < n_live) {   // uniform
             float wv[4];
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) wv[i] = wr[min(part + tpi * (u0 + 4 * blk + i), n_live - 1)];
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) acc += wv[i] * o[4 * blk + i];
           }
         }
@@ -415,7 +427,7 @@ void decode_kernel(const DecodeArgs a) {
         const int total = R * n_live;
         for (int base = threadIdx.x; base < total; base += 64 * kWaves * 8) {
           float v[8];
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int idx = base + u * 64 * kWaves;
             v[u] = -INFINITY;
@@ -425,7 +437,7 @@ void decode_kernel(const DecodeArgs a) {
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
           }
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < 8; ++u)
             if (base + u * 64 * kWaves < total) s_w[base + u * 64 * kWaves] = v[u];
         }
@@ -436,7 +448,7 @@ void decode_kernel(const DecodeArgs a) {
         float* wr = s_w + row * n_live;
         float M = -INFINITY;
         for (int s = lane; s < n_live; s += 64) M = fmaxf(M, wr[s]);
-  #pragma unroll
+#pragma unroll
         for (int o = 32; o >= 1; o >>= 1) M = xor_max(M, o);
         float den = 0.0f;
         for (int s = lane; s < n_live; s += 64) {
@@ -444,7 +456,7 @@ void decode_kernel(const DecodeArgs a) {
           wr[s] = w;
           den += w;
         }
-  #pragma unroll
+#pragma unroll
         for (int o = 32; o >= 1; o >>= 1) den = xor_sum(den, o);
         if (lane == 0) {
           s_den[row] = den;
@@ -745,38 +757,81 @@ void decode_kernel(const DecodeArgs a) {
 
         // ---- online softmax per row block -> P^T operand (V scale folded in)
         half8v pop[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          float x[8];
-          float mloc = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x[e] = fmaf(s_t[nb][e >> 2][e & 3], csk[e], mbias[e]);
-            mloc = fmaxf(mloc, x[e]);
-          }
+        if (NB == 1 && packed_sm) {
+          // Packed: lane (j, 4a + b) takes slots 2a, 2a + 1 (tokens 8j + 2a,
+          // 8j + 2a + 1) of row b from lane (j, b) with three bank-masked
+          // row shifts per value; row maxima reduce over a with row rotations;
+          // P~ returns to the B-operand layout of lanes (j, b) with row shifts
+          // the other way.  l and s_run stay per lane (summed over a in the
+          // wave merge); m is the same on the lanes of a row.
+          const int e0 = 8 * j + 2 * (r >> 2);
+          const float2v c2 = *reinterpret_cast<const float2v*>(&s_sc[wave][e0]);
+          const float2v v2 = *reinterpret_cast<const float2v*>(&s_sc[wave][32 + e0]);
+          const float2v m2 = *reinterpret_cast<const float2v*>(&s_sc[wave][64 + e0]);
+          float y0 = s_t[0][0][0], y1 = s_t[0][0][1];
+          y0 = dpp_f<0x114, 0x2>(y0, s_t[0][0][2]);
+          y1 = dpp_f<0x114, 0x2>(y1, s_t[0][0][3]);
+          y0 = dpp_f<0x118, 0x4>(y0, s_t[0][1][0]);
+          y1 = dpp_f<0x118, 0x4>(y1, s_t[0][1][1]);
+          y0 = dpp_f<0x11C, 0x8>(y0, s_t[0][1][2]);
+          y1 = dpp_f<0x11C, 0x8>(y1, s_t[0][1][3]);
+          const float x0 = fmaf(y0, c2[0], m2[0]);
+          const float x1 = fmaf(y1, c2[1], m2[1]);
+          float mloc = fmaxf(x0, x1);
+          mloc = fmaxf(mloc, dpp_f<0x124>(mloc, mloc));
+          mloc = fmaxf(mloc, dpp_f<0x128>(mloc, mloc));
           mloc = xor_max(mloc, 16);
           mloc = xor_max(mloc, 32);
-          const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
-          const float alpha = fast_exp2(m_run[nb] - m_new);
-          float lsum = 0.0f;
-          uint4v pw;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(x[e] - m_new);
-            const float p1 = fast_exp2(x[e + 1] - m_new);
-            lsum += p0 + p1;
-            pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
-          }
-          pop[nb] = bitcast<half8v>(pw);
-          float ps = s_run[nb] * alpha;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) ps = __builtin_amdgcn_fdot2(bitcast<half2v>(pw[h]), half2v{1, 1}, ps, false);
-          s_run[nb] = ps;
-          l_run[nb] = l_run[nb] * alpha + lsum;
-          m_run[nb] = m_new;
+          const float m_new = fmaxf(m_run[0], mloc);   // finite: every chunk has a valid token
+          const float alpha = fast_exp2(m_run[0] - m_new);
+          const float p0 = fast_exp2(x0 - m_new);
+          const float p1 = fast_exp2(x1 - m_new);
+          const half2v q2 = cvt_pk_f16(p0 * v2[0], p1 * v2[1]);
+          const float qf = bitcast<float>(q2);
+          const uint4v pw = {bitcast<uint32_t>(qf), bitcast<uint32_t>(dpp_f<0x104>(0.0f, qf)),
+                             bitcast<uint32_t>(dpp_f<0x108>(0.0f, qf)), bitcast<uint32_t>(dpp_f<0x10C>(0.0f, qf))};
+          pop[0] = bitcast<half8v>(pw);
+          s_run[0] = __builtin_amdgcn_fdot2(q2, half2v{1, 1}, s_run[0] * alpha, false);
+          l_run[0] = l_run[0] * alpha + (p0 + p1);
+          m_run[0] = m_new;
           if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-            for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
+            for (int p = 0; p < NPB; ++p) o_acc[0][p] *= alpha;
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            float x[8];
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              x[e] = fmaf(s_t[nb][e >> 2][e & 3], csk[e], mbias[e]);
+              mloc = fmaxf(mloc, x[e]);
+            }
+            mloc = xor_max(mloc, 16);
+            mloc = xor_max(mloc, 32);
+            const float m_new = fmaxf(m_run[nb], mloc);   // finite: every chunk has a valid token
+            const float alpha = fast_exp2(m_run[nb] - m_new);
+            float lsum = 0.0f;
+            uint4v pw;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const float p0 = fast_exp2(x[e] - m_new);
+              const float p1 = fast_exp2(x[e + 1] - m_new);
+              lsum += p0 + p1;
+              pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
+            }
+            pop[nb] = bitcast<half8v>(pw);
+            float ps = s_run[nb] * alpha;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) ps = __builtin_amdgcn_fdot2(bitcast<half2v>(pw[h]), half2v{1, 1}, ps, false);
+            s_run[nb] = ps;
+            l_run[nb] = l_run[nb] * alpha + lsum;
+            m_run[nb] = m_new;
+            if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+              for (int p = 0; p < NPB; ++p) o_acc[nb][p] *= alpha;
+            }
           }
         }
 
@@ -1013,6 +1068,12 @@ void decode_kernel(const DecodeArgs a) {
     // ---- merge the eight waves through LDS, one 16-row block at a time
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
+      if (NB == 1 && packed_sm) {   // per-lane sums of the packed softmax: add the four lanes of a row
+        l_run[0] += dpp_f<0x124>(l_run[0], l_run[0]);
+        l_run[0] += dpp_f<0x128>(l_run[0], l_run[0]);
+        s_run[0] += dpp_f<0x124>(s_run[0], s_run[0]);
+        s_run[0] += dpp_f<0x128>(s_run[0], s_run[0]);
+      }
       float l = xor_sum(l_run[nb], 16);
       l = xor_sum(l, 32);
       if constexpr (ASYM) {
