@@ -236,3 +236,17 @@ def test_decode_append_steps_reuse_workspace():
         assert int((ws[:64] != 0).sum()) == 0, "tickets not returned to zero"
     for a, b in zip(sep.tensors(), fused.tensors()):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq", [(3, 1, 1), (2, 1, 2), (1, 1, 3), (4, 2, 2), (6, 2, 1), (5, 1, 1)])
+@pytest.mark.parametrize("ns", [0, 3])
+def test_row_counts_around_packed_softmax(Hq, Hkv, Sq, ns):
+    """Groups of 1-5 query rows (G x Sq): up to 4 rows the softmax runs on
+    scores packed two per lane, 5 rows use the unpacked path."""
+    B, L, D = 2, 1500, 128
+    q, kc, ks, vc, vs = random_case(Hq * 10 + Hkv + Sq, B, Hq, Hkv, Sq, L, D)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, lse = _run(q, (kc, ks, vc, vs), L, scale, ns)
+    ro, rl = oracle.attention(q, kc, ks, vc, vs, L, scale)
+    assert_close(out, ro, f"Hq={Hq} Hkv={Hkv} Sq={Sq} ns={ns}")
+    assert compare(lse, rl)[0] < 1e-3
