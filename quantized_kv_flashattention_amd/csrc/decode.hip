@@ -58,6 +58,9 @@ namespace {
 // (256 per lane with eight waves) do not fit; it keeps four waves and gets
 // the whole register file of its SIMD slot.
 __host__ __device__ constexpr int waves_for(int NB) { return NB >= 4 ? 4 : 8; }
+// 16-row blocks of the kernel that runs R query rows per group: the
+// one-block kernel takes at most 8, so that hi/lo P~ chunks find free columns
+__host__ __device__ constexpr int row_blocks_for(int64_t R) { return R <= 8 ? 1 : R <= 32 ? 2 : 4; }
 template <int N>
 struct IntTag {
   static constexpr int value = N;
@@ -215,7 +218,10 @@ struct ChunkRegs {
 // skips the one-chunk prefetch to stay within 256 VGPRs.
 // (3-bit rows keep a second set of top-bit registers per chunk: their one
 // row-block variant asks for three waves per SIMD instead of four.)
-template <int D, int NB, bool PAGED, int BITS, int NGA>
+// PK: the one-block kernel for at most 4 query rows per group (symmetric
+// rows), whose softmax runs on packed scores; a kernel instantiation holds
+// one softmax layout only.
+template <int D, int NB, bool PAGED, int BITS, int NGA, bool PK>
 __global__ __launch_bounds__(64 * waves_for(NB))
 __attribute__((amdgpu_waves_per_eu(NB == 1 ? ((BITS == 3 || NGA > 0) ? 3 : 4) : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
@@ -248,6 +254,7 @@ void decode_kernel(const DecodeArgs a) {
   // weights: dynamic, sized by the launch for the rows this call has
   extern __shared__ __align__(16) float s_o[];
   __shared__ int s_last;
+  __shared__ int s_qwide[kWaves];   // query range check, per wave
   __shared__ float s_den[64];
   __shared__ float s_tm[64];    // buffer split: per-row score maximum
   // append mode: this split's new rows, indexed by row - pos
@@ -280,7 +287,10 @@ void decode_kernel(const DecodeArgs a) {
   const int rows_o = min(16, R);   // rows per wave in the merge buffer
   // At most 4 query rows in the one 16-row block: the softmax runs on packed
   // scores (2 per lane instead of 8, the other 48 lanes' rows being padding)
-  const bool packed_sm = !ASYM && NB == 1 && R <= 4;
+  static_assert(!PK || (NB == 1 && !ASYM), "packed softmax: one row block, symmetric rows");
+  // At most 8 query rows otherwise: rows r < 8 are duplicated into columns
+  // r + 8 of the block, whose lanes carry the low halves of hi/lo P~ chunks
+  constexpr bool dup_rows = NB == 1 && !PK;   // (the launch gives this kernel at most 8 rows)
   const bool append = a.k_new != nullptr;
   // rows this sequence attends, and where its new rows start (append mode)
   int pos_b = a.pos;
@@ -625,25 +635,55 @@ void decode_kernel(const DecodeArgs a) {
     // Converted once into LDS (shared by the eight waves): 16-byte chunk c of
     // row x sits at chunk c ^ (x % 16), so the 16 rows a wave reads together
     // fall in different banks.
-    for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 64 * kWaves) {
-      const int row = idx / DW;
-      const int c = idx - row * DW;
-      half8v h = half8v{};
-      if (row < R) {
-        const uint16_t* qr = a.q + (grow0 + row) * D + 8 * c;
-        const uint4v w = *reinterpret_cast<const uint4v*>(qr);
-        uint16_t e16[8];
+    // An element of magnitude 65536 or more (past fp16 range) anywhere in the
+    // group: the whole group's query is converted again, scaled by an exact
+    // power of two 2^-qshift, and the score scale qk carries 2^qshift.
+    auto convert_q = [&](float qmul) {
+      uint32_t mb = 0;
+      for (int idx = threadIdx.x; idx < NB * 16 * DW; idx += 64 * kWaves) {
+        const int row = idx / DW;
+        const int c = idx - row * DW;
+        half8v h = half8v{};
+        const int src = (dup_rows && row >= 8) ? row - 8 : row;
+        if (src < R) {
+          const uint16_t* qr = a.q + (grow0 + src) * D + 8 * c;
+          const uint4v w = *reinterpret_cast<const uint4v*>(qr);
+          mb = max(mb, bf16x8_max_abs_bits(w));
+          uint16_t e16[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
-          e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
+          for (int t = 0; t < 4; ++t) {
+            e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
+            e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (_Float16)(bf16_to_f32(e16[perm8(e)]) * qmul);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (_Float16)bf16_to_f32(e16[perm8(e)]);
+        *reinterpret_cast<half8v*>(&s_q[(row * DW + (c ^ (row & 15 & (DW - 1)))) * 8]) = h;
       }
-      *reinterpret_cast<half8v*>(&s_q[(row * DW + (c ^ (row & 15 & (DW - 1)))) * 8]) = h;
-    }
+      return mb;
+    };
+    const bool q_wide = __builtin_amdgcn_ballot_w64(convert_q(1.0f) >= 0x4780u) != 0;   // >= 65536
+    if (lane == 0) s_qwide[wave] = q_wide ? 1 : 0;
     __syncthreads();
+    int qshift = 0;
+    {
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) any |= s_qwide[w];
+      if (any) {   // rare: find the group's largest |q|, convert again
+        __syncthreads();
+        const uint32_t mb = convert_q(1.0f);   // (values rewritten unchanged)
+        if (lane == 0) s_qwide[wave] = 0;
+        __syncthreads();
+        __hip_atomic_fetch_max(&s_qwide[0], (int)mb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __syncthreads();
+        qshift = q_range_shift((uint32_t)s_qwide[0]);
+        __syncthreads();
+        convert_q(exp2i(-qshift));
+        __syncthreads();
+      }
+    }
+    const float qk = a.qk_log2 * exp2i(qshift);   // score scale in log2 units
 
     // Codes enter the MFMAs as exact fp16 values c + b (the bias b depends on
     // the code's position only).  Scores: each QK accumulator starts at
@@ -706,7 +746,7 @@ void decode_kernel(const DecodeArgs a) {
         //      the score is one FMA on every chunk, full or not.
         // lanes 0-31: K column scale x softmax scale x log2 e; lanes 32-63: V scale
         const float scv = f16bits_to_f32(lane < 32 ? cr.sk : cr.sv);
-        s_sc[wave][lane] = lane < 32 ? scv * a.qk_log2 : scv;
+        s_sc[wave][lane] = lane < 32 ? scv * qk : scv;
         if (lane < 32) s_sc[wave][64 + lane] = (c0 + lane < lim) ? 0.0f : -INFINITY;
         const float4v ck0 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j]);
         const float4v ck1 = *reinterpret_cast<const float4v*>(&s_sc[wave][8 * j + 4]);
@@ -755,9 +795,77 @@ void decode_kernel(const DecodeArgs a) {
           }
         }
 
+        // the V codes as new values, so that a second PV pass converts them
+        // again instead of keeping the first pass's operands live
+        auto fresh_v = [&]() {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(cr.vw[e]));
+          if constexpr (BITS == 3) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(cr.vh[e]));
+          }
+        };
+        // ---- O^T += V^T P^T for the P operands pp of every row block
+        auto pv_products = [&](const half8v (&pp)[NB]) {
+          if constexpr (BITS == 4) {
+            // V operand of blocks 2k, 2k+1: byte k of the eight token dwords,
+            // low and high nibble -> exact fp16 (token e = k index)
+#pragma unroll
+            for (int k = 0; k < NPB / 2; ++k) {
+              uint4v wlo, whi;
+#pragma unroll
+              for (int hh = 0; hh < 4; ++hh) {
+                const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
+                wlo[hh] = nib_b72(xb << 4);
+                whi[hh] = nib_b72(xb);
+              }
+              const half8v vlo = bitcast<half8v>(wlo);
+              const half8v vhi = bitcast<half8v>(whi);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                o_acc[nb][2 * k] = mfma16x16x32(vlo, pp[nb], o_acc[nb][2 * k]);
+                o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pp[nb], o_acc[nb][2 * k + 1]);
+              }
+            }
+          } else {
+            // 2/3-bit rows.  V operand of block 4 k2 + f: the 2-bit field f of
+            // byte k2 of the eight tokens' low bits (3 bits: with top bit
+            // 4 k2 + f of their top-bit bytes)
+#pragma unroll
+            for (int k2 = 0; k2 < NPB / 4; ++k2) {
+              uint4v pr[4];   // pr[hh][f]: field f of tokens 2 hh, 2 hh + 1 (c + lowbit_bias(f))
+#pragma unroll
+              for (int hh = 0; hh < 4; ++hh) {
+                const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k2);
+                const uint32_t zb = BITS == 3 ? pair_bytes(cr.vh[2 * hh], cr.vh[2 * hh + 1], 0) >> (4 * k2) : 0u;
+                pr[hh] = lowbit4_b<BITS>(xb, zb);
+              }
+#pragma unroll
+              for (int f = 0; f < 4; ++f) {
+                const uint4v w = {pr[0][f], pr[1][f], pr[2][f], pr[3][f]};
+                const half8v vop = bitcast<half8v>(w);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                  o_acc[nb][4 * k2 + f] = mfma16x16x32(vop, pp[nb], o_acc[nb][4 * k2 + f]);
+              }
+            }
+          }
+        };
+
+        // A V scale of this chunk past the precision limit: P~ is taken as an
+        // fp16 hi/lo pair (see pv_lo).  With free columns in the 16-row
+        // block (at most 8 query rows), the low halves ride in them: the
+        // packed softmax puts row b's in column 4 + b, the unpacked one
+        // duplicates rows r < 8 into columns r + 8, whose lanes feed the low
+        // halves (zeros in other chunks); the wave merge adds those columns
+        // to their rows.  Otherwise the low halves get PV products of their own.
+        constexpr uint32_t kLimBits = pv_scale_limit_bits(pv_code_max(BITS, false));
+        const bool hilo = __builtin_amdgcn_ballot_w64(lane >= 32 && (uint32_t)cr.sv > kLimBits) != 0;
         // ---- online softmax per row block -> P^T operand (V scale folded in)
         half8v pop[NB];
-        if (NB == 1 && packed_sm) {
+        float pe[NB][8];    // probabilities of the unpacked softmax (for the low halves of hi/lo chunks)
+        half2v hw[NB][4];   // their high halves P~
+        if constexpr (PK) {
           // Packed: lane (j, 4a + b) takes slots 2a, 2a + 1 (tokens 8j + 2a,
           // 8j + 2a + 1) of row b from lane (j, b) with three bank-masked
           // row shifts per value; row maxima reduce over a with row rotations;
@@ -786,12 +894,26 @@ void decode_kernel(const DecodeArgs a) {
           const float alpha = fast_exp2(m_run[0] - m_new);
           const float p0 = fast_exp2(x0 - m_new);
           const float p1 = fast_exp2(x1 - m_new);
-          const half2v q2 = cvt_pk_f16(p0 * v2[0], p1 * v2[1]);
+          half2v q2 = cvt_pk_f16(p0 * v2[0], p1 * v2[1]);
+          if (hilo) pin_v(q2);   // the low halves below are taken about exactly these values
           const float qf = bitcast<float>(q2);
-          const uint4v pw = {bitcast<uint32_t>(qf), bitcast<uint32_t>(dpp_f<0x104>(0.0f, qf)),
-                             bitcast<uint32_t>(dpp_f<0x108>(0.0f, qf)), bitcast<uint32_t>(dpp_f<0x10C>(0.0f, qf))};
-          pop[0] = bitcast<half8v>(pw);
-          s_run[0] = __builtin_amdgcn_fdot2(q2, half2v{1, 1}, s_run[0] * alpha, false);
+          float pw[4] = {dpp_f<0xE4, 0x1>(0.0f, qf), dpp_f<0x104, 0x1>(0.0f, qf), dpp_f<0x108, 0x1>(0.0f, qf),
+                         dpp_f<0x10C, 0x1>(0.0f, qf)};
+          float ps = __builtin_amdgcn_fdot2(q2, half2v{1, 1}, s_run[0] * alpha, false);
+          if (hilo) {   // low halves P~_lo = fp16(p s_V - P~) (residuals exact in fp32)
+            asm volatile("");   // a real branch: not speculated into every chunk
+            const half2v lo2 = {pv_lo(p0, v2[0], q2[0]), pv_lo(p1, v2[1], q2[1])};
+            const float lf = bitcast<float>(lo2);
+            ps = __builtin_amdgcn_fdot2(lo2, half2v{1, 1}, ps, false);
+            pw[0] = dpp_f<0x114, 0x2>(pw[0], lf);
+            pw[1] = dpp_f<0xE4, 0x2>(pw[1], lf);
+            pw[2] = dpp_f<0x104, 0x2>(pw[2], lf);
+            pw[3] = dpp_f<0x108, 0x2>(pw[3], lf);
+          }
+          const uint4v pu = {bitcast<uint32_t>(pw[0]), bitcast<uint32_t>(pw[1]), bitcast<uint32_t>(pw[2]),
+                             bitcast<uint32_t>(pw[3])};
+          pop[0] = bitcast<half8v>(pu);
+          s_run[0] = ps;
           l_run[0] = l_run[0] * alpha + (p0 + p1);
           m_run[0] = m_new;
           if (__ballot(alpha != 1.0f)) {
@@ -799,6 +921,9 @@ void decode_kernel(const DecodeArgs a) {
             for (int p = 0; p < NPB; ++p) o_acc[0][p] *= alpha;
           }
         } else {
+          // lanes of duplicated rows (columns r + 8 of a block of at most 8
+          // rows): the low halves of P~ in hi/lo chunks, 0 in the others
+          const bool dup_lane = dup_rows && r >= 8;
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             float x[8];
@@ -819,7 +944,22 @@ void decode_kernel(const DecodeArgs a) {
               const float p0 = fast_exp2(x[e] - m_new);
               const float p1 = fast_exp2(x[e + 1] - m_new);
               lsum += p0 + p1;
-              pw[e / 2] = bitcast<uint32_t>(cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]));
+              pe[nb][e] = p0;
+              pe[nb][e + 1] = p1;
+              hw[nb][e / 2] = cvt_pk_f16(p0 * sv[e], p1 * sv[e + 1]);
+              pw[e / 2] = dup_lane ? 0u : bitcast<uint32_t>(hw[nb][e / 2]);
+            }
+            if (NB == 1 && hilo && dup_rows) {   // duplicated rows' lanes: the low halves
+              asm volatile("");   // a real branch: not speculated into every chunk
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                // about the high halves the row's own lane feeds (same
+                // instruction on identical inputs: the same values)
+                pin_v(hw[nb][h]);
+                const half2v lo = {pv_lo(pe[nb][2 * h], sv[2 * h], hw[nb][h][0]),
+                                   pv_lo(pe[nb][2 * h + 1], sv[2 * h + 1], hw[nb][h][1])};
+                pw[h] = dup_lane ? bitcast<uint32_t>(lo) : pw[h];
+              }
             }
             pop[nb] = bitcast<half8v>(pw);
             float ps = s_run[nb] * alpha;
@@ -835,48 +975,25 @@ void decode_kernel(const DecodeArgs a) {
           }
         }
 
-        if constexpr (BITS == 4) {
-          // ---- O^T += V^T P^T.  V operand of blocks 2k, 2k+1: byte k of the eight
-          //      token dwords, low and high nibble -> exact fp16 (token e = k index)
+        pv_products(pop);
+        if (NB > 1 && hilo) {   // no free columns: PV products of the low halves
 #pragma unroll
-          for (int k = 0; k < NPB / 2; ++k) {
-            uint4v wlo, whi;
+          for (int nb = 0; nb < NB; ++nb) {
+            uint4v lw;
 #pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-              const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
-              wlo[hh] = nib_b72(xb << 4);
-              whi[hh] = nib_b72(xb);
+            for (int h = 0; h < 4; ++h) {
+              pin_v(hw[nb][h]);
+              lw[h] = bitcast<uint32_t>(half2v{pv_lo(pe[nb][2 * h], sv[2 * h], hw[nb][h][0]),
+                                               pv_lo(pe[nb][2 * h + 1], sv[2 * h + 1], hw[nb][h][1])});
             }
-            const half8v vlo = bitcast<half8v>(wlo);
-            const half8v vhi = bitcast<half8v>(whi);
+            float pl = s_run[nb];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              o_acc[nb][2 * k] = mfma16x16x32(vlo, pop[nb], o_acc[nb][2 * k]);
-              o_acc[nb][2 * k + 1] = mfma16x16x32(vhi, pop[nb], o_acc[nb][2 * k + 1]);
-            }
+            for (int h = 0; h < 4; ++h) pl = __builtin_amdgcn_fdot2(bitcast<half2v>(lw[h]), half2v{1, 1}, pl, false);
+            s_run[nb] = pl;
+            pop[nb] = bitcast<half8v>(lw);
           }
-        } else {
-          // ---- O^T += V^T P^T for 2/3-bit rows.  V operand of block 4 k2 + f: the
-          //      2-bit field f of byte k2 of the eight tokens' low bits (3 bits:
-          //      with top bit 4 k2 + f of their top-bit bytes)
-#pragma unroll
-          for (int k2 = 0; k2 < NPB / 4; ++k2) {
-            uint4v pr[4];   // pr[hh][f]: field f of tokens 2 hh, 2 hh + 1 (c + lowbit_bias(f))
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-              const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k2);
-              const uint32_t zb = BITS == 3 ? pair_bytes(cr.vh[2 * hh], cr.vh[2 * hh + 1], 0) >> (4 * k2) : 0u;
-              pr[hh] = lowbit4_b<BITS>(xb, zb);
-            }
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-              const uint4v w = {pr[0][f], pr[1][f], pr[2][f], pr[3][f]};
-              const half8v vop = bitcast<half8v>(w);
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                o_acc[nb][4 * k2 + f] = mfma16x16x32(vop, pop[nb], o_acc[nb][4 * k2 + f]);
-            }
-          }
+          fresh_v();
+          pv_products(pop);
         }
     };
 
@@ -891,13 +1008,20 @@ void decode_kernel(const DecodeArgs a) {
     // sum P~_g (79 - z); the wave merge forms sg - O.
     auto process_chunk_asym = [&](int c0, Regs& cr, int lim) {
       if constexpr (ASYM) {
+        // a V group scale of this chunk past the precision limit: P~_g also
+        // gets its low fp16 half (see pv_lo)
+        constexpr uint32_t kLimBits = pv_scale_limit_bits(pv_code_max(4, true));
+        bool big = false;
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) big = big || (lane * NPW + u < 32 * NGA && (cr.vpw[u] & 0xFFFFu) > kLimBits);
+        const bool hilo = __builtin_amdgcn_ballot_w64(big) != 0;
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
           const int w = lane * NPW + u;   // token w / NGA, group w % NGA
           if (w < 32 * NGA) {
             const int t = w / NGA, gi = w % NGA;
             const uint32_t pk = cr.kpw[u], pv = cr.vpw[u];
-            s_ak[wave][0][gi][t] = -f16bits_to_f32((uint16_t)pk) * a.qk_log2;
+            s_ak[wave][0][gi][t] = -f16bits_to_f32((uint16_t)pk) * qk;
             s_ak[wave][1][gi][t] = 79.0f - (float)((pk >> 16) & 15u);
             s_av[wave][0][gi][t] = bitcast<_Float16>((uint16_t)pv);
             s_av[wave][1][gi][t] = bitcast<_Float16>((uint16_t)(0x5400u | ((15u - ((pv >> 16) & 15u)) << 4)));
@@ -978,14 +1102,48 @@ void decode_kernel(const DecodeArgs a) {
         for (int gi = 0; gi < NGA; ++gi) {
           const half8v sv = *reinterpret_cast<const half8v*>(&s_av[wave][0][gi][8 * j]);
           const uint4v bzv = *reinterpret_cast<const uint4v*>(&s_av[wave][1][gi][8 * j]);
+          // the group's PV blocks for P operands pp
+          auto pv_group = [&](const half8v (&pp)[NB]) {
+#pragma unroll
+            for (int kq = 0; kq < NPB / 2 / NGA; ++kq) {
+              const int k = gi * (NPB / 2 / NGA) + kq;
+              uint4v wlo, whi;
+#pragma unroll
+              for (int hh = 0; hh < 4; ++hh) {
+                const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
+                wlo[hh] = nib_n79(xb << 4);
+                whi[hh] = nib_n79(xb);
+              }
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                o_acc[nb][2 * k] = mfma16x16x32(bitcast<half8v>(wlo), pp[nb], o_acc[nb][2 * k]);
+                o_acc[nb][2 * k + 1] = mfma16x16x32(bitcast<half8v>(whi), pp[nb], o_acc[nb][2 * k + 1]);
+              }
+            }
+          };
+          // lanes of duplicated rows (at most 8 query rows): the low halves
+          // of P~_g in hi/lo chunks, 0 in the others
+          const bool dup_lane = dup_rows && r >= 8;
           half8v pop[NB];
+          half2v ahw[NB][4];   // high halves P~_g
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             uint4v pw;
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
-              pw[h] = bitcast<uint32_t>(cvt_pk_f16(pr[nb][2 * h] * (float)sv[2 * h],
-                                                   pr[nb][2 * h + 1] * (float)sv[2 * h + 1]));
+            for (int h = 0; h < 4; ++h) {
+              ahw[nb][h] = cvt_pk_f16(pr[nb][2 * h] * (float)sv[2 * h], pr[nb][2 * h + 1] * (float)sv[2 * h + 1]);
+              pw[h] = dup_lane ? 0u : bitcast<uint32_t>(ahw[nb][h]);
+            }
+            if (NB == 1 && hilo && dup_rows) {   // duplicated rows' lanes: the low halves
+              asm volatile("");
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                pin_v(ahw[nb][h]);
+                const half2v lo = {pv_lo(pr[nb][2 * h], (float)sv[2 * h], ahw[nb][h][0]),
+                                   pv_lo(pr[nb][2 * h + 1], (float)sv[2 * h + 1], ahw[nb][h][1])};
+                pw[h] = dup_lane ? bitcast<uint32_t>(lo) : pw[h];
+              }
+            }
             float ps = sg[nb][gi];
 #pragma unroll
             for (int h = 0; h < 4; ++h)
@@ -993,21 +1151,27 @@ void decode_kernel(const DecodeArgs a) {
             sg[nb][gi] = ps;
             pop[nb] = bitcast<half8v>(pw);
           }
-#pragma unroll
-          for (int kq = 0; kq < NPB / 2 / NGA; ++kq) {
-            const int k = gi * (NPB / 2 / NGA) + kq;
-            uint4v wlo, whi;
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-              const uint32_t xb = pair_bytes(cr.vw[2 * hh], cr.vw[2 * hh + 1], k);
-              wlo[hh] = nib_n79(xb << 4);
-              whi[hh] = nib_n79(xb);
-            }
+          pv_group(pop);
+          if (NB > 1 && hilo) {   // no free columns: PV products of the low halves
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              o_acc[nb][2 * k] = mfma16x16x32(bitcast<half8v>(wlo), pop[nb], o_acc[nb][2 * k]);
-              o_acc[nb][2 * k + 1] = mfma16x16x32(bitcast<half8v>(whi), pop[nb], o_acc[nb][2 * k + 1]);
+              uint4v pw;
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                pin_v(ahw[nb][h]);
+                pw[h] = bitcast<uint32_t>(half2v{pv_lo(pr[nb][2 * h], (float)sv[2 * h], ahw[nb][h][0]),
+                                                 pv_lo(pr[nb][2 * h + 1], (float)sv[2 * h + 1], ahw[nb][h][1])});
+              }
+              float ps = sg[nb][gi];
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+                ps = __builtin_amdgcn_fdot2(bitcast<half2v>(pw[h]), bitcast<half2v>(bzv[h]), ps, false);
+              sg[nb][gi] = ps;
+              pop[nb] = bitcast<half8v>(pw);
             }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(cr.vw[e]));
+            pv_group(pop);
           }
         }
       }
@@ -1068,7 +1232,7 @@ void decode_kernel(const DecodeArgs a) {
     // ---- merge the eight waves through LDS, one 16-row block at a time
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (NB == 1 && packed_sm) {   // per-lane sums of the packed softmax: add the four lanes of a row
+      if constexpr (PK) {   // per-lane sums of the packed softmax: add the four lanes of a row
         l_run[0] += dpp_f<0x124>(l_run[0], l_run[0]);
         l_run[0] += dpp_f<0x128>(l_run[0], l_run[0]);
         s_run[0] += dpp_f<0x124>(s_run[0], s_run[0]);
@@ -1085,10 +1249,22 @@ void decode_kernel(const DecodeArgs a) {
           for (int p = gi * (NPB / NGA); p < (gi + 1) * (NPB / NGA); ++p) o_acc[nb][p] = sp - o_acc[nb][p];
         }
       } else {
+        if constexpr (PK) {   // low-half columns 4 + b (zero unless a chunk was hi/lo) into row b
+#pragma unroll
+          for (int p = 0; p < NPB; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o_acc[0][p][i] += dpp_f<0x104>(0.0f, o_acc[0][p][i]);
+        }
         float sp = xor_sum(s_run[nb], 16);
         sp = xor_sum(sp, 32);
 #pragma unroll
         for (int p = 0; p < NPB; ++p) o_acc[nb][p] -= vbias(p) * sp;
+      }
+      if constexpr (dup_rows) {   // duplicated rows' columns r + 8 (the low halves) into row r
+#pragma unroll
+        for (int p = 0; p < NPB; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o_acc[0][p][i] += dpp_f<0x108>(0.0f, o_acc[0][p][i]);
       }
       if (j == 0) {
         s_m[wave][r] = m_run[nb];
@@ -1281,16 +1457,25 @@ void decode_kernel(const DecodeArgs a) {
   merge_splits();
 }
 
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0>
-hipError_t launch_kernel(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool PK = false>
+hipError_t launch_kernel1(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
   // this kernel the larger dynamic LDS once
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA>),
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PK>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
   if (attr != hipSuccess) return attr;
-  decode_kernel<D, NB, PAGED, BITS, NGA><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  decode_kernel<D, NB, PAGED, BITS, NGA, PK><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
   return hipGetLastError();
+}
+
+// symmetric rows with at most 4 query rows per group: the packed-softmax kernel
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0>
+hipError_t launch_kernel(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
+  if constexpr (NB == 1 && NGA == 0) {
+    if (args.G * args.Sq <= 4) return launch_kernel1<D, NB, PAGED, BITS, NGA, true>(args, grid, lds, stream);
+  }
+  return launch_kernel1<D, NB, PAGED, BITS, NGA, false>(args, grid, lds, stream);
 }
 
 template <int D, int NB>
@@ -1314,8 +1499,8 @@ hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, int bi
 template <int D>
 hipError_t launch_d(const DecodeArgs& args, int B, int Hkv, int n_split, int bits, hipStream_t stream) {
   const int R = args.G * args.Sq;
-  if (R <= 16) return launch_nb<D, 1>(args, B, Hkv, n_split, bits, stream);
-  if (R <= 32) return launch_nb<D, 2>(args, B, Hkv, n_split, bits, stream);
+  if (row_blocks_for(R) == 1) return launch_nb<D, 1>(args, B, Hkv, n_split, bits, stream);
+  if (row_blocks_for(R) == 2) return launch_nb<D, 2>(args, B, Hkv, n_split, bits, stream);
   return launch_nb<D, 4>(args, B, Hkv, n_split, bits, stream);
 }
 
@@ -1326,7 +1511,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
   const int64_t chunks = (kv_len + kChunk - 1) / kChunk;
   const int64_t units = B * Hkv;
   const int64_t rows_per_group = rows / units;
-  const int waves = waves_for(rows_per_group <= 16 ? 1 : rows_per_group <= 32 ? 2 : 4);
+  const int waves = waves_for(row_blocks_for(rows_per_group));
   int64_t ns;
   if (num_splits <= 0) {
     // eight waves per CU (one 8-wave or two 4-wave workgroups): measured best

@@ -26,12 +26,20 @@
 // VALU instructions per tile as it can:
 //  * the conversion of a tile is shared by all NW waves;
 //  * online softmax keeps a per-row reference m_ref and rescales only when a
-//    tile may exceed it by more than kTau (base-2 exponent).  On full tiles the
-//    test uses an upper bound, max|s| x max|csk| of the tile, so the common
-//    tile needs no per-score product before the exponent: p = exp2(s csk -
-//    m_ref) is one fma.  Probabilities stay below 2^kTau, far inside fp16
-//    range, and the final normalisation by l = sum(p) is unaffected;
-//  * P~ = fp16(p x s_V) is one v_fma_mix per value with s_V read as fp16.
+//    tile may exceed it by more than tau (base-2 exponent; kTau, lowered on
+//    tiles whose largest V scale s_max would take 2^kTau s_max near the fp16
+//    limit, so that P~ = p s_V stays finite).  On full tiles the test uses an
+//    upper bound, max|s| x max|csk| of the tile, so the common tile needs no
+//    per-score product before the exponent: p = exp2(s csk - m_ref) is one
+//    fma.  The final normalisation by l = sum(p) is unaffected;
+//  * P~ = fp16(p x s_V) is one v_fma_mix per value with s_V read as fp16.  A
+//    tile whose largest V scale passes pv_scale_limit (channel outliers)
+//    takes P~ as an fp16 hi/lo pair and runs each PV product twice, which
+//    keeps the output's rounding error below the attention tolerance.
+//
+// Query range: a workgroup whose queries hold an element of magnitude 65536
+// or more scales them by an exact power of two into fp16 range and its score
+// scale by the inverse.
 //
 // Pipeline: LDS is double buffered.  While a wave computes on tile kt it
 // converts tile kt+1 (loaded into registers one iteration earlier) into the
@@ -131,6 +139,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __align__(16) float s_csk[2][NG][BN];     // K scale x qk_log2 (per group)
   __shared__ __align__(16) _Float16 s_svh[2][NG][BN];  // V scale (per group), [j][tb][vq][i]
   __shared__ float s_cmax[2];                      // max |csk| of the tile
+  __shared__ uint32_t s_qmx[NW];                   // per wave: largest |q| (bf16 bits)
+  __shared__ uint32_t s_vmx[NW];                   // per wave: largest |V scale| (fp16 bits)
   __shared__ __align__(16) float s_ones[BN];
 
   const int h = blockIdx.x;   // query head of this call: KV head h / G of the cache
@@ -160,26 +170,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool wave_active = wrow_lo < Sq;
 
   // Query operand (B of S^T = K Q^T): row qrow, k = 8j + e <-> head dim
-  // 8 (2 s + j) + perm8(e), matching K chunk plane 2 s + j.
+  // 8 (2 s + j) + perm8(e), matching K chunk plane 2 s + j.  The workgroup's
+  // largest |q| decides the range shift (an exact power of two, 0 unless
+  // some element is 65536 or more), folded into the score scale qk.
+  uint4v qraw[KS];
   half8v qop[KS];
+  uint32_t qmb = 0;
   if (qrow < Sq) {
     const uint16_t* qr = q + (((int64_t)b * Hq + hq) * Sq + qrow) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const uint4v w = *reinterpret_cast<const uint4v*>(qr + 8 * (2 * s + j));
-      uint16_t e16[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        e16[2 * t] = (uint16_t)(w[t] & 0xFFFFu);
-        e16[2 * t + 1] = (uint16_t)(w[t] >> 16);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qop[s][e] = (_Float16)bf16_to_f32(e16[perm8(e)]);
+      qraw[s] = *reinterpret_cast<const uint4v*>(qr + 8 * (2 * s + j));
+      qmb = max(qmb, bf16x8_max_abs_bits(qraw[s]));
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qop[s] = half8v{};
+    for (int s = 0; s < KS; ++s) qraw[s] = uint4v{0u, 0u, 0u, 0u};
   }
+  qmb = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(qmb)));
+  if (lane == 0) s_qmx[wave] = qmb;
+  // the shift is known after the first barrier below; tile 0's scale table is
+  // written with the unshifted score scale and corrected there if needed
+  float qk = qk_log2;   // score scale in log2 units (x 2^qshift)
 
   float16v o_acc[NDB];
 #pragma unroll
@@ -195,6 +207,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // asymmetric rows: parameter words (NG per token)
   const rsrc_t rkp = make_rsrc(ASYM ? kp + kvrow0 * NG : nullptr, ASYM ? kv_len * NG * 4 : 0);
   const rsrc_t rvp = make_rsrc(ASYM ? vp + kvrow0 * NG : nullptr, ASYM ? kv_len * NG * 4 : 0);
+
+  // Largest |V scale| (fp16 bits) over the keys the workgroup attends.  The
+  // values are 16 bits wide (the scales; asymmetric rows: the low halves of
+  // the parameter words), read in aligned 16-byte blocks that never leave
+  // the blocks holding them, with every element outside them masked.
+  uint32_t vmb = 0;
+  {
+    const int nkeys = min(kv_len, n_tiles * BN);
+    const uint16_t* vb = ASYM ? reinterpret_cast<const uint16_t*>(vp + kvrow0 * NG) : vs + kvrow0;
+    const int n = ASYM ? 2 * nkeys * NG : nkeys;
+    const int lead = (int)((reinterpret_cast<uintptr_t>(vb) >> 1) & 7);
+    const rsrc_t rs = make_rsrc(vb - lead, ((lead + n + 7) & ~7) * 2);
+#pragma unroll 4
+    for (int i0 = 8 * (int)threadIdx.x; i0 < lead + n; i0 += 8 * 64 * NW) {
+      const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(i0 * 2), 0, 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = i0 + e - lead;
+        const bool ok = i >= 0 && i < n && (!ASYM || (e & 1) == 0);
+        vmb = ok ? max(vmb, (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu) : vmb;
+      }
+    }
+    vmb = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(vmb)));
+    if (lane == 0) s_vmx[wave] = vmb;
+  }
 
   // Loader roles.  K: lane = token, wave = which ROWB / NW bytes of the row
   // (chunk planes KDW wave ..).  V: VT consecutive tokens x one dword (8 head
@@ -368,7 +405,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     if constexpr (ASYM) {
       if (sp_k) {
-        const float f = f16bits_to_f32((uint16_t)(spw & 0xFFFFu)) * qk_log2;
+        const float f = f16bits_to_f32((uint16_t)(spw & 0xFFFFu)) * qk;
         s_csk[buf][sp_g][lane] = f;
         if constexpr (!PRESCALED) {
           const float m = wave_max_nonneg(fabsf(f));
@@ -378,7 +415,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         s_svh[buf][sp_g][sv_slot] = bitcast<_Float16>((uint16_t)(spw & 0xFFFFu));
       }
     } else if (wave == 0) {
-      const float f = f16bits_to_f32(sc) * qk_log2;
+      const float f = f16bits_to_f32(sc) * qk;
       s_csk[buf][0][lane] = f;
       const float m = wave_max_nonneg(fabsf(f));
       if (lane == 0) s_cmax[buf] = m;
@@ -402,11 +439,46 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   store_tile(0);
   load_tile(BN);
   __syncthreads();
+  float tau_hl;
+  {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      qmb = max(qmb, s_qmx[w]);
+      vmb = max(vmb, s_vmx[w]);
+    }
+    vmb = __builtin_amdgcn_readfirstlane(vmb);   // uniform (LDS values)
+    // rescale threshold of the hi/lo form: p <= 2^tau with 2^tau s_max <=
+    // 2^15 keeps P~ finite in fp16 (below the precision limit s_max is far
+    // too small for that to bind: tau = kTau)
+    tau_hl = fminf(kTau, fmaxf(0.0f, 15.0f - __log2f(f16bits_to_f32((uint16_t)vmb))));
+    const int qshift = q_range_shift(qmb);   // uniform
+    if (qshift != 0) {   // rare: K scale columns of tile 0 again, scaled by 2^qshift
+      qk = qk_log2 * exp2i(qshift);
+      const float f = exp2i(qshift);
+      if (wave < NG) s_csk[0][wave][lane] *= f;   // wave g wrote group g's column (exact: a power of two)
+      if (wave == 0 && lane == 0 && !PRESCALED) s_cmax[0] *= f;
+      __syncthreads();
+    }
+    const float qmul = exp2i(-qshift);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint16_t e16[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        e16[2 * t] = (uint16_t)(qraw[s][t] & 0xFFFFu);
+        e16[2 * t + 1] = (uint16_t)(qraw[s][t] >> 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[s][e] = (_Float16)(bf16_to_f32(e16[perm8(e)]) * qmul);
+    }
+  }
 
   // One key tile.  ALL_FULL: the tile is visible to every row of the
-  // workgroup, so no wave skips it and no mask is evaluated.
-  auto step = [&](int kt, auto all_full) {
+  // workgroup, so no wave skips it and no mask is evaluated.  HILO: P~ as an
+  // fp16 hi/lo pair.
+  auto step = [&](int kt, auto all_full, auto hilo_c) {
     constexpr bool ALL_FULL = decltype(all_full)::value;
+    constexpr bool HILO = decltype(hilo_c)::value;
     const int t0 = kt * BN;
     const int buf = kt & 1;
     const _Float16* sk_ = s_k + buf * KBUF;
@@ -471,6 +543,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (need) {
       // ---- online softmax; lane's tokens: 32 tb + 8 (v/4) + 4 j + v%4
       const bool full = ALL_FULL || ((t0 + BN <= kv_len) && (!CAUSAL || t0 + BN - 1 <= wrow_lo + off));
+      const float tau = HILO ? tau_hl : kTau;
       auto csk4 = [&](int tb, int vq) {
         return *reinterpret_cast<const float4v*>(cbase + 32 * tb + 8 * vq + 4 * j);
       };
@@ -508,7 +581,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if constexpr (!PRESCALED) mx *= s_cmax[buf];
         ctab = cbase;
       }
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kTau)) {
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + tau)) {
         // some row of the wave may rise above its reference: move the
         // reference of those rows to their new maximum, rescale their state
         if (full) {
@@ -524,7 +597,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           }
         }
         mx = xor_max(mx, 32);
-        const bool up = mx > m_ref + kTau;
+        const bool up = mx > m_ref + tau;
         const float alpha = up ? fast_exp2(m_ref - mx) : 1.0f;
         m_ref = up ? mx : m_ref;
         m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -553,50 +626,96 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int kp = 0; kp < 2; ++kp) {
               const half8v sv = svh[2 * tb + kp];
-              half8v pg;
+              half8v pg, pl;
+              if constexpr (HILO) {   // low halves about the pinned high halves
 #pragma unroll
-              for (int e = 0; e < 8; ++e) pg[e] = (_Float16)fmaf(pr[kp][e], (float)sv[e], 0.0f);
+                for (int e = 0; e < 8; e += 2) {
+                  const half2v h = pv_hi2(pr[kp][e], (float)sv[e], pr[kp][e + 1], (float)sv[e + 1]);
+                  pg[e] = h[0];
+                  pg[e + 1] = h[1];
+                }
+                pin_v(pg);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pl[e] = pv_lo(pr[kp][e], (float)sv[e], pg[e]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pg[e] = (_Float16)fmaf(pr[kp][e], (float)sv[e], 0.0f);
+              }
 #pragma unroll
               for (int db = gi * (NDB / NG); db < (gi + 1) * (NDB / NG); ++db) {
                 const half8v a =
                     *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
                 o_acc[db] = mfma32x32x16(a, pg, o_acc[db]);
+                if constexpr (HILO) o_acc[db] = mfma32x32x16(a, pl, o_acc[db]);
               }
             }
           }
         }
       } else {
-        half8v pop[2][2];
         const half8v* svh = reinterpret_cast<const half8v*>(&s_svh[buf][0][32 * j]);
-  #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-  #pragma unroll
-          for (int kp = 0; kp < 2; ++kp) {
-            const half8v sv = svh[2 * tb + kp];  // tokens 32 tb + 8 (2 kp + e/4) + 4 j + e%4
-  #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              // v = 4 vq + i = 8 kp + e  ->  vq = 2 kp + e/4, i = e%4
-              const int vq = 2 * kp + (e >> 2);
-              const int i = e & 3;
-              const float c = ctab[32 * tb + 8 * vq + 4 * j + i];
-              const float p = fast_exp2(fmaf(st[tb][8 * kp + e], c, -m_use));
-              l_run += p;
-              // P~ = fp16(p x s_V): one rounding of the exact product
-              pop[tb][kp][e] = (_Float16)fmaf(p, (float)sv[e], 0.0f);
+        // p of value e of block (tb, kp): v = 4 vq + i = 8 kp + e  ->  vq = 2 kp + e/4, i = e%4
+        auto prob = [&](int tb, int kp, int e) {
+          const float c = ctab[32 * tb + 8 * (2 * kp + (e >> 2)) + 4 * j + (e & 3)];
+          return fast_exp2(fmaf(st[tb][8 * kp + e], c, -m_use));
+        };
+        // ---- O^T += V^T P^T; k = 8 j + e <-> token 32 tb + 16 kp + 8 (e/4) + 4 j + e%4
+        if constexpr (HILO) {
+          // each high half formed once (pinned) and its low half about
+          // exactly that value, then the PV products of both
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+              // keeps this step's LDS reads here: hoisted, the 16 V operands
+              // of the tile would be live at once
+              asm volatile("" ::: "memory");
+              const half8v sv = svh[2 * tb + kp];
+              half8v ph, pl;
+#pragma unroll
+              for (int e = 0; e < 8; e += 2) {
+                const float p0 = prob(tb, kp, e), p1 = prob(tb, kp, e + 1);
+                l_run += p0 + p1;
+                const half2v h = pv_hi2(p0, (float)sv[e], p1, (float)sv[e + 1]);
+                ph[e] = h[0];
+                ph[e + 1] = h[1];
+                pl[e] = pv_lo(p0, (float)sv[e], h[0]);
+                pl[e + 1] = pv_lo(p1, (float)sv[e + 1], h[1]);
+              }
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const half8v a =
+                    *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
+                o_acc[db] = mfma32x32x16(a, ph, o_acc[db]);
+                o_acc[db] = mfma32x32x16(a, pl, o_acc[db]);
+              }
             }
           }
-        }
-
-        // ---- O^T += V^T P^T; k = 8 j + e <-> token 32 tb + 16 kp + 8 (e/4) + 4 j + e%4
-  #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-  #pragma unroll
-          for (int kp = 0; kp < 2; ++kp) {
-  #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const half8v a =
-                  *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
-              o_acc[db] = mfma32x32x16(a, pop[tb][kp], o_acc[db]);
+        } else {
+          half8v pop[2][2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+              const half8v sv = svh[2 * tb + kp];  // tokens 32 tb + 8 (2 kp + e/4) + 4 j + e%4
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float p = prob(tb, kp, e);
+                l_run += p;
+                // P~ = fp16(p x s_V): one rounding of the exact product
+                pop[tb][kp][e] = (_Float16)fmaf(p, (float)sv[e], 0.0f);
+              }
+            }
+          }
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const half8v a =
+                    *reinterpret_cast<const half8v*>(sv_ + v_rd[db] + (4 * tb + 2 * kp) * VPL);
+                o_acc[db] = mfma32x32x16(a, pop[tb][kp], o_acc[db]);
+              }
             }
           }
         }
@@ -607,9 +726,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   int n_full = kv_len / BN;
   if (CAUSAL) n_full = min(n_full, (q0 + off + 1) / BN);
   n_full = min(n_full, n_tiles);
+  // A workgroup whose keys hold a V scale past the precision limit (channel
+  // outliers) takes P~ as an fp16 hi/lo pair on every tile; the common loops
+  // never evaluate the hi/lo products.
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
   int kt = 0;
-  for (; kt < n_full; ++kt) step(kt, std::integral_constant<bool, true>{});
-  for (; kt < n_tiles; ++kt) step(kt, std::integral_constant<bool, false>{});
+  if (vmb <= pv_scale_limit_bits(pv_code_max(BITS, ASYM))) {
+    for (; kt < n_full; ++kt) step(kt, T_{}, F_{});
+    for (; kt < n_tiles; ++kt) step(kt, F_{}, F_{});
+  } else {
+    for (; kt < n_tiles; ++kt) step(kt, F_{}, T_{});
+  }
 
   // ---- epilogue: O = O^T / l; lane owns row qrow, head dims 32 db + 8 vq + 4 j + i
   const float l = xor_sum(l_run, 32);

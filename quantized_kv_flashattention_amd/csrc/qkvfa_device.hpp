@@ -282,6 +282,81 @@ __device__ __forceinline__ half2v uz_pair2(uint32_t a, uint32_t b, int nib, uint
   return bitcast<half2v>((x & 0x000F000Fu) | 0x64006400u) - bitcast<half2v>(bias);
 }
 
+// fp32 pair -> packed fp16, round to nearest even (v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ half2v cvt_pk_f16(float a, float b) {
+  half2v r;
+  r[0] = (_Float16)a;
+  r[1] = (_Float16)b;
+  return r;
+}
+
+// ---- Precision of the PV operand.  P~ = fp16(p s_V) is rounded once, with
+// relative error at most 2^-11.  An output is sum_j P~_j c_j / l with
+// l = sum_j p_j (unrounded), so its rounding error is at most
+// 2^-11 sum_j p_j s_V,j |c_j| / l <= 2^-11 cmax max_j s_V,j, where cmax is the
+// largest code magnitude of a row with a normal fp16 scale (7 for int4 rows,
+// 3 and 1 for 3- and 2-bit rows, 15 for |u - z| of asymmetric rows; a row with
+// a subnormal scale has values below 2^-11 and adds nothing that matters).
+// Where a tile (decode: a wave's 32-token chunk) holds a V scale above
+// pv_scale_limit(cmax), so that bound would pass kPvErrBudget, the kernels
+// take P~ as two fp16 terms instead, hi = fp16(p s_V) and lo = fp16(p s_V -
+// hi) (the residual is exact in fp32), and run the PV products for both:
+// error at most 2^-22 relative.  Rows of moderate magnitude (every N(0, 1)
+// workload) never take that branch.
+constexpr float kPvErrBudget = 3.5e-3f;
+__host__ __device__ constexpr float pv_scale_limit(int cmax) { return kPvErrBudget * 2048.0f / (float)cmax; }
+__host__ __device__ constexpr int pv_code_max(int bits, bool asym) {
+  return asym ? 15 : bits == 4 ? 7 : bits == 3 ? 3 : 1;
+}
+// The same limit as fp16 bits: a non-negative fp16 compares as its bit pattern.
+__host__ __device__ constexpr uint32_t pv_scale_limit_bits(int cmax) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)pv_scale_limit(cmax));
+}
+
+// The low half of P~ about the high half hi that the PV product uses:
+// fp16(p s - hi), the residual formed exactly by the fma.  hi must be the
+// register the product reads: the callers pin it (pin_v) first, because the
+// compiler may otherwise form hi again with another instruction (an fp16 fma
+// rounds the product once, an fp32 product converted to fp16 twice), and
+// where the product lies on an fp16 rounding midpoint the two differ by an ulp.
+__device__ __forceinline__ _Float16 pv_lo(float p, float s, _Float16 hi) { return (_Float16)fmaf(p, s, -(float)hi); }
+template <typename T>
+__device__ __forceinline__ void pin_v(T& x) { asm volatile("" : "+v"(x)); }
+// The high half by one fixed sequence, for code that forms it in two places:
+// the fp32 product (opaque to the compiler, so it is not fused into an fp16
+// fma), then one conversion to fp16 (round to nearest even).
+__device__ __forceinline__ _Float16 pv_hi(float p, float s) {
+  float x = p * s;
+  pin_v(x);
+  return (_Float16)x;
+}
+// Two high halves at once (one packed conversion).
+__device__ __forceinline__ half2v pv_hi2(float p0, float s0, float p1, float s1) {
+  float2v x = {p0 * s0, p1 * s1};
+  pin_v(x);
+  return cvt_pk_f16(x[0], x[1]);
+}
+
+// ---- Query range.  Q (bf16) enters the MFMAs as fp16, exact for magnitudes
+// in [2^-14, 65536) (bf16 keeps 8 significand bits, fp16 11).  Rows of a
+// workgroup with a larger element are multiplied by 2^-k first (exact), k the
+// smallest shift that brings the workgroup's largest |q| below 65536, and the
+// score scale by 2^k, so the scores do not change.  |bf16 bits| of the
+// largest element -> k (0 for every element below 65536).
+__device__ __forceinline__ int q_range_shift(uint32_t max_abs_bits) {
+  const int e = (int)(max_abs_bits >> 7);   // biased bf16 exponent
+  return e > 142 ? e - 142 : 0;
+}
+// 2^n as an fp32 (|n| < 127)
+__device__ __forceinline__ float exp2i(int n) { return __builtin_bit_cast(float, (uint32_t)(127 + n) << 23); }
+// Largest |bf16| bit pattern of the eight elements in a 16-byte word.
+__device__ __forceinline__ uint32_t bf16x8_max_abs_bits(const uint4v& w) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) m = max(m, max(w[t] & 0x7FFFu, (w[t] >> 16) & 0x7FFFu));
+  return m;
+}
+
 // Raw buffer descriptor over [base, base + num_bytes): loads at offsets past
 // num_bytes return zero instead of touching memory (gfx9-family raw buffer
 // range check; the fourth descriptor word selects 32-bit data format).
@@ -317,13 +392,6 @@ __device__ __forceinline__ float f16bits_to_f32(uint16_t b) {
   return (float)bitcast<_Float16>(b);
 }
 
-// fp32 pair -> packed fp16, round to nearest even (v_cvt_pk_f16_f32 on gfx950).
-__device__ __forceinline__ half2v cvt_pk_f16(float a, float b) {
-  half2v r;
-  r[0] = (_Float16)a;
-  r[1] = (_Float16)b;
-  return r;
-}
 
 __device__ __forceinline__ float4v mfma16x16x32(half8v a, half8v b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
