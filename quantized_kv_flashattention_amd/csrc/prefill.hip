@@ -176,6 +176,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   uint4v qraw[KS];
   half8v qop[KS];
   uint32_t qmb = 0;
+  uint32_t vmb = 0;   // largest |V scale| of the workgroup's keys (fp16 bits)
   if (qrow < Sq) {
     const uint16_t* qr = q + (((int64_t)b * Hq + hq) * Sq + qrow) * D;
 #pragma unroll
@@ -207,31 +208,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // asymmetric rows: parameter words (NG per token)
   const rsrc_t rkp = make_rsrc(ASYM ? kp + kvrow0 * NG : nullptr, ASYM ? kv_len * NG * 4 : 0);
   const rsrc_t rvp = make_rsrc(ASYM ? vp + kvrow0 * NG : nullptr, ASYM ? kv_len * NG * 4 : 0);
-
-  // Largest |V scale| (fp16 bits) over the keys the workgroup attends.  The
-  // values are 16 bits wide (the scales; asymmetric rows: the low halves of
-  // the parameter words), read in aligned 16-byte blocks that never leave
-  // the blocks holding them, with every element outside them masked.
-  uint32_t vmb = 0;
-  {
-    const int nkeys = min(kv_len, n_tiles * BN);
-    const uint16_t* vb = ASYM ? reinterpret_cast<const uint16_t*>(vp + kvrow0 * NG) : vs + kvrow0;
-    const int n = ASYM ? 2 * nkeys * NG : nkeys;
-    const int lead = (int)((reinterpret_cast<uintptr_t>(vb) >> 1) & 7);
-    const rsrc_t rs = make_rsrc(vb - lead, ((lead + n + 7) & ~7) * 2);
-#pragma unroll 4
-    for (int i0 = 8 * (int)threadIdx.x; i0 < lead + n; i0 += 8 * 64 * NW) {
-      const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(i0 * 2), 0, 0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = i0 + e - lead;
-        const bool ok = i >= 0 && i < n && (!ASYM || (e & 1) == 0);
-        vmb = ok ? max(vmb, (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu) : vmb;
-      }
-    }
-    vmb = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(vmb)));
-    if (lane == 0) s_vmx[wave] = vmb;
-  }
 
   // Loader roles.  K: lane = token, wave = which ROWB / NW bytes of the row
   // (chunk planes KDW wave ..).  V: VT consecutive tokens x one dword (8 head
@@ -436,6 +412,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   if (threadIdx.x < BN) s_ones[threadIdx.x] = 1.0f;
   load_tile(0);
+  // Largest |V scale| (fp16 bits) over the keys the workgroup attends; its
+  // loads overlap tile 0's.  The values are 16 bits wide (the scales;
+  // asymmetric rows: the low halves of the parameter words), read in aligned
+  // 16-byte blocks that never leave the blocks holding them, with every
+  // element outside them masked.
+  {
+    const int nkeys = min(kv_len, n_tiles * BN);
+    const uint16_t* vb = ASYM ? reinterpret_cast<const uint16_t*>(vp + kvrow0 * NG) : vs + kvrow0;
+    const int n = ASYM ? 2 * nkeys * NG : nkeys;
+    const int lead = (int)((reinterpret_cast<uintptr_t>(vb) >> 1) & 7);
+    const rsrc_t rs = make_rsrc(vb - lead, ((lead + n + 7) & ~7) * 2);
+#pragma unroll 4
+    for (int i0 = 8 * (int)threadIdx.x; i0 < lead + n; i0 += 8 * 64 * NW) {
+      const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(i0 * 2), 0, 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = i0 + e - lead;
+        const bool ok = i >= 0 && i < n && (!ASYM || (e & 1) == 0);
+        vmb = ok ? max(vmb, (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu) : vmb;
+      }
+    }
+    vmb = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(vmb)));
+    if (lane == 0) s_vmx[wave] = vmb;
+  }
   store_tile(0);
   load_tile(BN);
   __syncthreads();
