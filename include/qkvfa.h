@@ -155,6 +155,29 @@ qkv_status qkv_decode(const uint16_t* q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qkv_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as qkv_decode (the same
+ * kernels and split plan: outputs are bit-identical); it calls no hipMalloc,
+ * hipFree or allocating routine.  The tickets and split partials live in a
+ * static device array of the library, 16 MiB per device, held from module
+ * load until the process ends: 16 KiB of ticket counters (B * Hkv <= 4096)
+ * and up to 16 MiB - 16 KiB of partials (Sq * Hq * B * n_split * (D + 1) * 4
+ * bytes, rounded up).  Larger calls fail with QKV_ERR_WORKSPACE before any
+ * launch.  The first call on a device resolves that device's copy and zeroes
+ * its tickets with a small kernel on `stream`; every completed call leaves
+ * them zero.  All calls on one device share the array, so calls that overlap
+ * on one device (other streams, other threads) race: the caller serializes
+ * them.
+ */
+qkv_status qkv_decode_noalloc(const uint16_t* q,
+                              const uint8_t* k_codes, const uint16_t* k_scales,
+                              const uint8_t* v_codes, const uint16_t* v_scales,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t kv_len,
+                              int64_t C, int64_t D, float softmax_scale, int num_splits,
+                              float* out, float* lse, void* stream);
+
+/*
  * 2- and 3-bit rows (the bit-width parameter of "Quantized Cross-Attention"
  * §4.1; 2-bit heads in TurboAttention §3.2).  A b-bit row of D codes takes
  * D*b/8 bytes: scale = fp16(absmax / (2^(b-1) - 1)) by IEEE fp32 division,

@@ -28,6 +28,7 @@ __all__ = [
     "quantize_append",
     "quantize_append_kv",
     "decode",
+    "decode_noalloc",
     "decode_append",
     "decode_paged",
     "DecodeBuffer",
@@ -86,6 +87,9 @@ def _load():
     lib.qkv_decode.restype = ci
     lib.qkv_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
                                vp, vp, vp, sz, vp]
+    lib.qkv_decode_noalloc.restype = ci
+    lib.qkv_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32, ci,
+                                       vp, vp, vp]
     lib.qkv_decode_append.restype = ci
     lib.qkv_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                       f32, ci, vp, vp, vp, sz, vp]
@@ -315,6 +319,20 @@ def decode(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False,
         _check(_lib.qkv_decode_bits(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
                                     C, D, int(bits), _scale(softmax_scale, D), int(num_splits), _ptr(out),
                                     _ptr(lse), _ptr(workspace), ws_bytes, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def decode_noalloc(q, cache, kv_len, softmax_scale=None, num_splits=0, return_lse=False, out=None, lse=None):
+    """``decode`` (int4 cache) through ``qkv_decode_noalloc``: no workspace; the library's
+    static per-device scratch holds the split partials.  ``out``/``lse`` given, it
+    allocates nothing."""
+    tensors = cache.tensors() if isinstance(cache, KVCache) else tuple(cache)
+    B, Hq, Hkv, Sq, kv_len, C, D = _attn_args(q, tensors, kv_len, 4)
+    out, lse = _outputs(q, out, lse, return_lse)
+    kc, ks, vc, vs = tensors
+    _check(_lib.qkv_decode_noalloc(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), B, Hq, Hkv, Sq, kv_len,
+                                   C, D, _scale(softmax_scale, D), int(num_splits), _ptr(out), _ptr(lse),
+                                   _stream(q)))
     return (out, lse) if return_lse else out
 
 

@@ -161,7 +161,7 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
                          const qkvfa::DecodeAppend* append, const qkvfa::DecodeVarlen* varlen,
                          void* stream, const char* fn, int bits = 4,
                          const qkvfa::DecodeAsym* asym = nullptr, const int32_t* kv_heads = nullptr,
-                         int64_t Hkv_sub = 0) {
+                         int64_t Hkv_sub = 0, bool static_scratch = false) {
   const std::string f(fn);
   qkv_status st = check_attention(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len,
                                   C, D, out, lse, fn);
@@ -179,8 +179,25 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
   // whose thread count must fit 32 bits
   if ((int64_t)plan.n_split * B * Hc > ((int64_t)1 << 32) / 512)
     return fail(QKV_ERR_UNSUPPORTED, f + ": too many workgroups (num_splits * B * Hkv)");
-  const size_t need = qkvfa::decode_workspace_bytes(rows, B * Hc, (int)D, plan.n_split);
-  if (need > 0) {
+  int64_t ticket_slots = 0;
+  if (static_scratch) {
+    // the library's static scratch stands in for the workspace: a fixed
+    // ticket region, then this call's partials
+    if (plan.n_split > 1) {
+      if (B * Hc > qkvfa::kScratchTickets)
+        return fail(QKV_ERR_WORKSPACE, f + ": B * Hkv exceeds the static scratch's " +
+                                           std::to_string(qkvfa::kScratchTickets) + " tickets; use qkv_decode");
+      const size_t part = qkvfa::decode_workspace_bytes(rows, 1, (int)D, plan.n_split) - 256;
+      if (qkvfa::kScratchTicketBytes + part > qkvfa::kScratchBytes)
+        return fail(QKV_ERR_WORKSPACE, f + ": split partials need " + std::to_string(part) +
+                                           " bytes, more than the static scratch holds (" +
+                                           std::to_string(qkvfa::kScratchBytes - qkvfa::kScratchTicketBytes) +
+                                           "); use fewer splits or qkv_decode");
+      const hipError_t e = qkvfa::decode_scratch(&workspace, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_status(e, fn);
+      ticket_slots = qkvfa::kScratchTickets;
+    }
+  } else if (const size_t need = qkvfa::decode_workspace_bytes(rows, B * Hc, (int)D, plan.n_split); need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(QKV_ERR_WORKSPACE, f + ": workspace smaller than qkv_decode_workspace_bytes()");
     if (!aligned(workspace, 16))
@@ -189,7 +206,8 @@ qkv_status decode_common(const uint16_t* q, const uint8_t* k_codes, const uint16
   return hip_status(qkvfa::launch_decode(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hc, Sq,
                                          kv_len, varlen ? varlen->page_size : C, (int)D,
                                          softmax_scale, plan, out, lse, workspace, append, varlen,
-                                         nullptr, bits, static_cast<hipStream_t>(stream), asym, kv_heads, Hkv),
+                                         nullptr, bits, static_cast<hipStream_t>(stream), asym, kv_heads, Hkv,
+                                         ticket_slots),
                     fn);
 }
 
@@ -205,6 +223,15 @@ qkv_status qkv_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t*
   return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D,
                        softmax_scale, num_splits, out, lse, workspace, workspace_bytes, nullptr,
                        nullptr, stream, "qkv_decode");
+}
+
+qkv_status qkv_decode_noalloc(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                              const uint8_t* v_codes, const uint16_t* v_scales, int64_t B, int64_t Hq,
+                              int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int64_t D,
+                              float softmax_scale, int num_splits, float* out, float* lse, void* stream) {
+  return decode_common(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, Sq, kv_len, C, D,
+                       softmax_scale, num_splits, out, lse, nullptr, 0, nullptr, nullptr, stream,
+                       "qkv_decode_noalloc", 4, nullptr, nullptr, 0, true);
 }
 
 qkv_status qkv_decode_bits(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,

@@ -47,6 +47,9 @@
 // to a separate append followed by decode.
 #include <math.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "qkvfa_device.hpp"
 #include "qkvfa_internal.h"
 
@@ -1568,7 +1571,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          float softmax_scale, const DecodePlan& plan, float* out, float* lse,
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
                          const DecodeTail* tail, int bits, hipStream_t stream, const DecodeAsym* asym,
-                         const int32_t* kv_heads, int64_t Hkv_all) {
+                         const int32_t* kv_heads, int64_t Hkv_all, int64_t ticket_slots) {
   DecodeArgs a;
   a.kv_heads = kv_heads;
   a.Hkv_all = (int)(kv_heads ? Hkv_all : Hkv);
@@ -1618,7 +1621,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
   if (plan.n_split > 1) {
     const int64_t rows = B * Hkv * (Hq / a.Hkv_all) * Sq;   // this call's query rows
     char* w = static_cast<char*>(workspace);
-    const size_t t = align256((size_t)B * Hkv * sizeof(uint32_t));
+    const size_t t = align256((size_t)std::max<int64_t>(B * Hkv, ticket_slots) * sizeof(uint32_t));
     const size_t o = align256((size_t)rows * plan.n_split * D * sizeof(float));
     a.tickets = reinterpret_cast<uint32_t*>(w);
     a.part_o = reinterpret_cast<float*>(w + t);
@@ -1631,6 +1634,47 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
   a.qk_log2 = softmax_scale * kLog2e;
   if (D == 128) return launch_d<128>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);
   return launch_d<64>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);
+}
+
+// ---- allocation-free decode: one static scratch per device ----------------
+// A file-scope device array: each device holds its own copy at its own
+// address from module load until the process ends.  In host code its name
+// stands for a host-side shadow, never a device address, so host code uses
+// only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+__global__ void zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t decode_scratch(void** ptr, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the tickets must start at zero; a kernel rather than a memset, so a
+    // first call under stream capture records no memset node
+    hipLaunchKernelGGL(zero_words, dim3(16), dim3(256), 0, stream, static_cast<uint32_t*>(p), (int)kScratchTickets);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 }  // namespace qkvfa

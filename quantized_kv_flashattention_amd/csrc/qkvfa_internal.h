@@ -83,7 +83,17 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          void* workspace, const DecodeAppend* append, const DecodeVarlen* varlen,
                          const DecodeTail* tail, int bits, hipStream_t stream,
                          const DecodeAsym* asym = nullptr, const int32_t* kv_heads = nullptr,
-                         int64_t Hkv_all = 0);
+                         int64_t Hkv_all = 0, int64_t ticket_slots = 0);
+
+// Static scratch of the allocation-free decode: kScratchTickets ticket
+// counters at offset 0 (zero between calls), split partials from
+// kScratchTicketBytes on; kScratchBytes in all.  decode_scratch returns the
+// current device's copy, resolving its address (and zeroing its tickets with
+// a fill kernel on `stream`) on the first call on that device.
+constexpr int64_t kScratchTickets = 4096;
+constexpr size_t kScratchTicketBytes = (size_t)kScratchTickets * 4;
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr, hipStream_t stream);
 
 // Quantize-append of asymmetric group-wise 4-bit K and V rows (codes and
 // parameter words as in DecodeAsym) into cache rows [pos, pos + T).

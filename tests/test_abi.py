@@ -395,3 +395,23 @@ def test_prefill_heads_argument_errors(lib):
     assert ph(Sq=101) == 1        # causal needs Sq <= kv_len
     assert ph(L=129) == 1
     assert b"qkv_prefill_heads" in lib.qkv_last_error()
+
+
+def test_decode_noalloc_argument_errors(lib):
+    lib.qkv_decode_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 7 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+
+    def nd(**kw):
+        a = dict(B=1, Hq=4, Hkv=2, Sq=1, L=100, C=128, D=128, ns=0, q=P, out=P)
+        a.update(kw)
+        return lib.qkv_decode_noalloc(a["q"], P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["L"], a["C"],
+                                      a["D"], 0.1, a["ns"], a["out"], None, None)
+    assert nd(D=80) == 2
+    assert nd(q=None) == 1
+    assert nd(ns=-1) == 1
+    # more (batch, KV head) tickets than the static scratch holds
+    assert nd(B=4097, Hq=1, Hkv=1, ns=2) == 3
+    assert b"static scratch" in lib.qkv_last_error()
+    # 1024 rows x 64 splits x (128 + 1) x 4 bytes of partials: past 16 MiB
+    assert nd(B=16, Hq=64, Hkv=1, L=131072, C=131072, ns=64) == 3
+    assert b"static scratch" in lib.qkv_last_error()
