@@ -15,11 +15,12 @@ Printed (stdout, one JSON line): the headline decode throughput in GB/s of
 packed KV bytes (codes + scales) per step, the roofline of the decode kernel
 (achieved HBM GB/s of its algorithmic bytes over its average launch duration
 in the timed region -- one launch per step -- measured with HIP events on the
-launch stream), the CPU oracle timed on a
-bounded sample of the same workload, and secondary figures (128K-token
-decode, a ragged 64-sequence batch over a paged cache, the decode step with
-the INT8 buffer, decode over 2- and 3-bit caches, 16K causal prefill
-TFLOP/s, ViT-B prefill, bulk quantize-append).
+launch stream), the CPU oracle timed on a bounded sample of the same
+workload (and of the ViT-B and 16K causal prefill workloads), and secondary
+figures (128K-token decode, a ragged 64-sequence batch over a paged cache,
+the decode step with the INT8 buffer, decode over 2- and 3-bit and
+asymmetric caches, 16K causal prefill TFLOP/s, ViT-B prefill GB/s and
+TFLOP/s, the achievable-HBM streaming read, bulk quantize-append).
 Everything else goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline]
@@ -33,6 +34,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -165,6 +168,13 @@ def prefill_flops(w):
     pairs = w.Sq * (w.Sq + 1) // 2 if (w.causal and w.Sq == w.L) else (
         sum(min(w.L, i + w.L - w.Sq + 1) for i in range(w.Sq)) if w.causal else w.Sq * w.L)
     return 4.0 * w.D * pairs * w.B * w.Hq
+
+
+def prefill_bytes(w, bits=4, group=0):
+    """Algorithmic HBM bytes of a prefill: Q (bf16) and O (fp32) once, every
+    KV head's cache rows [0, L) once (codes + scales or parameter words)."""
+    row = w.D * bits // 8 + (4 * (w.D // group) if group else 2)
+    return w.B * w.Hq * w.Sq * w.D * (2 + 4) + 2 * w.B * w.Hkv * w.L * row
 
 
 def bench_decode(torch, qkv, w, steps, warmup, with_append):
@@ -456,10 +466,15 @@ def bench_prefill(torch, qkv, w, iters, bits=4, group=0):
         run(i)
     avg_ms, med_ms = per_launch_ms(torch, run, iters, 1)
     fl = prefill_flops(w)
+    nbytes = prefill_bytes(w, bits, group)
     res = {"workload": w.name, "bits": bits, "group": group or None, "avg_ms": avg_ms, "median_ms": med_ms,
            "flops": fl,
-           "TFLOPs": fl / (avg_ms * 1e-3) / 1e12}
+           "TFLOPs": fl / (avg_ms * 1e-3) / 1e12, "algorithmic_bytes": nbytes,
+           "GBps": nbytes / (avg_ms * 1e-3) / 1e9}
     res["frac_mfma"] = res["TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+    res["frac_hbm"] = res["GBps"] / HBM_PEAK_GBS
+    # the roof that binds: the larger of the two fractions' time floors
+    res["bound"] = "hbm" if nbytes / HBM_PEAK_GBS / 1e9 > fl / MFMA_F16_PEAK_TFLOPS / 1e12 else "mfma"
     del cache, q, out
     torch.cuda.empty_cache()
     return res
@@ -467,14 +482,30 @@ def bench_prefill(torch, qkv, w, iters, bits=4, group=0):
 
 def bench_hbm_context(torch, iters=10):
     """Achievable-HBM context (not the headline's peak, which stays nominal):
-    a read-only reduction over 1 GiB and a 512 MiB device-to-device copy,
-    torch's own kernels, back to back with events around the batch."""
+    the library's plain streaming-read kernel over 1 GiB (qkvb_stream_read,
+    16-byte loads, four in flight per thread; best of a few grid sizes) and
+    torch's 512 MiB device-to-device copy, back to back with events around
+    the batch."""
+    import ctypes
+    blib = ctypes.CDLL(os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa_bench.so"))
+    blib.qkvb_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
     n = (1 << 30) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
     y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    red = torch.empty(65536, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def read(grid):
+        def fn():
+            if blib.qkvb_stream_read(x.data_ptr(), 1 << 30, red.data_ptr(), grid, stream) != 0:
+                raise RuntimeError("qkvb_stream_read failed")
+        return fn
+
     res = {}
-    for name, fn, nbytes in (("read_1GiB_sum", lambda: x.sum(), 1 << 30),
-                             ("copy_512MiB", lambda: y.copy_(x[: n // 2]), 2 * (1 << 29))):
+    legs = [(f"stream_read_1GiB_grid{g}", read(g), 1 << 30) for g in (1024, 2048, 4096, 8192)]
+    legs.append(("copy_512MiB", lambda: y.copy_(x[: n // 2]), 2 * (1 << 29)))
+    for name, fn, nbytes in legs:
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -486,7 +517,9 @@ def bench_hbm_context(torch, iters=10):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / iters
         res[name] = {"ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    del x, y
+    best = max((k for k in res if k.startswith("stream_read")), key=lambda k: res[k]["GBps"])
+    res["stream_read_best"] = dict(res[best], leg=best)
+    del x, y, red
     torch.cuda.empty_cache()
     return res
 
@@ -513,16 +546,85 @@ def bench_quantize(torch, qkv, w, iters):
             "GBps": nbytes / (avg_ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(w, budget_s):
-    """The CPU oracle on a bounded sample of the decode workload (whole KV groups)."""
-    import numpy as np
-    import oracle
-    from qkv_inputs import make_qkv
+def cpu_info():
+    """(cores in this process's affinity mask, BLAS pool threads or None, CPU model)."""
+    aff = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas = None
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return aff, blas, model
+
+
+def cpu_prefill_sample(w, budget_s, seed=0):
+    """The CPU oracle on a bounded sample of a prefill workload: whole (batch,
+    head) pairs of a short non-causal workload, or evenly spaced query rows of
+    one KV group's heads of a long causal one.  Rate in TFLOP/s of the sampled
+    attention (4 D flops per query-key pair) and, for the short workload, GB/s
+    of the packed KV bytes the sample's heads read.
+    """
+    import oracle
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w, seed)
+    G = w.G
+    row = w.D // 2 + 2
+    t_total, flops, nbytes, done = 0.0, 0.0, 0, 0
+    if not w.causal:
+        pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+        for b, g in pairs:
+            t0 = time.perf_counter()
+            kc, ksc = oracle.quantize_rows(k[b:b + 1, g:g + 1])
+            vc, vsc = oracle.quantize_rows(v[b:b + 1, g:g + 1])
+            oracle.attention(q_bits[b:b + 1, g * G:(g + 1) * G], kc, ksc, vc, vsc, w.L, w.softmax_scale)
+            t_total += time.perf_counter() - t0
+            done += 1
+            flops += 4.0 * w.D * w.Sq * w.L * G
+            nbytes += 2 * w.L * row
+            if t_total >= budget_s:
+                break
+        sample = f"{done} of {len(pairs)} (batch, KV head) groups of {w.name} ({G} heads x {w.Sq} rows each)"
+    else:
+        t0 = time.perf_counter()
+        kc, ksc = oracle.quantize_rows(k[:1, :1])
+        vc, vsc = oracle.quantize_rows(v[:1, :1])
+        t_total += time.perf_counter() - t0
+        nbytes = 2 * w.L * row
+        off = w.L - w.Sq
+        n_rows = 8
+        while True:
+            rows = sorted({int(r) for r in np.linspace(0, w.Sq - 1, n_rows)})
+            t0 = time.perf_counter()
+            oracle.attention(q_bits[:1, :G], kc, ksc, vc, vsc, w.L, w.softmax_scale, causal=True,
+                             heads=[(0, h) for h in range(G)], rows=rows)
+            t_total += time.perf_counter() - t0
+            done += len(rows)
+            flops += 4.0 * w.D * G * sum(r + off + 1 for r in rows)
+            if t_total >= budget_s or n_rows >= w.Sq:
+                break
+            n_rows *= 2
+        sample = (f"{done} query rows (evenly spaced, causal) x {G} heads of KV group (0, 0) of {w.name}, "
+                  f"quantizing that group's {w.L} K/V rows once")
+    return {"TFLOPs": flops / t_total / 1e12,
+            "GBps_packed_kv": None if w.causal else nbytes / t_total / 1e9,
+            "seconds": round(t_total, 2), "sample": sample}
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU oracle on a bounded sample of the decode workload (whole KV groups)."""
+    import oracle
+    from qkv_inputs import make_qkv
+    aff, blas, model = cpu_info()
+    threads = min(aff, blas) if blas else aff   # the BLAS pool runs within the affinity mask
     q_bits, k, v = make_qkv(w)
     groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     done, t_total, nbytes = 0, 0.0, 0
@@ -544,6 +646,7 @@ def cpu_baseline(w, budget_s):
         "sample": (f"{done} of {len(groups)} (batch, KV head) groups of {w.name} "
                    f"(quantize K/V rows + fp64 attention of {G} heads x {w.L} tokens each), "
                    f"{t_total:.1f} s; GB/s counts packed KV bytes as on the GPU"),
+        "affinity_cores": aff, "blas_threads": blas, "cpu_model": model,
     }
 
 
@@ -718,6 +821,9 @@ def main():
         log("quantize:", json.dumps(secondary["quantize_append"]))
 
     cpu = cpu_baseline(w3, args.cpu_budget)
+    if args.only == "all":
+        cpu["other_configs"] = {n: cpu_prefill_sample(workload(n), args.cpu_budget / 2)
+                                for n in ("vit_b_selfattn", "causal_prefill_16k")}
     log("cpu:", json.dumps(cpu))
 
     value = head["step_GBps_packed_kv"]

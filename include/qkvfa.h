@@ -41,7 +41,18 @@
  * QKV_ERR_HIP.  No C++ exception crosses this interface.
  * Preconditions that are not checked (their violation gives unspecified
  * output, never an out-of-bounds access): finite inputs; row absmax of
- * quantized data <= 7 * 65504; |q| < 65504 for every query element.
+ * quantized data <= 7 * 65504 (fp16 scales); scores q.k * softmax_scale
+ * finite in fp32.  Queries may hold any finite bfloat16: where a query
+ * group's largest |q| reaches 65536 the kernels scale it by an exact power of
+ * two into fp16 range and fold the inverse into the score scale.
+ * Precision: the softmax probabilities enter the PV product as fp16
+ * P~ = p * s_V (the V scale folded into P: "Quantized Cross-Attention", §3.4,
+ * softmax in quantized space, in its exact reading); where a V scale
+ * passes the limit at which one fp16 rounding of P~ could cost more than
+ * 3.5e-3 of an output (int4 1.02, 3-bit 2.39, 2-bit 7.17, asymmetric rows
+ * 0.48; channel outliers, TurboAttention §3.1), P~ is taken as an fp16
+ * high/low pair, so outputs stay within 4e-3 of fp64 attention over the
+ * dequantized cache.
  */
 #ifndef QKVFA_H
 #define QKVFA_H

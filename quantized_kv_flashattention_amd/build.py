@@ -17,6 +17,9 @@ LIB_NAME = "libqkvfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "prefill.hip"]
+# measurement helper (achievable-HBM streaming read), a library of its own
+BENCH_LIB_PATH = os.path.join(PKG_DIR, "libqkvfa_bench.so")
+BENCH_SOURCES = ["bench_read.hip"]
 
 # No fast-math: the quantizer needs IEEE fp32 division and round-half-even.
 # Packed fp32 VALU ops are disabled (-packed-fp32-ops) for every device file.
@@ -43,10 +46,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into ``libqkvfa.so`` next to this file; return its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _link(sources, path, verbose):
+    tmp = path + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -56,7 +58,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``libqkvfa.so`` (and the measurement helper ``libqkvfa_bench.so``)
+    next to this file; return the path of ``libqkvfa.so``."""
+    _link(SOURCES, LIB_PATH, verbose)
+    _link(BENCH_SOURCES, BENCH_LIB_PATH, verbose)
     return LIB_PATH
 
 

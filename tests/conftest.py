@@ -11,8 +11,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    lib = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")
-    if not os.path.exists(lib):
+    pkg = os.path.join(ROOT, "quantized_kv_flashattention_amd")
+    if not all(os.path.exists(os.path.join(pkg, n)) for n in ("libqkvfa.so", "libqkvfa_bench.so")):
         # nothing built yet: build once (hipcc cross-compiles without a GPU)
         import importlib.util
         spec = importlib.util.spec_from_file_location(

@@ -415,3 +415,23 @@ def test_decode_noalloc_argument_errors(lib):
     # 1024 rows x 64 splits x (128 + 1) x 4 bytes of partials: past 16 MiB
     assert nd(B=16, Hq=64, Hkv=1, L=131072, C=131072, ns=64) == 3
     assert b"static scratch" in lib.qkv_last_error()
+
+
+BENCH_HEADER = os.path.join(ROOT, "include", "qkvfa_bench.h")
+BENCH_LIB = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa_bench.so")
+
+
+def test_bench_helper_exports_and_argument_errors():
+    L = ctypes.CDLL(BENCH_LIB)
+    text = re.sub(r"/\*.*?\*/", "", open(BENCH_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qkvb_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["qkvb_stream_read"]
+    for n in names:
+        assert hasattr(L, n), n
+    f = L.qkvb_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 16, P, 1, None) == 1
+    assert f(P, 17, P, 1, None) == 1          # not a multiple of 16
+    assert f(P + 4, 16, P, 1, None) == 1      # misaligned
+    assert f(P, 16, P, 0, None) == 1
+    assert f(P, 16, None, 1, None) == 1
