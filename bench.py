@@ -677,6 +677,16 @@ def profile_target(target: str, iters: int):
                              softmax_scale=w.softmax_scale, out=out)
         torch.cuda.synchronize()
         return
+    if target == "vit":
+        w = workload("vit_b_selfattn")
+        q_bits, k, v = make_qkv(w)
+        cache = upload_cache(torch, qkv, k, v, 1)[0]
+        q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+        out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+        for _ in range(iters):
+            qkv.prefill(q, cache, w.L, False, softmax_scale=w.softmax_scale, out=out)
+        torch.cuda.synchronize()
+        return
     if target == "prefill":
         w = workload("causal_prefill_16k")
         q_bits, k, v = make_qkv(w)
@@ -762,7 +772,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "headline", "decode", "prefill"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--profile-target", choices=["decode", "long", "paged", "prefill", "copy"], default=None,
+    ap.add_argument("--profile-target", choices=["decode", "long", "paged", "prefill", "vit", "copy"], default=None,
                     help="run one kernel repeatedly for rocprofv3 counter passes, print nothing")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")

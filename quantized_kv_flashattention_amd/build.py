@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libqkvfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "prefill.hip", "prefill_short.hip"]
 # measurement helper (achievable-HBM streaming read), a library of its own
 BENCH_LIB_PATH = os.path.join(PKG_DIR, "libqkvfa_bench.so")
 BENCH_SOURCES = ["bench_read.hip"]

@@ -87,21 +87,6 @@ namespace {
 constexpr int BN = 64;        // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-// Maximum over the 64 lanes of a wave of a non-negative float (the integer
-// order of the bit patterns is the float order for non-negative values),
-// returned uniformly.  Prefix maxima inside each 16-lane row, then the row
-// broadcasts carry them across rows; lane 63 ends with the wave maximum.
-__device__ __forceinline__ float wave_max_nonneg(float x) {
-  int v = bitcast<int>(x);
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));  // row_shr:1
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));  // row_shr:2
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));  // row_shr:4
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));  // row_shr:8
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
-  return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
-}
-
 template <int D, int NW, bool CAUSAL, int BITS, int NGA>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
@@ -816,6 +801,9 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* kc, const uint16_t* 
                           int64_t Hkv, int64_t Sq, int64_t kv_len, int64_t C, int D,
                           float softmax_scale, int causal, float* out, float* lse,
                           hipStream_t stream, int bits, const int32_t* kv_heads, int64_t Hkv_all) {
+  if (prefill_short_fits(D, Sq, kv_len, bits))
+    return launch_prefill_short(q, kc, ks, vc, vs, B, Hq, Hkv, Sq, kv_len, C, softmax_scale, causal, out, lse,
+                                stream, kv_heads, Hkv_all);
   const PrefillArgs a = {q, kc, ks, vc, vs, nullptr, nullptr, kv_heads, kv_heads ? Hkv_all : Hkv, B, Hq, Hkv, Sq,
                          kv_len, C, softmax_scale * kLog2e, out, lse};
   return launch_any(a, D, causal, stream, bits, 0);

@@ -404,6 +404,21 @@ __device__ __forceinline__ float16v mfma32x32x16(half8v a, half8v b, float16v c)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Wave64 butterfly max / sum across lanes differing in bit `mask`.
+// Maximum over the 64 lanes of a wave of a non-negative float (the integer
+// order of the bit patterns is the float order for non-negative values),
+// returned uniformly.  Prefix maxima inside each 16-lane row, then the row
+// broadcasts carry them across rows; lane 63 ends with the wave maximum.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  int v = bitcast<int>(x);
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
+}
+
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
 

@@ -85,6 +85,14 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          const DecodeAsym* asym = nullptr, const int32_t* kv_heads = nullptr,
                          int64_t Hkv_all = 0, int64_t ticket_slots = 0);
 
+// Short-sequence prefill (kv_len <= 256, D = 64, int4 rows, Sq <= 256): one
+// workgroup per query head holds the head's whole converted key range in LDS.
+bool prefill_short_fits(int64_t D, int64_t Sq, int64_t kv_len, int bits);
+hipError_t launch_prefill_short(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
+                                const uint16_t* vs, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                                int64_t kv_len, int64_t C, float softmax_scale, int causal, float* out,
+                                float* lse, hipStream_t stream, const int32_t* kv_heads, int64_t Hkv_all);
+
 // Static scratch of the allocation-free decode: kScratchTickets ticket
 // counters at offset 0 (zero between calls), split partials from
 // kScratchTicketBytes on; kScratchBytes in all.  decode_scratch returns the
