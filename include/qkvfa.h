@@ -49,10 +49,10 @@
  * P~ = p * s_V (the V scale folded into P: "Quantized Cross-Attention", §3.4,
  * softmax in quantized space, in its exact reading); where a V scale
  * passes the limit at which one fp16 rounding of P~ could cost more than
- * 3.5e-3 of an output (int4 1.02, 3-bit 2.39, 2-bit 7.17, asymmetric rows
- * 0.48; channel outliers, TurboAttention §3.1), P~ is taken as an fp16
- * high/low pair, so outputs stay within 4e-3 of fp64 attention over the
- * dequantized cache.
+ * 3.5e-3 of an output (int4 1.02, 3-bit 2.39, 2-bit 7.17; asymmetric rows:
+ * s max(z, 15 - z) above 7.17; channel outliers, TurboAttention §3.1), P~ is
+ * taken as an fp16 high/low pair, so outputs stay within 4e-3 of fp64
+ * attention over the dequantized cache.
  */
 #ifndef QKVFA_H
 #define QKVFA_H

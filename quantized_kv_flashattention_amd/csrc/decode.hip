@@ -1013,10 +1013,9 @@ void decode_kernel(const DecodeArgs a) {
       if constexpr (ASYM) {
         // a V group scale of this chunk past the precision limit: P~_g also
         // gets its low fp16 half (see pv_lo)
-        constexpr uint32_t kLimBits = pv_scale_limit_bits(pv_code_max(4, true));
         bool big = false;
 #pragma unroll
-        for (int u = 0; u < NPW; ++u) big = big || (lane * NPW + u < 32 * NGA && (cr.vpw[u] & 0xFFFFu) > kLimBits);
+        for (int u = 0; u < NPW; ++u) big = big || (lane * NPW + u < 32 * NGA && asym_needs_hilo(cr.vpw[u]));
         const bool hilo = __builtin_amdgcn_ballot_w64(big) != 0;
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ float s_cmax[2];                      // max |csk| of the tile
   __shared__ uint32_t s_qmx[NW];                   // per wave: largest |q| (bf16 bits)
   __shared__ uint32_t s_vmx[NW];                   // per wave: largest |V scale| (fp16 bits)
+  __shared__ float s_vam[NW];                      // per wave: largest s max(z, 15 - z) (asymmetric rows)
   __shared__ __align__(16) float s_ones[BN];
 
   const int h = blockIdx.x;   // query head of this call: KV head h / G of the cache
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   half8v qop[KS];
   uint32_t qmb = 0;
   uint32_t vmb = 0;   // largest |V scale| of the workgroup's keys (fp16 bits)
+  float vam = 0.0f;   // asymmetric rows: largest s max(z, 15 - z) of those keys
   if (qrow < Sq) {
     const uint16_t* qr = q + (((int64_t)b * Hq + hq) * Sq + qrow) * D;
 #pragma unroll
@@ -416,10 +418,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int i = i0 + e - lead;
         const bool ok = i >= 0 && i < n && (!ASYM || (e & 1) == 0);
         vmb = ok ? max(vmb, (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu) : vmb;
+        if constexpr (ASYM)
+          if ((e & 1) == 0) vam = ok ? fmaxf(vam, asym_value_max(w[e >> 1])) : vam;
       }
     }
     vmb = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(vmb)));
     if (lane == 0) s_vmx[wave] = vmb;
+    if constexpr (ASYM) {
+      vam = wave_max_nonneg(vam);
+      if (lane == 0) s_vam[wave] = vam;
+    }
   }
   store_tile(0);
   load_tile(BN);
@@ -430,8 +438,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int w = 0; w < NW; ++w) {
       qmb = max(qmb, s_qmx[w]);
       vmb = max(vmb, s_vmx[w]);
+      if constexpr (ASYM) vam = fmaxf(vam, s_vam[w]);
     }
     vmb = __builtin_amdgcn_readfirstlane(vmb);   // uniform (LDS values)
+    vam = bitcast<float>(__builtin_amdgcn_readfirstlane(bitcast<int>(vam)));
     // rescale threshold of the hi/lo form: p <= 2^tau with 2^tau s_max <=
     // 2^15 keeps P~ finite in fp16 (below the precision limit s_max is far
     // too small for that to bind: tau = kTau)
@@ -717,7 +727,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   int kt = 0;
-  if (vmb <= pv_scale_limit_bits(pv_code_max(BITS, ASYM))) {
+  const bool wg_hilo = ASYM ? vam > kPvErrBudget * 2048.0f : vmb > pv_scale_limit_bits(pv_code_max(BITS, false));
+  if (!wg_hilo) {
     for (; kt < n_full; ++kt) step(kt, T_{}, F_{});
     for (; kt < n_tiles; ++kt) step(kt, F_{}, F_{});
   } else {

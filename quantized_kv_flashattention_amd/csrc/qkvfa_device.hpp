@@ -295,8 +295,10 @@ __device__ __forceinline__ half2v cvt_pk_f16(float a, float b) {
 // l = sum_j p_j (unrounded), so its rounding error is at most
 // 2^-11 sum_j p_j s_V,j |c_j| / l <= 2^-11 cmax max_j s_V,j, where cmax is the
 // largest code magnitude of a row with a normal fp16 scale (7 for int4 rows,
-// 3 and 1 for 3- and 2-bit rows, 15 for |u - z| of asymmetric rows; a row with
-// a subnormal scale has values below 2^-11 and adds nothing that matters).
+// 3 and 1 for 3- and 2-bit rows; a row with a subnormal scale has values
+// below 2^-11 and adds nothing that matters).  An asymmetric group's codes
+// satisfy |u - z| <= max(z, 15 - z), so its bound is 2^-11 s max(z, 15 - z)
+// (asym_needs_hilo).
 // Where a tile (decode: a wave's 32-token chunk) holds a V scale above
 // pv_scale_limit(cmax), so that bound would pass kPvErrBudget, the kernels
 // take P~ as two fp16 terms instead, hi = fp16(p s_V) and lo = fp16(p s_V -
@@ -312,6 +314,15 @@ __host__ __device__ constexpr int pv_code_max(int bits, bool asym) {
 __host__ __device__ constexpr uint32_t pv_scale_limit_bits(int cmax) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)pv_scale_limit(cmax));
 }
+// An asymmetric parameter word (fp16 scale s in bits 0-15, zero point z in
+// bits 16-19): s max(z, 15 - z), the group's largest |value| -- past
+// kPvErrBudget x 2^11 (7.168) one rounding of P~_g could cost more than the
+// budget.  (s between 0.478 at z = 0 or 15 and 0.896 at z = 7 or 8.)
+__device__ __forceinline__ float asym_value_max(uint32_t w) {
+  const uint32_t z = (w >> 16) & 15u;
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0x7FFFu)) * (float)(z > 7u ? z : 15u - z);
+}
+__device__ __forceinline__ bool asym_needs_hilo(uint32_t w) { return asym_value_max(w) > kPvErrBudget * 2048.0f; }
 
 // The low half of P~ about the high half hi that the PV product uses:
 // fp16(p s - hi), the residual formed exactly by the fma.  hi must be the
