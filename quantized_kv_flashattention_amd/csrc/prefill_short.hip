@@ -24,17 +24,16 @@
 // of step vq are exactly its B operand of the PV product for tokens 8 vq ..
 // 8 vq + 7 -- no data moves between lanes except the row max.
 //
-// LDS (dynamic, sized by kv_len):
-//   K: fp16 rows of 64 head dims (128 B) in unpack8_perm order, 16-byte chunk
-//      c of token t at chunk slot c ^ ((t >> 1) & 7): the 16 lanes of one
-//      read phase (16 consecutive tokens, one chunk) and of one conversion
-//      write phase (2 tokens x 8 chunks) cover all 64 banks.  Key blocks read
-//      rows up to the next multiple of 32; rows past kv_len land in the V
-//      region (finite values), and their scores are replaced by -inf.
-//   V: fp16 transposed, [64 dims][Sv tokens], Sv = kv_len rounded up to 8
-//      (plus 8 where that is a multiple of 16, so that the dim stride is an
-//      odd multiple of 4 dwords: a PV read of 16 consecutive dims hits 16
-//      distinct 2-dword bank pairs); tokens past kv_len hold zeros.
+// LDS (72 KB, fixed strides, so that each read of a key block is one base
+// address plus immediate offsets):
+//   K: fp16 rows of 64 head dims in unpack8_perm order, 144 bytes apart (an
+//      odd multiple of 16: the 16 lanes of a read phase, 16 consecutive
+//      tokens of one 16-byte chunk, cover all 64 banks).  Key blocks read
+//      rows up to the next multiple of 32; rows past kv_len hold whatever
+//      the LDS held, and their scores are replaced by -inf.
+//   V: fp16 transposed, [64 dims][264 tokens] (an odd multiple of 8 tokens:
+//      a PV read of 16 consecutive dims hits 16 distinct 2-dword bank
+//      pairs); tokens from kv_len to the next multiple of 8 hold zeros.
 //   tables: fp32 K scale x softmax_scale x log2(e) per token, fp16 V scale
 //      per token (zeros past kv_len).
 #include <math.h>
@@ -64,25 +63,14 @@ constexpr int kSMaxWaves = 8;
 constexpr int kShortRowGroups = 0;
 constexpr int kShortRowGroupWaves = 4;
 
-struct ShortLayout {
-  int lk8, lk32, sv;
-  int v_off, csk_off, svh_off, bytes;   // byte offsets into the dynamic LDS
-};
-
-__host__ __device__ inline ShortLayout short_layout(int L) {
-  ShortLayout s;
-  s.lk8 = (L + 7) & ~7;
-  s.lk32 = (L + 31) & ~31;
-  s.sv = (L + 7) & ~7;
-  if (s.sv % 16 == 0) s.sv += 8;
-  s.v_off = s.lk8 * kSD * 2;
-  s.csk_off = s.v_off + kSD * s.sv * 2;
-  s.svh_off = s.csk_off + s.lk32 * 4;
-  const int end = s.svh_off + s.sv * 2;
-  const int kreach = s.lk32 * kSD * 2;   // K reads of the last key block end here
-  s.bytes = ((end > kreach ? end : kreach) + 15) & ~15;
-  return s;
-}
+// LDS strides (halves), fixed so that every read of a key block is one base
+// address plus immediate offsets: K rows of 72 halves (144 bytes, an odd
+// multiple of 16: the 16 lanes of a read phase -- 16 consecutive tokens, one
+// 16-byte chunk -- cover all 64 banks), V^T rows of 264 tokens (an odd
+// multiple of 8: the 16 dims of a read phase hit 16 distinct bank pairs).
+constexpr int kSKStride = 72;
+constexpr int kSVStride = 264;
+constexpr int kSMaxKeys = 256;
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu(4))) void prefill_short_kernel(
@@ -91,15 +79,14 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
     int Hkv_all, int Hq, int Hkv, int G, int Sq, int kv_len, int64_t C, float qk_log2, int n_heads, int rgs,
     float* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int D = kSD;
-  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ __align__(16) _Float16 sK[kSMaxKeys * kSKStride];   // K rows, fp16 codes in unpack8_perm order
+  __shared__ __align__(16) _Float16 sV[kSD * kSVStride];         // V^T, fp16 codes (zeros past kv_len)
+  __shared__ __align__(16) float csk[kSMaxKeys];                  // K scale x softmax scale x log2 e (0 past kv_len)
+  __shared__ __align__(16) _Float16 svh[kSVStride];               // V scale (0 past kv_len)
   // per wave: largest |q| (bf16 bits), |K scale| and |V scale| (fp16 bits)
   __shared__ uint32_t s_mx[3][kSMaxWaves];
-
-  const ShortLayout ly = short_layout(kv_len);
-  _Float16* sK = reinterpret_cast<_Float16*>(smem);
-  _Float16* sV = reinterpret_cast<_Float16*>(smem + ly.v_off);
-  float* csk = reinterpret_cast<float*>(smem + ly.csk_off);
-  _Float16* svh = reinterpret_cast<_Float16*>(smem + ly.svh_off);
+  const int lk8 = (kv_len + 7) & ~7;     // tokens converted (zeros past kv_len)
+  const int lk32 = (kv_len + 31) & ~31;  // tokens the key blocks read
 
   const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
   const int nth = 64 * nw;
@@ -119,7 +106,7 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
   const int row0 = rg * 32 * nw;   // first query row of this workgroup
   const int row = row0 + wave * 32 + r;
   const int off = kv_len - Sq;   // >= 0 whenever CAUSAL
-  const int nq = ly.sv / 4;      // V token quads
+  const int nq = lk8 / 4;        // V token quads
 
   // (batch, layer query head, cache row 0) of head index hh
   auto head_of = [&](int hh, int& b, int& hq, int64_t& kvrow0) {
@@ -137,7 +124,7 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
   uint4v qraw[D / 16];
   uint32_t kraw[8];
   uint32_t vraw[3][4];
-  uint32_t ksc, vsc0, vsc1;
+  uint32_t ksc, vsc0;
   auto issue_loads = [&](int hh) {
     int b, hq;
     int64_t kvrow0;
@@ -167,7 +154,6 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
     }
     ksc = __builtin_amdgcn_raw_buffer_load_b16(rks, (uint32_t)(tid * 2), 0, 0);
     vsc0 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (uint32_t)(tid * 2), 0, 0);
-    vsc1 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (uint32_t)((tid + nth) * 2), 0, 0);
   };
 
   const int wrow_lo = row0 + wave * 32;
@@ -179,7 +165,11 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
   int nfull = kv_len / 32;
   if (CAUSAL) nfull = min(nfull, max(0, (wrow_lo + off + 1) / 32));
   nfull = min(nfull, nkb);
-  const int kslot = (r >> 1) & 7;
+  // per-lane bases: K row r at chunk j, V^T row r at token 4 j, tables at 4 j
+  const _Float16* kbase = sK + r * kSKStride + 8 * j;
+  const _Float16* vbase = sV + r * kSVStride + 4 * j;
+  const float* cbase = csk + 4 * j;
+  const _Float16* sbase = svh + 4 * j;
 
   issue_loads(hh);
   {
@@ -190,7 +180,7 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
       for (int s = 0; s < D / 16; ++s) qmb = max(qmb, bf16x8_max_abs_bits(qraw[s]));
       qmb = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(qmb)));
       // K and V scale maxima in one reduction: |K| in bits 16-30, |V| in bits 0-14
-      const uint32_t kv = ((ksc & 0x7FFFu) << 16) | max(vsc0 & 0x7FFFu, vsc1 & 0x7FFFu);
+      const uint32_t kv = ((ksc & 0x7FFFu) << 16) | (vsc0 & 0x7FFFu);
       const uint32_t kvk = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(kv & 0x7FFF0000u)));
       const uint32_t kvv = bitcast<uint32_t>(wave_max_nonneg(bitcast<float>(kv & 0x7FFFu)));
       if (lane == 0) {
@@ -236,9 +226,9 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int i = tid + it * nth;
-      if (i < ly.lk8 * 8) {
+      if (i < lk8 * 8) {
         const int t = i >> 3, w = i & 7;
-        *reinterpret_cast<half8v*>(sK + t * D + 8 * (w ^ ((t >> 1) & 7))) = unpack8_perm(kraw[it]);
+        *reinterpret_cast<half8v*>(sK + t * kSKStride + 8 * w) = unpack8_perm(kraw[it]);
       }
     }
 #pragma unroll
@@ -251,13 +241,12 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
           const half2v a = nib_pair2(vraw[it][0], vraw[it][1], n);
           const half2v c2 = nib_pair2(vraw[it][2], vraw[it][3], n);
           const uint2v x = {bitcast<uint32_t>(a), bitcast<uint32_t>(c2)};
-          *reinterpret_cast<uint2v*>(sV + (8 * w + n) * ly.sv + 4 * u) = x;
+          *reinterpret_cast<uint2v*>(sV + (8 * w + n) * kSVStride + 4 * u) = x;
         }
       }
     }
-    if (tid < ly.lk32) csk[tid] = f16bits_to_f32((uint16_t)ksc) * qk;
-    if (tid < ly.sv) svh[tid] = bitcast<_Float16>((uint16_t)vsc0);
-    if (tid + nth < ly.sv) svh[tid + nth] = bitcast<_Float16>((uint16_t)vsc1);
+    if (tid < lk32) csk[tid] = f16bits_to_f32((uint16_t)ksc) * qk;
+    if (tid < lk8) svh[tid] = bitcast<_Float16>((uint16_t)vsc0);
     __syncthreads();
 
     int b, hq;
@@ -287,11 +276,11 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
       float16v st = float16v{};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const half8v a = *reinterpret_cast<const half8v*>(sK + (t0 + r) * D + 8 * ((2 * s + j) ^ kslot));
+        const half8v a = *reinterpret_cast<const half8v*>(kbase + t0 * kSKStride + 16 * s);
         st = mfma32x32x16(a, qop[s], st);
       }
       // ---- online softmax; lane's tokens t0 + 8 vq + 4 j + i
-      auto colf = [&](int vq) { return *reinterpret_cast<const float4v*>(csk + t0 + 8 * vq + 4 * j); };
+      auto colf = [&](int vq) { return *reinterpret_cast<const float4v*>(cbase + t0 + 8 * vq); };
       const float tau = HILO ? tau_hl : kSTau;
       float mx;
       if constexpr (FULL) {
@@ -338,7 +327,10 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
         if (!FULL && t0 + 8 * vq >= kv_len) break;   // uniform
-        const half4v sv = *reinterpret_cast<const half4v*>(svh + t0 + 8 * vq + 4 * j);
+        // keeps this step's LDS reads here: hoisted, the four steps' column
+        // factors, V scales and V operands would be live at once
+        asm volatile("" ::: "memory");
+        const half4v sv = *reinterpret_cast<const half4v*>(sbase + t0 + 8 * vq);
         float p[4];
         if constexpr (FULL) {
           const float4v c = colf(vq);
@@ -364,7 +356,7 @@ __global__ __launch_bounds__(64 * kSMaxWaves) __attribute__((amdgpu_waves_per_eu
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const half4v a = *reinterpret_cast<const half4v*>(sV + (32 * db + r) * ly.sv + t0 + 8 * vq + 4 * j);
+          const half4v a = *reinterpret_cast<const half4v*>(vbase + 32 * db * kSVStride + t0 + 8 * vq);
           o_acc[db] = mfma32x32x8(a, ph, o_acc[db]);
           if constexpr (HILO) o_acc[db] = mfma32x32x8(a, pl, o_acc[db]);
         }
@@ -417,17 +409,8 @@ hipError_t launch_prefill_short(const uint16_t* q, const uint8_t* kc, const uint
   const int nw = (int)std::max<int64_t>(4, (Sq + 32 * rgs - 1) / (32 * rgs));
   const int n_heads = (int)(B * Hkv * G);
   const int grid = ((n_heads + 7) / 8) * 8 * rgs;
-  const ShortLayout ly = short_layout((int)kv_len);
   auto kern = causal ? prefill_short_kernel<true> : prefill_short_kernel<false>;
-  // a 256-token head takes 68 KB of LDS: allow the kernels the larger
-  // dynamic LDS once
-  static const hipError_t attr[2] = {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_short_kernel<false>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, short_layout(256).bytes),
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_short_kernel<true>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, short_layout(256).bytes)};
-  if (attr[causal ? 1 : 0] != hipSuccess) return attr[causal ? 1 : 0];
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), (size_t)ly.bytes, stream, q, kc, ks, vc, vs, kv_heads, Hall,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), 0, stream, q, kc, ks, vc, vs, kv_heads, Hall,
                      (int)Hq, (int)Hkv, G, (int)Sq, (int)kv_len, C, softmax_scale * kLog2e, n_heads, rgs, out, lse);
   return hipGetLastError();
 }
