@@ -464,7 +464,10 @@ def bench_prefill(torch, qkv, w, iters, bits=4, group=0):
 
     for i in range(2):
         run(i)
-    avg_ms, med_ms = per_launch_ms(torch, run, iters, 1)
+    # back-to-back launches behind a GPU hold (no per-launch event packets,
+    # which add ~2 us to a 30 us kernel); the per-launch median beside it
+    avg_ms = region_ms(torch, run, iters, 1)
+    _, med_ms = per_launch_ms(torch, run, iters, 1)
     fl = prefill_flops(w)
     nbytes = prefill_bytes(w, bits, group)
     res = {"workload": w.name, "bits": bits, "group": group or None, "avg_ms": avg_ms, "median_ms": med_ms,
