@@ -280,7 +280,7 @@ def bench_paged(torch, qkv, w, steps):
     cached = torch.from_numpy(lens - 1).cuda()        # rows before the step; the step appends one
     out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
     max_len = int(lens.max())
-    # the library's plan for per-sequence lengths: its uniform plan, with splits of at most 4096 tokens
+    # the library's plan for per-sequence lengths: its uniform plan, with splits of at most 128 chunks
     ns = max(qkv.decode_auto_splits(w.B, w.Hq, w.Hkv, w.Sq, max_len, w.D), -(-max_len // 4096))
     ws = torch.zeros(max(qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, max_len, w.D), 1),
                      dtype=torch.uint8, device="cuda")

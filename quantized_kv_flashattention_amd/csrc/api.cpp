@@ -471,7 +471,6 @@ qkvfa::DecodePlan buffered_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, 
     p = qkvfa::plan_decode(B, Hkv, B * Hq * Sq, kv_len, (int)D, num_splits, current_cus(), false);
   } else {
     p.n_split = 0;
-    p.split_len = 32;
   }
   if (tail_rows > 0) p.n_split += 1;
   return p;

@@ -2,8 +2,12 @@
 //
 // Each of the G*Sq query rows of a GQA group attends cache rows [0, kv_len)
 // (append-then-attend decode, TurboAttention arXiv 2412.08585 §2.1).  The KV
-// length is cut into ranges ("splits"); each workgroup streams the packed
-// int4 K/V codes of one (split, KV head, batch) straight from HBM with
+// rows are dealt to "splits" chunk by chunk: with n splits, split s takes the
+// 32-token chunks s, s + n, s + 2n, ..., so the workgroups of one (batch, KV
+// head) stream neighbouring rows at the same time (measured: fewer separate
+// streams in flight read HBM faster than one contiguous range per split).
+// Each workgroup streams the packed int4 K/V codes of one (split, KV head,
+// batch) straight from HBM with
 // coalesced loads, converts the codes exactly to fp16 in registers (no
 // dequantized K/V is ever written anywhere: "Quantized Cross-Attention ..."
 // §3.1), and runs an online softmax (FlashAttention, TurboAttention §2.2).
@@ -37,11 +41,11 @@
 // The ticket returns to zero after the merge, ready for the next call.
 //
 // Append mode (a decode step that first appends its new K/V rows): before
-// streaming, the workgroup whose split holds new rows quantizes them with the
+// streaming, each workgroup quantizes the new rows of its own chunks with the
 // shared row quantizer, writes codes and scales to the cache (for later steps)
 // and keeps a copy in LDS.  The new rows are the last rows of the attended
-// range, so the chunk loop streams only the older rows of the split and at
-// most two tail chunks then take the new rows from the LDS copy: the kernel
+// range, so the chunk loop streams only chunks of older rows and the chunks
+// that hold new rows (at most three) then take them from the LDS copy: the kernel
 // never reads the rows it wrote and needs no memory ordering between those
 // stores and its own loads.  Outputs and the written rows are bit-identical
 // to a separate append followed by decode.
@@ -80,7 +84,7 @@ __device__ __forceinline__ float dpp_f(float old, float src) {
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
 constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
-constexpr int kRaggedSplitChunks = 128;     // ragged batches: at most 4096 tokens per split
+constexpr int kRaggedSplitChunks = 128;     // ragged batches: at most 128 chunks per split
 constexpr int kMaxTail = 64;                // rows of the INT8 decode buffer one call attends
 constexpr int kMaxMergeLse = 4 * 16 * 68;  // LSE table of the merging workgroup (floats)
 
@@ -162,7 +166,7 @@ struct DecodeArgs {
   const float* tv_new;
   int tail_len, tail_rows, buf_rows;
   int64_t C;
-  int Hq, Hkv, G, Sq, kv_len, split_len, n_split;
+  int Hq, Hkv, G, Sq, kv_len, n_split;
   float qk_log2;
 };
 
@@ -309,8 +313,36 @@ void decode_kernel(const DecodeArgs a) {
   // rows of this call's (batch, KV head) units only (= grow0 without a map).
   const int64_t grow0 = ((int64_t)b * a.Hq + (int64_t)gq * G) * Sq;
   const int64_t prow0 = ((int64_t)b * a.Hkv + g) * G * Sq;
-  const int t_begin = split * a.split_len;
-  const int t_end = min(L_b, t_begin + a.split_len);   // <= t_begin: nothing to attend here
+  // The chunks of cache split `split` (of ns_c; with an INT8 buffer the last
+  // split attends the buffered rows instead): c_first, c_first + c_step, ...,
+  // c_count of them, among the sequence's gc_end 32-token chunks.
+  //  * contiguous cache: interleaved, split s takes chunks s, s + ns_c, ...
+  //    With lengths per sequence, a sequence uses only as many splits as its
+  //    length needs at the plan's chunks per split (the longest uses them
+  //    all), so a short sequence keeps few workgroups busy.
+  //  * paged cache: a range of cps consecutive chunks, so that each page is
+  //    read by one workgroup (interleaved, both workgroups of a page would
+  //    look up its address translation: measured 9% slower on a ragged batch)
+  const int t_end = L_b;
+  const int gc_end = (t_end + kChunk - 1) / kChunk;   // chunks of the sequence
+  int ns_c = max(a.n_split - (a.tail_rows > 0 ? 1 : 0), 1);
+  const int cps = ((a.kv_len + kChunk - 1) / kChunk + ns_c - 1) / ns_c;   // the plan's chunks per split
+  if (!PAGED && a.kv_lens != nullptr) ns_c = max(min(ns_c, (gc_end + cps - 1) / cps), 1);
+  const int c_first = PAGED ? split * cps : split;
+  const int c_step = PAGED ? 1 : ns_c;
+  const int c_count = PAGED ? min(max(gc_end - c_first, 0), cps)
+                            : (split < ns_c && gc_end > split ? (gc_end - split + ns_c - 1) / ns_c : 0);
+  // splits with a chunk of this sequence: a prefix 0 .. n_used - 1
+  const int n_used = PAGED ? min((gc_end + cps - 1) / cps, ns_c) : min(ns_c, gc_end);
+  const int t_begin = c_first * kChunk;   // first row of the split's first chunk
+  const int cstride = c_step * kChunk;     // rows between its chunks
+  const bool nothing = c_count == 0;
+  // chunk gc of the sequence is this split's chunk number *k
+  auto own_chunk = [&](int gc, int* k) {
+    const int d = gc - c_first;
+    *k = d / c_step;
+    return d >= 0 && d % c_step == 0 && *k < c_count;
+  };
 
   // Row index (in the cache arrays' row space) of token t of this (batch, KV
   // head): contiguous cache row (b, g, t), or row t % P of its page.
@@ -318,7 +350,8 @@ void decode_kernel(const DecodeArgs a) {
   const int P = PAGED ? a.page_size : 1;
   const int pg0 = PAGED ? t_begin / P : 0;
   // pages of this split whose ids are cached in LDS
-  const int npg = (PAGED && t_end > t_begin) ? min((t_end - 1) / P - pg0 + 1, kMaxSplitPages) : 0;
+  const int t_last = min(t_end, (c_first + c_count) * kChunk) - 1;   // the split's last row
+  const int npg = (PAGED && !nothing) ? min(t_last / P - pg0 + 1, kMaxSplitPages) : 0;
   auto page_of = [&](int t) -> int64_t {   // from the table in global memory
     const int idx = min(t / P, a.max_pages - 1);
     const int pid = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_pages + idx]);
@@ -345,14 +378,13 @@ void decode_kernel(const DecodeArgs a) {
   const uint32_t offv = (uint32_t)(8 * j * ROWB + (BITS == 4 ? 4 : 2) * (r % DW));
   const uint32_t offs = (uint32_t)(2 * (lane & 31));
 
-  // ---- append mode: this split's new rows [new_lo, new_hi)
-  const int new_lo = append ? max(pos_b, t_begin) : 0;
-  const int new_hi = append ? min(pos_b + a.n_new, t_end) : 0;
-  // The chunk loop covers the split up to the first chunk that holds a new
-  // row; the remaining (tail) chunks are handled after it, each by the wave
-  // the plain decode gives it, so the arithmetic is the plain decode's.
-  const int t_main =
-      append ? min(t_end, t_begin + (max(pos_b, t_begin) - t_begin) / kChunk * kChunk) : t_end;
+  // ---- append mode: rows [pos_b, t_end) are new.  The chunk loop covers
+  // this split's chunks before the first that holds a new row (chunks
+  // [0, gc_main) of the sequence, rows below t_main); the split's remaining
+  // (tail) chunks are handled after it, each by the wave the plain decode
+  // gives it, so the arithmetic is the plain decode's.
+  const int gc_main = append ? pos_b / kChunk : gc_end;
+  const int t_main = append ? gc_main * kChunk : t_end;
 
   const bool direct = (a.n_split == 1);
   // one descriptor over all partial outputs (the planner keeps them < 2 GiB)
@@ -378,7 +410,7 @@ void decode_kernel(const DecodeArgs a) {
     if (!s_last) return;
     const int n_split = a.n_split;
     // splits that start before this sequence's length; the rest attended nothing
-    const int n_live = a.tail_rows > 0 ? n_split : min(n_split, (L_b + a.split_len - 1) / a.split_len);
+    const int n_live = a.tail_rows > 0 ? n_split : n_used;
     // item idx: four output values (query row idx / (D/4), dims 4 (idx % (D/4)) + 0..3)
     const int n_items = R * (D / 4);
     auto item_off = [&](int idx) -> uint32_t {
@@ -526,13 +558,13 @@ void decode_kernel(const DecodeArgs a) {
   // split that has cache rows to attend.
   auto main_body = [&]() {
     // Codes of the chunk starting at token c0, through buffer descriptors whose
-    // range ends at t_main <= kv_len (the split end, before any new rows): the
-    // hardware returns zero for
-    // any row at or past it (those tokens are masked) without touching memory.
-    // So no load leaves the valid rows, the last chunk needs no clamping, and a
-    // chunk past the split can be "loaded" unconditionally (all zeros, no
-    // traffic), which keeps the prefetch branch-free: a conditional prefetch
-    // makes the compiler wait for every outstanding load where the paths join.
+    // range ends at lim <= kv_len (the end of the split's last chunk, before
+    // any new rows): the hardware returns zero for any row at or past it
+    // (those tokens are masked) without touching memory.  So no load leaves
+    // the valid rows, the last chunk needs no clamping, and a chunk past the
+    // split can be "loaded" unconditionally (all zeros, no traffic), which
+    // keeps the prefetch branch-free: a conditional prefetch makes the
+    // compiler wait for every outstanding load where the paths join.
     auto load_chunk = [&](int c0, Regs& cr, int lim, bool from_lds) {
       // a chunk is 32 rows; with a paged cache it never straddles a page.  The
       // clamp is made scalar explicitly: computed in a vector register, the
@@ -602,18 +634,24 @@ void decode_kernel(const DecodeArgs a) {
       }
     };
 
-    const int n_chunks = (t_main - t_begin + kChunk - 1) / kChunk;
+    // this split's chunks before gc_main
+    const int n_chunks = gc_main > c_first ? min((gc_main - c_first + c_step - 1) / c_step, c_count) : 0;
     Regs cur;
-    load_chunk(t_begin + wave * kChunk, cur, t_main, false);
+    // loads stop at the end of the split's last chunk as well: a paged split's
+    // range is followed by another split's rows
+    const int t_ld = min(t_main, (c_first + (c_count - 1) * c_step + 1) * kChunk);
+    load_chunk(t_begin + wave * cstride, cur, t_ld, false);
 
-    // ---- append mode: quantize the new rows (one wave per row and tensor,
-    //      from the last wave down: with one row block the first half of the
-    //      waves converts the query meanwhile), while the first chunk loads
-    //      (4-bit caches only)
+    // ---- append mode: quantize the new rows of this split's chunks (one wave
+    //      per row and tensor, from the last wave down: with one row block the
+    //      first half of the waves converts the query meanwhile), while the
+    //      first chunk loads (4-bit caches only)
     if (BITS == 4 && !ASYM && append) {
-      const int ntask = 2 * max(new_hi - new_lo, 0);
+      const int ntask = 2 * max(t_end - pos_b, 0);
       for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
-        const int t = new_lo + (task >> 1);
+        const int t = pos_b + (task >> 1);
+        int k;
+        if (!own_chunk(t / kChunk, &k)) continue;   // another split's chunk
         const bool isv = (task & 1) != 0;
         const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - pos_b)) * D;
         const int64_t row = row_of(t, false);
@@ -1186,33 +1224,36 @@ void decode_kernel(const DecodeArgs a) {
     };
 
     for (int c = wave; c < n_chunks; c += kWaves) {
-      const int c0 = t_begin + c * kChunk;
+      const int c0 = t_begin + c * cstride;
       // Compiler-only barrier: keeps the query-operand LDS reads inside the loop
       // instead of hoisted into (NB * D / 8) live registers per lane.
       asm volatile("" ::: "memory");
       if constexpr (kPrefetch) {
         Regs nxt;
-        load_chunk(c0 + kWaves * kChunk, nxt, t_main, true);
+        load_chunk(c0 + kWaves * cstride, nxt, t_ld, true);
         process(c0, cur, t_main);
         cur = nxt;
       } else {
         process(c0, cur, t_main);
-        load_chunk(c0 + kWaves * kChunk, cur, t_main, true);
+        load_chunk(c0 + kWaves * cstride, cur, t_ld, true);
       }
     }
 
-    // ---- append mode: tail chunks [t_main, t_end).  Rows before pos come from
-    //      the cache (the load range ends at pos, so no row at or past it is
+    // ---- append mode: this split's tail chunks (chunks gc_main .. gc_end - 1
+    //      of the sequence that are its own).  Rows before pos come from the
+    //      cache (the load range ends at pos, so no row at or past it is
     //      read), rows from pos on from the LDS copy of the new rows.
     if constexpr (BITS == 4 && !ASYM) if (append) {
-      for (int c0 = t_main; c0 < t_end; c0 += kChunk) {
-        if (wave != ((c0 - t_begin) / kChunk) % kWaves) continue;
+      for (int gc = gc_main; gc < gc_end; ++gc) {
+        int k;
+        if (!own_chunk(gc, &k) || wave != k % kWaves) continue;
+        const int c0 = gc * kChunk;
         Regs cr;
         load_chunk(c0, cr, max(pos_b, c0), true);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
-          if (tk >= pos_b && tk < new_hi) {
+          if (tk >= pos_b && tk < t_end) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) cr.kw[kb][kk] = s_nk[(tk - pos_b) * DW + KK * j + kk];
           }
@@ -1220,10 +1261,10 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tv = c0 + 8 * j + e;
-          if (tv >= pos_b && tv < new_hi) cr.vw[e] = s_nv[(tv - pos_b) * DW + (r % DW)];
+          if (tv >= pos_b && tv < t_end) cr.vw[e] = s_nv[(tv - pos_b) * DW + (r % DW)];
         }
         const int ts = c0 + (lane & 31);
-        if (ts >= pos_b && ts < new_hi) {
+        if (ts >= pos_b && ts < t_end) {
           cr.sk = s_nks[ts - pos_b];
           cr.sv = s_nvs[ts - pos_b];
         }
@@ -1439,10 +1480,10 @@ void decode_kernel(const DecodeArgs a) {
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  // ---- a split past this sequence's length: nothing to attend.  It writes
+  // ---- a split with no chunk of this sequence: nothing to attend.  It writes
   //      no partial (the merge skips it), only takes its ticket; alone, it
   //      writes the empty result (output 0, LSE -inf).
-  } else if (t_end <= t_begin) {
+  } else if (nothing) {
     if (direct) {
       for (int idx = threadIdx.x; idx < R * (D / 4); idx += 64 * kWaves) {
         const int row = idx / (D / 4);
@@ -1518,7 +1559,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
   if (num_splits <= 0) {
     // eight waves per CU (one 8-wave or two 4-wave workgroups): measured best
     // on MI355X for both a 128-group 8K-token and an 8-group 128K-token
-    // decode.  Every workgroup starts at once and streams its range at the
+    // decode.  Every workgroup starts at once and streams its chunks at the
     // shared HBM rate; more splits add per-split epilogue and merge latency
     // without adding bandwidth
     const int64_t target_wgs = (int64_t)(num_cus > 0 ? num_cus : 256) * 8 / waves;
@@ -1526,10 +1567,10 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
     const int64_t max_ns = chunks / waves > 0 ? chunks / waves : 1;   // >= one chunk per wave
     if (ns > max_ns) ns = max_ns;
     // Lengths that differ per sequence (known only on the device): the plan
-    // covers the longest, so a sequence's work is its number of non-empty
+    // covers the longest, and a shorter sequence has shorter (or empty late)
     // splits.  Splits of at most kRaggedSplitChunks chunks keep the longest
     // sequences from finishing alone (measured on a 64-sequence batch of
-    // 512..16384 tokens: 4096-token splits 138 us, one split each 158 us)
+    // 512..16384 tokens: 128-chunk splits 138 us, one split each 158 us)
     if (ragged) {
       const int64_t ns_r = (chunks + kRaggedSplitChunks - 1) / kRaggedSplitChunks;
       if (ns < ns_r) ns = ns_r;
@@ -1546,10 +1587,8 @@ DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int
   const int64_t max_ns_bytes = ((int64_t)1 << 31) / ((int64_t)rows * D * 4 + 1);
   if (ns > max_ns_bytes) ns = max_ns_bytes;
   if (ns < 1) ns = 1;
-  const int64_t cps = (chunks + ns - 1) / ns;   // chunks per split
   DecodePlan p;
-  p.split_len = (int)(cps * kChunk);
-  p.n_split = (int)((chunks + cps - 1) / cps);   // no empty split
+  p.n_split = (int)ns;   // <= chunks: every split has a chunk
   return p;
 }
 
@@ -1629,7 +1668,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* kc, const uint16_t* k
   }
   a.C = C;
   a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / a.Hkv_all); a.Sq = (int)Sq; a.kv_len = (int)kv_len;
-  a.split_len = plan.split_len; a.n_split = plan.n_split;
+  a.n_split = plan.n_split;
   a.qk_log2 = softmax_scale * kLog2e;
   if (D == 128) return launch_d<128>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);
   return launch_d<64>(a, (int)B, (int)Hkv, plan.n_split, bits, stream);

@@ -18,13 +18,12 @@ hipError_t launch_quantize_append(const float* src, uint8_t* codes, uint16_t* sc
                                   int h_src = 0);
 
 struct DecodePlan {
-  int n_split;     // number of KV ranges
-  int split_len;   // tokens per range (multiple of 32)
+  int n_split;     // number of splits; split s takes 32-token chunks s, s + n_split, ...
 };
 
 // Split plan for rows = B*Hq*Sq query rows; num_splits = 0 picks the count.
 // ragged: per-sequence lengths up to kv_len (the count then also bounds the
-// tokens per split).
+// chunks per split).
 DecodePlan plan_decode(int64_t B, int64_t Hkv, int64_t rows, int64_t kv_len, int D, int num_splits,
                        int num_cus, bool ragged);
 

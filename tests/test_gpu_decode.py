@@ -173,6 +173,8 @@ APPEND_CASES = [
     (1, 4, 2, 3, 0, 3, 8, 64, 0),           # the whole cache is new
     (1, 2, 2, 64, 100, 64, 200, 64, 0),     # the most new rows one call takes
     (3, 12, 4, 1, 2049, 2, 2100, 128, 0),   # two new rows, one query row
+    (1, 8, 2, 1, 100, 64, 200, 64, 2),      # new rows in chunks 3, 4, 5: splits 1, 0, 1
+    (2, 8, 2, 2, 60, 40, 128, 128, 3),      # new rows in chunks 1, 2, 3: splits 1, 2, 0
 ]
 
 

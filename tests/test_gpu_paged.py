@@ -143,7 +143,7 @@ CASES = [
     (1, 4, 1, 16, (700,), 128, 32, 16, 0),                   # 64 rows per group; new rows cross a page
     (3, 8, 2, 1, (0, 0, 40), 64, 32, 2, 5),                  # appends into empty sequences
     (2, 8, 8, 1, (20000, 17), 64, 32, 0, 1),                 # one split over 625 pages
-    (4, 8, 2, 1, (50, 700, 2500, 9000), 128, 64, 1, 40),    # 1, 3, 10, 36 live splits: both merge forms
+    (4, 8, 2, 1, (50, 700, 2500, 9000), 128, 64, 1, 40),    # 2, 22, 40, 40 live splits: both merge forms
 ]
 
 
@@ -163,10 +163,13 @@ def test_paged_decode_matches_oracle(case, paged):
     _check(q, exp, table, lens, n_new, P, scale, out, lse, f"{case} paged={paged}")
 
 
-@pytest.mark.parametrize("n_new,ns", [(0, 0), (1, 0), (3, 4)])
-def test_paged_equals_contiguous_bitwise(n_new, ns):
-    """Equal lengths and a tight bound: the paged step is the contiguous step,
-    bit for bit (same split plan, same arithmetic), only the addresses differ."""
+@pytest.mark.parametrize("n_new,ns", [(0, 1), (1, 1), (0, 0), (1, 0), (3, 4)])
+def test_paged_equals_contiguous(n_new, ns):
+    """Equal lengths and a tight bound.  With one split the paged step is the
+    contiguous step bit for bit (same arithmetic, only the addresses differ);
+    with several, a paged split takes a range of consecutive chunks and a
+    contiguous one interleaved chunks, so the two agree up to the merge's
+    rounding.  The cache rows an appending step writes are identical."""
     B, Hq, Hkv, D, P, L = 3, 32, 8, 128, 64, 3000
     lens = (L,) * B
     q, pool, table, k_new, v_new = _pool_case(5, B, Hq, Hkv, 1, lens, D, P, n_new, True)
@@ -183,8 +186,16 @@ def test_paged_equals_contiguous_bitwise(n_new, ns):
     else:
         o2, l2 = qkv.decode(q_to_dev(q), ref, L, softmax_scale=0.088, num_splits=ns, return_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, o2), f"max diff {float((out - o2).abs().max())}"
-    assert torch.equal(lse, l2)
+    if ns == 1:
+        assert torch.equal(out, o2), f"max diff {float((out - o2).abs().max())}"
+        assert torch.equal(lse, l2)
+    else:
+        # each side rounds P~ = p s_V to fp16 once per value: an output moves by
+        # at most 2^-11 * 7 * max s_V on either side (7 = the largest |code|)
+        vs_max = float(np.concatenate([cc[3].reshape(-1).view(np.float16).astype(np.float32),
+                                       np.abs(v_new).reshape(-1) / 7]).max())
+        assert float((out - o2).abs().max()) <= 2 * 2.0 ** -11 * 7 * vs_max
+        assert float((lse - l2).abs().max()) < 1e-5
     if n_new:
         got = _from_dev(cache)
         want = _from_dev(ref)
