@@ -239,6 +239,11 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int DW = D / 8;     // dwords per packed row
   constexpr int NPB = D / 16;   // PV MFMAs (16 head dims each)
   constexpr int ROWB = D * BITS / 8;   // bytes per packed row
+  // Cache policy of the code, scale and parameter loads: non-temporal (each
+  // row is read once per call; measured 5% faster on the 8K step).  3-bit
+  // rows take two loads from each row (low and top bits), which the
+  // non-temporal policy turned into separate fetches (12% slower): normal.
+  constexpr int kStream = BITS == 3 ? 0 : 2;
   // bias of element e (0..7) of a K operand and of the codes of PV block p
   auto kbias = [](int e) { return BITS == 4 ? kNibBias : lowbit_bias<BITS>(e >> 1); };
   auto vbias = [](int p) { return BITS == 4 ? kNibBias : lowbit_bias<BITS>(p & 3); };
@@ -579,37 +584,37 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if constexpr (KK == 4) {
-            const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, 0);
+            const uint4v w = __builtin_amdgcn_raw_buffer_load_b128(rk, offk + kb * 4 * ROWB, 0, kStream);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) cr.kw[kb][kk] = w[kk];
           } else {
-            const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, 0);
+            const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, offk + kb * 4 * ROWB, 0, kStream);
             cr.kw[kb][0] = w[0];
             cr.kw[kb][1] = w[1];
           }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, 0);
+        for (int e = 0; e < 8; ++e) cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, offv + e * ROWB, 0, kStream);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const uint32_t o = offk + kb * 4 * ROWB;
           if constexpr (KK == 4) {
-            const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0);
+            const uint2v w = __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, kStream);
             cr.kw[kb][0] = w[0];
             cr.kw[kb][1] = w[1];
             // top bits: KK bytes at D/4 + KK j of the row (o sits at 2 KK j)
-            if constexpr (BITS == 3) cr.kh[kb] = __builtin_amdgcn_raw_buffer_load_b32(rk, o + D / 4 - KK * j, 0, 0);
+            if constexpr (BITS == 3) cr.kh[kb] = __builtin_amdgcn_raw_buffer_load_b32(rk, o + D / 4 - KK * j, 0, kStream);
           } else {
-            cr.kw[kb][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o, 0, 0);
-            if constexpr (BITS == 3) cr.kh[kb] = __builtin_amdgcn_raw_buffer_load_b16(rk, o + D / 4 - KK * j, 0, 0);
+            cr.kw[kb][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, o, 0, kStream);
+            if constexpr (BITS == 3) cr.kh[kb] = __builtin_amdgcn_raw_buffer_load_b16(rk, o + D / 4 - KK * j, 0, kStream);
           }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, offv + e * ROWB, 0, 0);
+          cr.vw[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, offv + e * ROWB, 0, kStream);
           if constexpr (BITS == 3)   // top bits: byte D/4 + r % DW of the row (offv sits at 2 (r % DW))
-            cr.vh[e] = __builtin_amdgcn_raw_buffer_load_b8(rv, offv + e * ROWB + D / 4 - (r % DW), 0, 0);
+            cr.vh[e] = __builtin_amdgcn_raw_buffer_load_b8(rv, offv + e * ROWB + D / 4 - (r % DW), 0, kStream);
         }
       }
       if constexpr (ASYM) {
@@ -618,19 +623,19 @@ void decode_kernel(const DecodeArgs a) {
         const rsrc_t rkp = make_rsrc(a.kp + row0 * NGA, rows_left * NGA * 4);
         const rsrc_t rvp = make_rsrc(a.vp + row0 * NGA, rows_left * NGA * 4);
         if constexpr (NPW == 2) {
-          const uint2v wk = __builtin_amdgcn_raw_buffer_load_b64(rkp, 8 * lane, 0, 0);
-          const uint2v wv = __builtin_amdgcn_raw_buffer_load_b64(rvp, 8 * lane, 0, 0);
+          const uint2v wk = __builtin_amdgcn_raw_buffer_load_b64(rkp, 8 * lane, 0, kStream);
+          const uint2v wv = __builtin_amdgcn_raw_buffer_load_b64(rvp, 8 * lane, 0, kStream);
           cr.kpw[0] = wk[0];
           cr.kpw[1] = wk[1];
           cr.vpw[0] = wv[0];
           cr.vpw[1] = wv[1];
         } else {
-          cr.kpw[0] = __builtin_amdgcn_raw_buffer_load_b32(rkp, 4 * lane, 0, 0);
-          cr.vpw[0] = __builtin_amdgcn_raw_buffer_load_b32(rvp, 4 * lane, 0, 0);
+          cr.kpw[0] = __builtin_amdgcn_raw_buffer_load_b32(rkp, 4 * lane, 0, kStream);
+          cr.vpw[0] = __builtin_amdgcn_raw_buffer_load_b32(rvp, 4 * lane, 0, kStream);
         }
       } else {
-        cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, 0);
-        cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, 0);
+        cr.sk = __builtin_amdgcn_raw_buffer_load_b16(rks, offs, 0, kStream);
+        cr.sv = __builtin_amdgcn_raw_buffer_load_b16(rvs, offs, 0, kStream);
       }
     };
 
