@@ -179,21 +179,33 @@ __device__ __forceinline__ half8v unpack8_perm_b(uint32_t x) {
   return bitcast<half8v>(w);
 }
 
+// One v_bitop3_b32: bit 4a + 2b + c of the table T is the result bit for
+// input bits a, b, c.
+template <uint32_t T>
+__device__ __forceinline__ uint32_t bitop3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, T);
+}
+constexpr uint32_t kAndXor = 0x6C;      // (a & c) ^ b
+constexpr uint32_t kAndOr = 0xEA;       // (a & b) | c
+constexpr uint32_t kNotAndOr = 0xAE;    // (~a & b) | c
+
 // 2-bit field in bits 4-5 (and 20-21) -> c + 66; in bits 6-7 (22-23) -> c + 18.
+// ((x ^ s) & m) | e with the sign bit s inside the mask m and the exponent e
+// outside it is (x & m) ^ (s | e): one v_bitop3.
 __device__ __forceinline__ uint32_t b2_at4(uint32_t x) {
-  return ((x ^ 0x00200020u) & 0x00300030u) | 0x54005400u;
+  return bitop3<kAndXor>(x, 0x00200020u | 0x54005400u, 0x00300030u);
 }
 __device__ __forceinline__ uint32_t b2_at6(uint32_t x) {
-  return ((x ^ 0x00800080u) & 0x00C000C0u) | 0x4C004C00u;
+  return bitop3<kAndXor>(x, 0x00800080u | 0x4C004C00u, 0x00C000C0u);
 }
 // 3-bit code: its low two bits in bits 4-5 of x and its top bit at bit 6 of
 // zs (both halves alike) -> c + 68; low bits in 6-7, top bit at 8 -> c + 20.
 // The top bit enters inverted (offset binary c + 4 = low + 4 (1 - top)).
 __device__ __forceinline__ uint32_t b3_at4(uint32_t x, uint32_t zs) {
-  return ((x & 0x00300030u) | 0x54005400u) | (~zs & 0x00400040u);
+  return bitop3<kNotAndOr>(zs, 0x00400040u, bitop3<kAndOr>(x, 0x00300030u, 0x54005400u));
 }
 __device__ __forceinline__ uint32_t b3_at6(uint32_t x, uint32_t zs) {
-  return ((x & 0x00C000C0u) | 0x4C004C00u) | (~zs & 0x01000100u);
+  return bitop3<kNotAndOr>(zs, 0x01000100u, bitop3<kAndOr>(x, 0x00C000C0u, 0x4C004C00u));
 }
 
 // Bias of pair f (0..3) of a low-bit operand built by lowbit4_b.
