@@ -173,16 +173,17 @@ struct DecodeArgs {
 // One row of D fp32 values quantized by one wave: lane l < D/2 owns elements
 // 2l and 2l+1 (= byte l of the packed row).  Codes and scale go to the cache
 // row in global memory and to an LDS copy.
+// A wave quantizes one row: lane l < D/2 holds elements 2l, 2l + 1
 template <int D>
-__device__ __forceinline__ void quantize_row_wave(const float* __restrict__ src, int lane,
-                                                  uint8_t* gcodes, uint16_t* gscale,
+__device__ __forceinline__ float2 load_row_pair(const float* __restrict__ src, int lane) {
+  float2 v = {0.0f, 0.0f};
+  if (lane < D / 2) v = *reinterpret_cast<const float2*>(src + 2 * lane);
+  return v;
+}
+template <int D>
+__device__ __forceinline__ void quantize_row_wave(float2 v, int lane, uint8_t* gcodes, uint16_t* gscale,
                                                   uint8_t* lcodes, uint16_t* lscale) {
-  float x0 = 0.0f, x1 = 0.0f;
-  if (lane < D / 2) {
-    const float2 v = *reinterpret_cast<const float2*>(src + 2 * lane);
-    x0 = v.x;
-    x1 = v.y;
-  }
+  const float x0 = v.x, x1 = v.y;
   float m = fmaxf(fabsf(x0), fabsf(x1));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = xor_max(m, o);
@@ -228,7 +229,9 @@ struct ChunkRegs {
 // PK: the one-block kernel for at most 4 query rows per group (symmetric
 // rows), whose softmax runs on packed scores; a kernel instantiation holds
 // one softmax layout only.
-template <int D, int NB, bool PAGED, int BITS, int NGA, bool PK>
+// APP: the append-mode instantiation (a decode step that appends its new
+// K/V rows first); the plain decode's kernel carries none of that code.
+template <int D, int NB, bool PAGED, int BITS, int NGA, bool PK, bool APP>
 __global__ __launch_bounds__(64 * waves_for(NB))
 __attribute__((amdgpu_waves_per_eu(NB == 1 ? ((BITS == 3 || NGA > 0) ? 3 : 4) : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
@@ -307,7 +310,8 @@ void decode_kernel(const DecodeArgs a) {
   // At most 8 query rows otherwise: rows r < 8 are duplicated into columns
   // r + 8 of the block, whose lanes carry the low halves of hi/lo P~ chunks
   constexpr bool dup_rows = NB == 1 && !PK;   // (the launch gives this kernel at most 8 rows)
-  const bool append = a.k_new != nullptr;
+  static_assert(!APP || (BITS == 4 && NGA == 0), "append mode: 4-bit symmetric rows");
+  const bool append = APP;   // the launch picks APP = (a.k_new != nullptr)
   // rows this sequence attends, and where its new rows start (append mode)
   int pos_b = a.pos;
   int L_b = a.kv_len;
@@ -648,7 +652,20 @@ void decode_kernel(const DecodeArgs a) {
     Regs cur;
     // loads stop at the end of the split's last chunk as well: a paged split's
     // range is followed by another split's rows
-    const int t_ld = min(t_main, (c_first + (c_count - 1) * c_step + 1) * kChunk);
+    // (append mode: they stop at the first new row, so the prefetch that
+    // follows a wave's last chunk loads the cache rows of the split's first
+    // tail chunk, for the wave the plain decode gives it)
+    const int t_ld = min(append ? pos_b : t_main, (c_first + (c_count - 1) * c_step + 1) * kChunk);
+    // append mode: this wave's first quantize task (below) reads its fp32
+    // row before the chunk loads are issued, so that waiting for the row does
+    // not wait for them
+    const int ntask = (BITS == 4 && !ASYM && append) ? 2 * max(t_end - pos_b, 0) : 0;
+    auto task_src = [&](int task) {
+      const bool isv = (task & 1) != 0;
+      return (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (task >> 1)) * D;
+    };
+    float2 first_row = {0.0f, 0.0f};
+    if (kWaves - 1 - wave < ntask) first_row = load_row_pair<D>(task_src(kWaves - 1 - wave), lane);
     load_chunk(t_begin + wave * cstride, cur, t_ld, false);
 
     // ---- append mode: quantize the new rows of this split's chunks (one wave
@@ -656,13 +673,12 @@ void decode_kernel(const DecodeArgs a) {
     //      first half of the waves converts the query meanwhile), while the
     //      first chunk loads (4-bit caches only)
     if (BITS == 4 && !ASYM && append) {
-      const int ntask = 2 * max(t_end - pos_b, 0);
       for (int task = kWaves - 1 - wave; task < ntask; task += kWaves) {
         const int t = pos_b + (task >> 1);
         int k;
         if (!own_chunk(t / kChunk, &k)) continue;   // another split's chunk
         const bool isv = (task & 1) != 0;
-        const float* src = (isv ? a.v_new : a.k_new) + (((int64_t)b * a.Hkv + g) * a.n_new + (t - pos_b)) * D;
+        const float2 src = task == kWaves - 1 - wave ? first_row : load_row_pair<D>(task_src(task), lane);
         const int64_t row = row_of(t, false);
         uint8_t* gcodes = (isv ? a.vc_w : a.kc_w) + row * ROWB;
         uint16_t* gscale = (isv ? a.vs_w : a.ks_w) + row;
@@ -1274,7 +1290,8 @@ void decode_kernel(const DecodeArgs a) {
         if (!own_chunk(gc, &k) || wave != k % kWaves) continue;
         const int c0 = gc * kChunk;
         Regs cr;
-        load_chunk(c0, cr, max(pos_b, c0), true);
+        if (k == n_chunks) cr = cur;   // loaded by the wave's last prefetch
+        else load_chunk(c0, cr, max(pos_b, c0), true);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
@@ -1525,16 +1542,26 @@ void decode_kernel(const DecodeArgs a) {
   merge_splits();
 }
 
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool PK = false>
-hipError_t launch_kernel1(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool PK = false, bool APP = false>
+hipError_t launch_kernel2(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
   // this kernel the larger dynamic LDS once
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PK>),
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PK, APP>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
   if (attr != hipSuccess) return attr;
-  decode_kernel<D, NB, PAGED, BITS, NGA, PK><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  decode_kernel<D, NB, PAGED, BITS, NGA, PK, APP><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
   return hipGetLastError();
+}
+
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool PK = false>
+hipError_t launch_kernel1(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
+  if constexpr (BITS == 4 && NGA == 0) {
+    if (args.k_new != nullptr) return launch_kernel2<D, NB, PAGED, BITS, NGA, PK, true>(args, grid, lds, stream);
+  } else {
+    if (args.k_new != nullptr) return hipErrorInvalidValue;   // the API allows append on 4-bit rows only
+  }
+  return launch_kernel2<D, NB, PAGED, BITS, NGA, PK, false>(args, grid, lds, stream);
 }
 
 // symmetric rows with at most 4 query rows per group: the packed-softmax kernel
