@@ -442,7 +442,35 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
   return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
 }
 
-__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
-__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+// Partner values across lane halves (mask 32) or 16-lane rows (mask 16):
+// v_permlane32_swap / v_permlane16_swap (CDNA4) exchange them in a VALU
+// instruction, with no LDS round trip.  Given two copies of v, the swap
+// leaves one holding every lane pair's lower value and the other its upper
+// value, so combining the two gives each lane f(v[l], v[l ^ mask]) (the same
+// operands as a shuffle; max and sum are commutative).  Other masks shuffle.
+__device__ __forceinline__ void xor_pair(float v, int mask, float& lo, float& hi) {
+  if (mask == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(v), bitcast<uint32_t>(v), false, false);
+    lo = bitcast<float>((uint32_t)r[0]);
+    hi = bitcast<float>((uint32_t)r[1]);
+  } else if (mask == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(v), bitcast<uint32_t>(v), false, false);
+    lo = bitcast<float>((uint32_t)r[0]);
+    hi = bitcast<float>((uint32_t)r[1]);
+  } else {
+    lo = v;
+    hi = __shfl_xor(v, mask, 64);
+  }
+}
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  float lo, hi;
+  xor_pair(v, mask, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+  float lo, hi;
+  xor_pair(v, mask, lo, hi);
+  return lo + hi;
+}
 
 }  // namespace qkvfa
