@@ -442,12 +442,22 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
   return bitcast<float>(__builtin_amdgcn_readlane(v, 63));
 }
 
-// Partner values across lane halves (mask 32) or 16-lane rows (mask 16):
-// v_permlane32_swap / v_permlane16_swap (CDNA4) exchange them in a VALU
-// instruction, with no LDS round trip.  Given two copies of v, the swap
-// leaves one holding every lane pair's lower value and the other its upper
-// value, so combining the two gives each lane f(v[l], v[l ^ mask]) (the same
-// operands as a shuffle; max and sum are commutative).  Other masks shuffle.
+// DPP move inside 16-lane rows of the wave: lanes whose 4-lane bank is in
+// BANK (bit k: lanes 4k..4k+3 of each row) take src from the lane CTRL
+// names, the others keep old.
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp_mov(float old, float src) {
+  return bitcast<float>(__builtin_amdgcn_update_dpp(bitcast<int>(old), bitcast<int>(src), CTRL, 0xF, BANK, false));
+}
+
+// Partner values v[l ^ mask] without an LDS round trip.  Across lane halves
+// (mask 32) or 16-lane rows (mask 16): v_permlane32_swap / v_permlane16_swap
+// (CDNA4) exchange them in one VALU instruction -- given two copies of v, the
+// swap leaves one holding every lane pair's lower value and the other its
+// upper value, so each lane gets the pair (v[l], v[l ^ mask]) in some order
+// (max and sum are commutative, so the result equals a shuffle's).  Inside a
+// row: DPP quad permutations (masks 1, 2), a rotation by 8 (mask 8), and two
+// bank-masked row shifts by 4 (mask 4).
 __device__ __forceinline__ void xor_pair(float v, int mask, float& lo, float& hi) {
   if (mask == 32) {
     const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(v), bitcast<uint32_t>(v), false, false);
@@ -457,6 +467,18 @@ __device__ __forceinline__ void xor_pair(float v, int mask, float& lo, float& hi
     const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(v), bitcast<uint32_t>(v), false, false);
     lo = bitcast<float>((uint32_t)r[0]);
     hi = bitcast<float>((uint32_t)r[1]);
+  } else if (mask == 8) {
+    lo = v;
+    hi = dpp_mov<0x128, 0xF>(v, v);                        // row_ror:8
+  } else if (mask == 4) {
+    lo = v;
+    hi = dpp_mov<0x114, 0xA>(dpp_mov<0x104, 0x5>(v, v), v);   // row_shl:4 on banks 0, 2; row_shr:4 on 1, 3
+  } else if (mask == 2) {
+    lo = v;
+    hi = dpp_mov<0x4E, 0xF>(v, v);                         // quad_perm [2, 3, 0, 1]
+  } else if (mask == 1) {
+    lo = v;
+    hi = dpp_mov<0xB1, 0xF>(v, v);                         // quad_perm [1, 0, 3, 2]
   } else {
     lo = v;
     hi = __shfl_xor(v, mask, 64);
