@@ -768,6 +768,96 @@ def summarize_profiles(root: str):
     print(json.dumps(result, indent=1))
 
 
+def phase_table(torch, qkv, w, launches=10):
+    """Per-workgroup phase timestamps of one decode step launch (append 1
+    token + decode), from the measurement build libqkvfa_trace.so (the same
+    kernels plus s_memrealtime stores).  The step is launched `launches`
+    times back to back behind a GPU hold over rotated cache copies; the
+    timestamps of the last launch are read back.  Returns the table rows
+    (phase, min / median / max over workgroups in microseconds from the
+    launch's first workgroup entry) and per-phase durations."""
+    import ctypes
+    path = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa_trace.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with `python quantized_kv_flashattention_amd/build.py`")
+    qkv._LIB_PATH = path
+    qkv._lib = qkv._load()
+    qkv._lib.qkv_trace_read.restype = ctypes.c_int
+    qkv._lib.qkv_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    from qkv_inputs import make_qkv
+    q_bits, k, v = make_qkv(w)
+    kv_bytes, _ = decode_bytes(w)
+    n_copies = max(4, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    caches = upload_cache(torch, qkv, k, v, n_copies)
+    k_new = torch.from_numpy(k[:, :, -1:].copy()).cuda()
+    v_new = torch.from_numpy(v[:, :, -1:].copy()).cuda()
+    del k, v
+    q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    ns = qkv.decode_auto_splits(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D)
+    ws = torch.zeros(max(qkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.L, w.D), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        qkv.decode_append(q, k_new, v_new, caches[i % n_copies], w.L - 1, softmax_scale=w.softmax_scale, out=out,
+                          workspace=ws)
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    avg_ms = region_ms(torch, step, launches, n_copies)
+    n_wg = ns * w.B * w.Hkv
+    buf = np.zeros((n_wg, 16), dtype=np.uint64)
+    rc = qkv._lib.qkv_trace_read(buf.ctypes.data, n_wg)
+    if rc != 0:
+        raise RuntimeError(f"qkv_trace_read failed ({rc})")
+    t = buf.astype(np.float64) / 100.0          # s_memrealtime: 100 MHz -> microseconds
+    t0 = t[:, 0].min()
+    merged = buf[:, 13] == 1
+    loop_end = t[:, 2:10].max(axis=1)
+    cols = {"entry": t[:, 0], "chunk loop start": t[:, 1], "first wave done": t[:, 2:10].min(axis=1),
+            "last wave done": loop_end, "wave merge + partial written": t[:, 10],
+            "ticket drawn": t[:, 11], "exit (non-merging)": t[:, 12][~merged],
+            "exit (merging)": t[:, 12][merged]}
+    rows = []
+    for name, x in cols.items():
+        x = x - t0
+        rows.append({"phase": name, "n": int(x.size), "min_us": round(float(x.min()), 2),
+                     "median_us": round(float(np.median(x)), 2), "max_us": round(float(x.max()), 2)})
+    dur = {
+        "launch (first entry to last exit)": float(t[:, 12].max() - t0),
+        "loop, per workgroup (start to last wave)": float(np.median(loop_end - t[:, 1])),
+        "wave spread inside a workgroup (last - first wave done)": float(np.median(loop_end - t[:, 2:10].min(axis=1))),
+        "wave merge + partial (last wave done to written)": float(np.median(t[:, 10] - loop_end)),
+        "store wait + ticket (written to ticket)": float(np.median(t[:, 11] - t[:, 10])),
+        "split merge (ticket to exit, merging workgroups)": float(np.median((t[:, 12] - t[:, 11])[merged])),
+        "last loop end to last exit": float(t[:, 12].max() - loop_end.max()),
+    }
+    res = {"workload": w.name, "n_split": ns, "workgroups": n_wg, "launches": launches,
+           "avg_launch_ms_trace_build": avg_ms, "rows": rows,
+           "durations_us": {k: round(v, 2) for k, v in dur.items()}}
+    qkv._LIB_PATH = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")
+    qkv._lib = qkv._load()
+    return res
+
+
+def print_phase_table(res):
+    print(f"workload {res['workload']}: {res['workgroups']} workgroups ({res['n_split']} splits), "
+          f"last of {res['launches']} back-to-back launches; trace build {res['avg_launch_ms_trace_build'] * 1e3:.2f} "
+          f"us per launch")
+    print()
+    print("| phase (us from the first workgroup's entry) | workgroups | min | median | max |")
+    print("|---|---|---|---|---|")
+    for r in res["rows"]:
+        print(f"| {r['phase']} | {r['n']} | {r['min_us']:.2f} | {r['median_us']:.2f} | {r['max_us']:.2f} |")
+    print()
+    print("| duration | us |")
+    print("|---|---|")
+    for k, v in res["durations_us"].items():
+        print(f"| {k} | {v:.2f} |")
+    print()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -779,7 +869,20 @@ def main():
                     help="run one kernel repeatedly for rocprofv3 counter passes, print nothing")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")
+    ap.add_argument("--phase-table", action="store_true",
+                    help="print per-workgroup phase timestamps of the Llama-3-8B decode step "
+                         "(measurement build libqkvfa_trace.so) as markdown tables, then a JSON line")
     args = ap.parse_args()
+    if args.phase_table:
+        import torch
+        import quantized_kv_flashattention_amd as qkv
+        from qkv_inputs import workload
+        torch.cuda.set_device(0)
+        res = [phase_table(torch, qkv, workload("llama3_8b_decode"))]
+        for r in res:
+            print_phase_table(r)
+        print(json.dumps(res), flush=True)
+        return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
         return

@@ -20,6 +20,8 @@ SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "prefill.hip", "prefill_shor
 # measurement helper (achievable-HBM streaming read), a library of its own
 BENCH_LIB_PATH = os.path.join(PKG_DIR, "libqkvfa_bench.so")
 BENCH_SOURCES = ["bench_read.hip"]
+# measurement build: the same sources with decode phase timestamps
+TRACE_LIB_PATH = os.path.join(PKG_DIR, "libqkvfa_trace.so")
 
 # No fast-math: the quantizer needs IEEE fp32 division and round-half-even.
 # Packed fp32 VALU ops are disabled (-packed-fp32-ops) for every device file.
@@ -46,9 +48,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _link(sources, path, verbose):
+def _link(sources, path, verbose, extra=()):
     tmp = path + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -61,13 +63,16 @@ def _link(sources, path, verbose):
     os.replace(tmp, path)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile ``libqkvfa.so`` (and the measurement helper ``libqkvfa_bench.so``)
-    next to this file; return the path of ``libqkvfa.so``."""
+def build(verbose: bool = False, trace: bool = True) -> str:
+    """Compile ``libqkvfa.so`` and the measurement libraries (``libqkvfa_bench.so``,
+    and unless ``trace`` is false ``libqkvfa_trace.so``) next to this file;
+    return the path of ``libqkvfa.so``."""
     _link(SOURCES, LIB_PATH, verbose)
     _link(BENCH_SOURCES, BENCH_LIB_PATH, verbose)
+    if trace:
+        _link(SOURCES, TRACE_LIB_PATH, verbose, extra=["-DQKVFA_PHASE_TRACE"])
     return LIB_PATH
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--no-trace" not in sys.argv))

@@ -1,6 +1,9 @@
 // C ABI of libqkvfa: argument validation, split planning and kernel launch.
 // Every check happens before anything is enqueued; no exception leaves here.
 #include "qkvfa.h"
+#ifdef QKVFA_PHASE_TRACE
+#include "qkvfa_trace.h"
+#endif
 
 #include <hip/hip_runtime.h>
 
@@ -616,5 +619,14 @@ qkv_status qkv_prefill_asym(const uint16_t* q, const uint8_t* k_codes, const uin
                         reinterpret_cast<const uint16_t*>(v_params), B, Hq, Hkv, Sq, kv_len, C, D, softmax_scale,
                         causal, out, lse, stream, 4, "qkv_prefill_asym", group);
 }
+
+#ifdef QKVFA_PHASE_TRACE
+qkv_status qkv_trace_read(uint64_t* dst, int64_t n_wgs) {
+  if (!dst || n_wgs < 0) return fail(QKV_ERR_INVALID_ARG, "qkv_trace_read: null destination or negative count");
+  const hipError_t e = qkvfa::trace_read(dst, n_wgs);
+  if (e != hipSuccess) return fail(QKV_ERR_HIP, std::string("qkv_trace_read: ") + hipGetErrorString(e));
+  return QKV_OK;
+}
+#endif
 
 }  // extern "C"

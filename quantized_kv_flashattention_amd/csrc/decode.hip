@@ -170,6 +170,48 @@ struct DecodeArgs {
   float qk_log2;
 };
 
+// Phase timestamps (measurement build only, QKVFA_PHASE_TRACE): workgroup
+// w < kTraceWgs of a launch writes s_memrealtime values (100 MHz) to
+// g_trace[w][slot]: 0 entry, 1 chunk loop start, 2 + wave: that wave's last
+// chunk done, 10 wave merge and partial written, 11 ticket drawn, 12 exit,
+// 13 whether the workgroup merged the splits (0/1).  Each launch rewrites
+// every slot it reaches (held in LDS, written out at exit); qkv_trace_read
+// copies them to the host.
+constexpr int kTraceWgs = 4096;
+constexpr int kTraceSlots = 16;
+#ifdef QKVFA_PHASE_TRACE
+__device__ uint64_t g_trace[kTraceWgs * kTraceSlots];
+// stamps go to an LDS copy (an immediate LDS address: no registers kept live
+// across the kernel for them); thread 0 writes the copy out as it exits
+#define QKVFA_TRACE_LDS __shared__ uint64_t s_trace[kTraceSlots];
+#define QKVFA_STAMP(slot, cond) \
+  do {                          \
+    if (cond) s_trace[(slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define QKVFA_TRACE_PUT(slot, cond, v) \
+  do {                                 \
+    if (cond) s_trace[(slot)] = (v);   \
+  } while (0)
+#define QKVFA_TRACE_FLUSH()                                                                   \
+  do {                                                                                        \
+    if (threadIdx.x == 0 && blockIdx.x < (uint32_t)kTraceWgs) {                               \
+      s_trace[12] = __builtin_amdgcn_s_memrealtime();                                         \
+      for (int i_ = 0; i_ < kTraceSlots; ++i_) g_trace[blockIdx.x * kTraceSlots + i_] = s_trace[i_]; \
+    }                                                                                         \
+  } while (0)
+#else
+#define QKVFA_TRACE_LDS
+#define QKVFA_STAMP(slot, cond) \
+  do {                          \
+  } while (0)
+#define QKVFA_TRACE_PUT(slot, cond, v) \
+  do {                                 \
+  } while (0)
+#define QKVFA_TRACE_FLUSH() \
+  do {                      \
+  } while (0)
+#endif
+
 // One row of D fp32 values quantized by one wave: lane l < D/2 owns elements
 // 2l and 2l+1 (= byte l of the packed row).  Codes and scale go to the cache
 // row in global memory and to an LDS copy.
@@ -284,7 +326,9 @@ void decode_kernel(const DecodeArgs a) {
   // paged cache: the page ids of this split's tokens (from page t_begin / P on)
   __shared__ int s_pid[PAGED ? kMaxSplitPages : 1];
 
+  QKVFA_TRACE_LDS
   const int lane = threadIdx.x & 63;
+  QKVFA_STAMP(0, threadIdx.x == 0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int j = lane >> 4;
@@ -420,7 +464,12 @@ void decode_kernel(const DecodeArgs a) {
       s_last = (prev == (uint32_t)(a.n_split - 1));
     }
     __syncthreads();
-    if (!s_last) return;
+    QKVFA_STAMP(11, threadIdx.x == 0);
+    QKVFA_TRACE_PUT(13, threadIdx.x == 0, (uint64_t)(s_last ? 1 : 0));
+    if (!s_last) {
+      QKVFA_TRACE_FLUSH();
+      return;
+    }
     const int n_split = a.n_split;
     // splits that start before this sequence's length; the rest attended nothing
     const int n_live = a.tail_rows > 0 ? n_split : n_used;
@@ -565,6 +614,7 @@ void decode_kernel(const DecodeArgs a) {
     if (n_live <= 4) merge_with(IntTag<4>{});
     else merge_with(IntTag<16>{});
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    QKVFA_TRACE_FLUSH();
   };
 
   // The chunk loop, the wave merge and the partial (or direct) output of a
@@ -1248,6 +1298,7 @@ void decode_kernel(const DecodeArgs a) {
         process_chunk(c0, cr, lim);
     };
 
+    QKVFA_STAMP(1, threadIdx.x == 0);
     if constexpr (kTwoSets) {
       // Two register sets in fixed roles, two chunks per trip: no copy of the
       // prefetched set at the back edge (a copy is one VALU move per register
@@ -1314,6 +1365,7 @@ void decode_kernel(const DecodeArgs a) {
       }
     }
 
+    QKVFA_STAMP(2 + wave, lane == 0);
     // ---- merge the eight waves through LDS, one 16-row block at a time
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -1538,7 +1590,11 @@ void decode_kernel(const DecodeArgs a) {
   } else {
     main_body();
   }
-  if (direct) return;
+  QKVFA_STAMP(10, threadIdx.x == 0);
+  if (direct) {
+    QKVFA_TRACE_FLUSH();
+    return;
+  }
   merge_splits();
 }
 
@@ -1766,5 +1822,13 @@ hipError_t decode_scratch(void** ptr, hipStream_t stream) {
   *ptr = g_scratch[dev];
   return hipSuccess;
 }
+
+#ifdef QKVFA_PHASE_TRACE
+hipError_t trace_read(uint64_t* dst, int64_t n_wgs) {
+  if (n_wgs < 0 || n_wgs > kTraceWgs) return hipErrorInvalidValue;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_trace), (size_t)n_wgs * kTraceSlots * sizeof(uint64_t), 0,
+                             hipMemcpyDeviceToHost);
+}
+#endif
 
 }  // namespace qkvfa

@@ -102,6 +102,12 @@ constexpr size_t kScratchTicketBytes = (size_t)kScratchTickets * 4;
 constexpr size_t kScratchBytes = (size_t)16 << 20;
 hipError_t decode_scratch(void** ptr, hipStream_t stream);
 
+#ifdef QKVFA_PHASE_TRACE
+// Measurement build: copy the decode phase timestamps of workgroups
+// [0, n_wgs) of the last launch (16 uint64 each) to host memory.
+hipError_t trace_read(uint64_t* dst, int64_t n_wgs);
+#endif
+
 // Quantize-append of asymmetric group-wise 4-bit K and V rows (codes and
 // parameter words as in DecodeAsym) into cache rows [pos, pos + T).
 hipError_t launch_quantize_append_asym(const float* src, uint8_t* codes, uint32_t* params,

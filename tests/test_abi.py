@@ -435,3 +435,27 @@ def test_bench_helper_exports_and_argument_errors():
     assert f(P + 4, 16, P, 1, None) == 1      # misaligned
     assert f(P, 16, P, 0, None) == 1
     assert f(P, 16, None, 1, None) == 1
+
+
+TRACE_HEADER = os.path.join(ROOT, "include", "qkvfa_trace.h")
+TRACE_LIB = os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa_trace.so")
+
+
+def test_trace_build_exports_the_abi_and_its_reader():
+    """The measurement build (decode phase timestamps) exports every call of
+    qkvfa.h and qkv_trace_read; bad arguments fail before any device work."""
+    if not os.path.exists(TRACE_LIB):
+        pytest.skip("libqkvfa_trace.so not built")
+    tl = ctypes.CDLL(TRACE_LIB)
+    for n in declared_functions():
+        assert hasattr(tl, n), n
+    text = re.sub(r"/\*.*?\*/", "", open(TRACE_HEADER).read(), flags=re.S)
+    assert re.findall(r"\b(qkv_[a-z_0-9]+)\s*\(", text) == ["qkv_trace_read"]
+    tl.qkv_trace_read.restype = ctypes.c_int
+    tl.qkv_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    assert tl.qkv_trace_read(None, 4) == 1                     # QKV_ERR_INVALID_ARG
+    buf = (ctypes.c_uint64 * 16)()
+    assert tl.qkv_trace_read(ctypes.addressof(buf), -1) == 1
+    # the plain library has no trace reader
+    assert not hasattr(ctypes.CDLL(os.path.join(ROOT, "quantized_kv_flashattention_amd", "libqkvfa.so")),
+                       "qkv_trace_read")
