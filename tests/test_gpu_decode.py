@@ -9,6 +9,7 @@ import torch
 
 import oracle
 import quantized_kv_flashattention_amd as qkv
+from qkv_inputs import f32_to_bf16_bits
 from gpu_helpers import (DEV, MAX_ABS_TOL, MEAN_ABS_TOL, assert_close, cache_to_dev, compare,
                          full_workload, q_to_dev, random_case)
 
@@ -175,6 +176,9 @@ APPEND_CASES = [
     (3, 12, 4, 1, 2049, 2, 2100, 128, 0),   # two new rows, one query row
     (1, 8, 2, 1, 100, 64, 200, 64, 2),      # new rows in chunks 3, 4, 5: splits 1, 0, 1
     (2, 8, 2, 2, 60, 40, 128, 128, 3),      # new rows in chunks 1, 2, 3: splits 1, 2, 0
+    (2, 6, 3, 1, 1499, 1, 1600, 128, 0),    # 2 rows per group (packed softmax), D 128
+    (2, 3, 1, 1, 700, 2, 720, 64, 3),       # 3 rows per group (packed softmax), D 64
+    (1, 2, 2, 2, 257, 3, 300, 64, 0),       # 2 rows per group from 2 query positions
 ]
 
 
@@ -251,4 +255,36 @@ def test_row_counts_around_packed_softmax(Hq, Hkv, Sq, ns):
     out, lse = _run(q, (kc, ks, vc, vs), L, scale, ns)
     ro, rl = oracle.attention(q, kc, ks, vc, vs, L, scale)
     assert_close(out, ro, f"Hq={Hq} Hkv={Hkv} Sq={Sq} ns={ns}")
+    assert compare(lse, rl)[0] < 1e-3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("Hq,Hkv,Sq", [(2, 1, 1), (6, 2, 1), (1, 1, 2), (1, 1, 3)])
+def test_packed_softmax_across_widths(D, bits, Hq, Hkv, Sq):
+    """Groups of 2 and 3 query rows (the packed softmax's partly filled lane
+    groups) at both head dims and every code width, with outlier channels in
+    K and V, against the oracle (b-bit caches: the oracle's b-bit attention)."""
+    B, L, C = 2, 1100, 1130
+    seed = 31 * D + 7 * bits + 3 * Hq + Hkv + Sq
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    if bits == 4:
+        q, kc, ks, vc, vs = random_case(seed, B, Hq, Hkv, Sq, L, D, C, outliers=True)
+        out, lse = _run(q, (kc, ks, vc, vs), L, scale)
+        ro, rl = oracle.attention(q, kc, ks, vc, vs, L, scale)
+    else:
+        rng = np.random.default_rng(seed)
+        q = f32_to_bf16_bits(rng.standard_normal((B, Hq, Sq, D)).astype(np.float32))
+        arrs = []
+        for f in (1.0, 1.5):
+            x = (rng.standard_normal((B, Hkv, C, D)) * f).astype(np.float32)
+            x[:, :, :, rng.choice(D, size=2, replace=False)] *= 8.0     # outlier channels
+            arrs += list(oracle.quantize_rows_bits(x, bits))
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        h = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(DEV)
+        cache = qkv.KVCache(t(arrs[0]), h(arrs[1]), t(arrs[2]), h(arrs[3]))
+        out, lse = qkv.decode(q_to_dev(q), cache, L, softmax_scale=scale, return_lse=True, bits=bits)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention_bits(q, *arrs, L, scale, bits)
+    assert_close(out, ro, f"D={D} bits={bits} rows={Hq // Hkv * Sq}")
     assert compare(lse, rl)[0] < 1e-3

@@ -144,6 +144,8 @@ CASES = [
     (3, 8, 2, 1, (0, 0, 40), 64, 32, 2, 5),                  # appends into empty sequences
     (2, 8, 8, 1, (20000, 17), 64, 32, 0, 1),                 # one split over 625 pages
     (4, 8, 2, 1, (50, 700, 2500, 9000), 128, 64, 1, 40),    # 2, 22, 40, 40 live splits: both merge forms
+    (3, 6, 2, 1, (700, 1500, 33), 128, 64, 1, 0),            # 3 rows per group (packed softmax)
+    (2, 4, 2, 1, (2000, 5), 64, 32, 1, 3),                   # 2 rows per group (packed softmax)
 ]
 
 
