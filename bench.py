@@ -680,6 +680,23 @@ def profile_target(target: str, iters: int):
                              softmax_scale=w.softmax_scale, out=out)
         torch.cuda.synchronize()
         return
+    if target == "lowbit":
+        # decode only over 4-, 3- and 2-bit caches of the Llama-3-8B shape
+        # (one kernel instantiation per width)
+        w = workload("llama3_8b_decode")
+        q_bits, k, v = make_qkv(w)
+        q = torch.from_numpy(q_bits.view("int16")).cuda().view(torch.bfloat16)
+        out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.float32, device="cuda")
+        kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        del k, v
+        for bits in (4, 3, 2):
+            c = qkv.KVCache.empty(w.B, w.Hkv, w.L, w.D, bits=bits)
+            qkv.quantize_append_kv(kt, vt, c, 0, bits=bits)
+            for _ in range(iters):
+                qkv.decode(q, c, w.L, softmax_scale=w.softmax_scale, out=out, bits=bits)
+            torch.cuda.synchronize()
+            del c
+        return
     if target == "vit":
         w = workload("vit_b_selfattn")
         q_bits, k, v = make_qkv(w)
@@ -865,7 +882,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["all", "headline", "decode", "prefill"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--profile-target", choices=["decode", "long", "paged", "prefill", "vit", "copy"], default=None,
+    ap.add_argument("--profile-target", choices=["decode", "long", "paged", "prefill", "vit", "copy", "lowbit"],
+                    default=None,
                     help="run one kernel repeatedly for rocprofv3 counter passes, print nothing")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")
