@@ -702,10 +702,7 @@ void decode_kernel(const DecodeArgs a) {
     Regs cur;
     // loads stop at the end of the split's last chunk as well: a paged split's
     // range is followed by another split's rows
-    // (append mode: they stop at the first new row, so the prefetch that
-    // follows a wave's last chunk loads the cache rows of the split's first
-    // tail chunk, for the wave the plain decode gives it)
-    const int t_ld = min(append ? pos_b : t_main, (c_first + (c_count - 1) * c_step + 1) * kChunk);
+    const int t_ld = min(t_main, (c_first + (c_count - 1) * c_step + 1) * kChunk);
     // append mode: this wave's first quantize task (below) reads its fp32
     // row before the chunk loads are issued, so that waiting for the row does
     // not wait for them
@@ -1341,8 +1338,7 @@ void decode_kernel(const DecodeArgs a) {
         if (!own_chunk(gc, &k) || wave != k % kWaves) continue;
         const int c0 = gc * kChunk;
         Regs cr;
-        if (k == n_chunks) cr = cur;   // loaded by the wave's last prefetch
-        else load_chunk(c0, cr, max(pos_b, c0), true);
+        load_chunk(c0, cr, max(pos_b, c0), true);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int tk = c0 + 8 * (r >> 2) + 4 * kb + (r & 3);
