@@ -888,7 +888,7 @@ def main():
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE passes in DIR")
     ap.add_argument("--phase-table", action="store_true",
-                    help="print per-workgroup phase timestamps of the Llama-3-8B decode step "
+                    help="print per-workgroup phase timestamps of the Llama-3-8B and 128K decode steps "
                          "(measurement build libqkvfa_trace.so) as markdown tables, then a JSON line")
     args = ap.parse_args()
     if args.phase_table:
@@ -896,7 +896,7 @@ def main():
         import quantized_kv_flashattention_amd as qkv
         from qkv_inputs import workload
         torch.cuda.set_device(0)
-        res = [phase_table(torch, qkv, workload("llama3_8b_decode"))]
+        res = [phase_table(torch, qkv, workload(n)) for n in ("llama3_8b_decode", "long_context_decode")]
         for r in res:
             print_phase_table(r)
         print(json.dumps(res), flush=True)
