@@ -268,12 +268,13 @@ struct ChunkRegs {
 // skips the one-chunk prefetch to stay within 256 VGPRs.
 // (3-bit rows keep a second set of top-bit registers per chunk: their one
 // row-block variant asks for three waves per SIMD instead of four.)
-// PK: the one-block kernel for at most 4 query rows per group (symmetric
-// rows), whose softmax runs on packed scores; a kernel instantiation holds
-// one softmax layout only.
+// PKR: the one-block kernel for at most 4 (PKR = 4) or at most 8 (PKR = 8)
+// query rows per group (symmetric rows), whose softmax runs on packed
+// scores; 0: the unpacked softmax.  A kernel instantiation holds one
+// softmax layout only.
 // APP: the append-mode instantiation (a decode step that appends its new
 // K/V rows first); the plain decode's kernel carries none of that code.
-template <int D, int NB, bool PAGED, int BITS, int NGA, bool PK, bool APP>
+template <int D, int NB, bool PAGED, int BITS, int NGA, int PKR, bool APP>
 __global__ __launch_bounds__(64 * waves_for(NB))
 __attribute__((amdgpu_waves_per_eu(NB == 1 ? ((BITS == 3 || NGA > 0) ? 3 : 4) : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
@@ -350,10 +351,12 @@ void decode_kernel(const DecodeArgs a) {
   const int rows_o = min(16, R);   // rows per wave in the merge buffer
   // At most 4 query rows in the one 16-row block: the softmax runs on packed
   // scores (2 per lane instead of 8, the other 48 lanes' rows being padding)
-  static_assert(!PK || (NB == 1 && !ASYM), "packed softmax: one row block, symmetric rows");
+  constexpr bool PK = PKR == 4;    // packed, at most 4 rows: row b's low halves in column 4 + b
+  constexpr bool PK8 = PKR == 8;   // packed, at most 8 rows: row b's low halves in column 8 + b
+  static_assert(PKR == 0 || (NB == 1 && !ASYM), "packed softmax: one row block, symmetric rows");
   // At most 8 query rows otherwise: rows r < 8 are duplicated into columns
   // r + 8 of the block, whose lanes carry the low halves of hi/lo P~ chunks
-  constexpr bool dup_rows = NB == 1 && !PK;   // (the launch gives this kernel at most 8 rows)
+  constexpr bool dup_rows = NB == 1 && !PK && !PK8;   // (the launch gives this kernel at most 8 rows)
   static_assert(!APP || (BITS == 4 && NGA == 0), "append mode: 4-bit symmetric rows");
   const bool append = APP;   // the launch picks APP = (a.k_new != nullptr)
   // rows this sequence attends, and where its new rows start (append mode)
@@ -1033,6 +1036,75 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int p = 0; p < NPB; ++p) o_acc[0][p] *= alpha;
           }
+        } else if constexpr (PK8) {
+          // Packed, at most 8 rows: lane (j, 8a + b) takes slots 4a .. 4a + 3
+          // (tokens 8j + 4a .. 8j + 4a + 3) of row b; lanes (j, 8 + b) get
+          // slots 4-7 of lane (j, b) with one row shift per value.  Row maxima
+          // reduce over a with a row rotation by 8.  P~ returns to the
+          // B-operand layout of lanes (j, b) with row shifts the other way;
+          // lanes (j, 8 + b) then feed the low halves of hi/lo chunks
+          // (column 8 + b, added to row b in the wave merge), else zeros.
+          const bool upper = r >= 8;   // a = 1
+          const int e0 = 8 * j + (upper ? 4 : 0);
+          const float4v c4 = *reinterpret_cast<const float4v*>(&s_sc[wave][e0]);
+          const float4v v4 = *reinterpret_cast<const float4v*>(&s_sc[wave][32 + e0]);
+          const float4v m4 = *reinterpret_cast<const float4v*>(&s_sc[wave][64 + e0]);
+          float x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = dpp_f<0x118, 0xC>(s_t[0][0][i], s_t[0][1][i]);   // row_shr:8 on lanes 8-15
+            x[i] = fmaf(y, c4[i], m4[i]);
+          }
+          float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+          mloc = fmaxf(mloc, dpp_f<0x128>(mloc, mloc));
+          mloc = xor_max(mloc, 16);
+          mloc = xor_max(mloc, 32);
+          const float m_new = fmaxf(m_run[0], mloc);   // finite: every chunk has a valid token
+          const float alpha = fast_exp2(m_run[0] - m_new);
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_new);
+          half2v q01 = cvt_pk_f16(p[0] * v4[0], p[1] * v4[1]);
+          half2v q23 = cvt_pk_f16(p[2] * v4[2], p[3] * v4[3]);
+          if (hilo) {   // the low halves below are taken about exactly these values
+            pin_v(q01);
+            pin_v(q23);
+          }
+          const float h01 = bitcast<float>(q01), h23 = bitcast<float>(q23);
+          // lanes 0-7: own slots 0-3, slots 4-7 from lane + 8 (row_shl:8)
+          float pw[4] = {h01, h23, dpp_f<0x108, 0x3>(h01, h01), dpp_f<0x108, 0x3>(h23, h23)};
+          // s_run: the P~ values this lane computed (high halves, and low
+          // halves below), whichever lane feeds them to the products; the
+          // wave merge sums the two lanes of a row
+          float ps = __builtin_amdgcn_fdot2(q01, half2v{1, 1}, s_run[0] * alpha, false);
+          ps = __builtin_amdgcn_fdot2(q23, half2v{1, 1}, ps, false);
+          if (upper) pw[0] = pw[1] = pw[2] = pw[3] = 0.0f;   // its high halves went to lanes 0-7
+          if (hilo) {   // low halves P~_lo = fp16(p s_V - P~) (residuals exact in fp32)
+            asm volatile("");   // a real branch: not speculated into every chunk
+            const half2v lo01 = {pv_lo(p[0], v4[0], q01[0]), pv_lo(p[1], v4[1], q01[1])};
+            const half2v lo23 = {pv_lo(p[2], v4[2], q23[0]), pv_lo(p[3], v4[3], q23[1])};
+            ps = __builtin_amdgcn_fdot2(lo01, half2v{1, 1}, ps, false);
+            ps = __builtin_amdgcn_fdot2(lo23, half2v{1, 1}, ps, false);
+            const float l01 = bitcast<float>(lo01), l23 = bitcast<float>(lo23);
+            // lanes 8-15: slots 0-3 from lane - 8 (row_shr:8), own slots 4-7
+            const float s01 = dpp_f<0x118, 0xC>(0.0f, l01), s23 = dpp_f<0x118, 0xC>(0.0f, l23);
+            if (upper) {
+              pw[0] = s01;
+              pw[1] = s23;
+              pw[2] = l01;
+              pw[3] = l23;
+            }
+          }
+          const uint4v pu = {bitcast<uint32_t>(pw[0]), bitcast<uint32_t>(pw[1]), bitcast<uint32_t>(pw[2]),
+                             bitcast<uint32_t>(pw[3])};
+          pop[0] = bitcast<half8v>(pu);
+          s_run[0] = ps;
+          l_run[0] = l_run[0] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+          m_run[0] = m_new;
+          if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int q = 0; q < NPB; ++q) o_acc[0][q] *= alpha;
+          }
         } else {
           // lanes of duplicated rows (columns r + 8 of a block of at most 8
           // rows): the low halves of P~ in hi/lo chunks, 0 in the others
@@ -1371,6 +1443,10 @@ void decode_kernel(const DecodeArgs a) {
         s_run[0] += dpp_f<0x124>(s_run[0], s_run[0]);
         s_run[0] += dpp_f<0x128>(s_run[0], s_run[0]);
       }
+      if constexpr (PK8) {   // the two lanes (j, b), (j, 8 + b) of a row
+        l_run[0] += dpp_f<0x128>(l_run[0], l_run[0]);
+        s_run[0] += dpp_f<0x128>(s_run[0], s_run[0]);
+      }
       float l = xor_sum(l_run[nb], 16);
       l = xor_sum(l, 32);
       if constexpr (ASYM) {
@@ -1387,6 +1463,12 @@ void decode_kernel(const DecodeArgs a) {
           for (int p = 0; p < NPB; ++p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) o_acc[0][p][i] += dpp_f<0x104>(0.0f, o_acc[0][p][i]);
+        }
+        if constexpr (PK8) {   // low-half columns 8 + b (zero unless a chunk was hi/lo) into row b
+#pragma unroll
+          for (int p = 0; p < NPB; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o_acc[0][p][i] += dpp_f<0x108>(0.0f, o_acc[0][p][i]);
         }
         float sp = xor_sum(s_run[nb], 16);
         sp = xor_sum(sp, 32);
@@ -1594,35 +1676,38 @@ void decode_kernel(const DecodeArgs a) {
   merge_splits();
 }
 
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool PK = false, bool APP = false>
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, int PKR = 0, bool APP = false>
 hipError_t launch_kernel2(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
   // this kernel the larger dynamic LDS once
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PK, APP>),
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PKR, APP>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
   if (attr != hipSuccess) return attr;
-  decode_kernel<D, NB, PAGED, BITS, NGA, PK, APP><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  decode_kernel<D, NB, PAGED, BITS, NGA, PKR, APP><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
   return hipGetLastError();
 }
 
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool PK = false>
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, int PKR = 0>
 hipError_t launch_kernel1(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   if constexpr (BITS == 4 && NGA == 0) {
-    if (args.k_new != nullptr) return launch_kernel2<D, NB, PAGED, BITS, NGA, PK, true>(args, grid, lds, stream);
+    if (args.k_new != nullptr) return launch_kernel2<D, NB, PAGED, BITS, NGA, PKR, true>(args, grid, lds, stream);
   } else {
     if (args.k_new != nullptr) return hipErrorInvalidValue;   // the API allows append on 4-bit rows only
   }
-  return launch_kernel2<D, NB, PAGED, BITS, NGA, PK, false>(args, grid, lds, stream);
+  return launch_kernel2<D, NB, PAGED, BITS, NGA, PKR, false>(args, grid, lds, stream);
 }
 
-// symmetric rows with at most 4 query rows per group: the packed-softmax kernel
+// symmetric rows with at most 4 or at most 8 query rows per group: the
+// packed-softmax kernels
 template <int D, int NB, bool PAGED, int BITS, int NGA = 0>
 hipError_t launch_kernel(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   if constexpr (NB == 1 && NGA == 0) {
-    if (args.G * args.Sq <= 4) return launch_kernel1<D, NB, PAGED, BITS, NGA, true>(args, grid, lds, stream);
+    if (args.G * args.Sq <= 4) return launch_kernel1<D, NB, PAGED, BITS, NGA, 4>(args, grid, lds, stream);
+    return launch_kernel1<D, NB, PAGED, BITS, NGA, 8>(args, grid, lds, stream);
+  } else {
+    return launch_kernel1<D, NB, PAGED, BITS, NGA, 0>(args, grid, lds, stream);
   }
-  return launch_kernel1<D, NB, PAGED, BITS, NGA, false>(args, grid, lds, stream);
 }
 
 template <int D, int NB>
