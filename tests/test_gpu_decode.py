@@ -260,11 +260,13 @@ def test_row_counts_around_packed_softmax(Hq, Hkv, Sq, ns):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("Hq,Hkv,Sq", [(2, 1, 1), (6, 2, 1), (1, 1, 2), (1, 1, 3)])
+@pytest.mark.parametrize("Hq,Hkv,Sq", [(2, 1, 1), (6, 2, 1), (1, 1, 2), (1, 1, 3),
+                                        (5, 1, 1), (3, 1, 2), (7, 1, 1), (8, 1, 1)])
 def test_packed_softmax_across_widths(D, bits, Hq, Hkv, Sq):
-    """Groups of 2 and 3 query rows (the packed softmax's partly filled lane
-    groups) at both head dims and every code width, with outlier channels in
-    K and V, against the oracle (b-bit caches: the oracle's b-bit attention)."""
+    """Groups of 2, 3 (the 4-row packed softmax's partly filled lane groups)
+    and 5-8 query rows (the 8-row packed form) at both head dims and every
+    code width, with outlier channels in K and V, against the oracle (b-bit
+    caches: the oracle's b-bit attention)."""
     B, L, C = 2, 1100, 1130
     seed = 31 * D + 7 * bits + 3 * Hq + Hkv + Sq
     scale = float(np.float32(1.0 / np.sqrt(D)))
