@@ -1,8 +1,8 @@
 """GPU parity of the short-sequence prefill (kv_len <= 256, D = 64, int4 rows:
 one workgroup per head, whole key range in LDS) against the fp64 oracle:
-ragged key counts around every padding boundary (8-token V rows, 16-token
-stride rule, 32-token key blocks), query counts from 1 to 256 (4 to 8
-waves), causal with Sq <= kv_len, GQA and head maps, channel-outlier V under
+ragged key counts around every padding boundary (8-token V rows, complete
+and partial 16-token PV groups, 32-token key blocks), query counts from 1 to
+256 (one or two 32-row blocks per wave), causal with Sq <= kv_len, GQA and head maps, channel-outlier V under
 concentrated attention (hi/lo P~), V scales near the fp16 limit, and
 queries past fp16 range."""
 import numpy as np
