@@ -83,6 +83,7 @@ __device__ __forceinline__ float dpp_f(float old, float src) {
 }
 constexpr int kChunk = 32;     // tokens per wave iteration
 constexpr int kCoherent = 16;  // buffer-op cache policy: device scope (sc1)
+constexpr int kRangeSplits = 8;   // cache splits from which a split reads one range of chunks
 constexpr int kMaxSplitPages = 512;         // page ids of one split cached in LDS (paged cache)
 constexpr int kRaggedSplitChunks = 128;     // ragged batches: at most 128 chunks per split
 constexpr int kMaxTail = 64;                // rows of the INT8 decode buffer one call attends
@@ -274,7 +275,7 @@ struct ChunkRegs {
 // softmax layout only.
 // APP: the append-mode instantiation (a decode step that appends its new
 // K/V rows first); the plain decode's kernel carries none of that code.
-template <int D, int NB, bool PAGED, int BITS, int NGA, int PKR, bool APP>
+template <int D, int NB, bool PAGED, int BITS, int NGA, int PKR, bool APP, bool RNG>
 __global__ __launch_bounds__(64 * waves_for(NB))
 __attribute__((amdgpu_waves_per_eu(NB == 1 ? ((BITS == 3 || NGA > 0) ? 3 : 4) : 1, 8)))
 void decode_kernel(const DecodeArgs a) {
@@ -376,24 +377,29 @@ void decode_kernel(const DecodeArgs a) {
   // The chunks of cache split `split` (of ns_c; with an INT8 buffer the last
   // split attends the buffered rows instead): c_first, c_first + c_step, ...,
   // c_count of them, among the sequence's gc_end 32-token chunks.
-  //  * contiguous cache: interleaved, split s takes chunks s, s + ns_c, ...
-  //    With lengths per sequence, a sequence uses only as many splits as its
-  //    length needs at the plan's chunks per split (the longest uses them
-  //    all), so a short sequence keeps few workgroups busy.
-  //  * paged cache: a range of cps consecutive chunks, so that each page is
-  //    read by one workgroup (interleaved, both workgroups of a page would
-  //    look up its address translation: measured 9% slower on a ragged batch)
+  //  * contiguous cache, up to 7 splits (RNG false): interleaved, split s takes chunks s,
+  //    s + ns_c, ...  With lengths per sequence, a sequence uses only as many
+  //    splits as its length needs at the plan's chunks per split (the longest
+  //    uses them all), so a short sequence keeps few workgroups busy.
+  //  * contiguous int4 cache with 8 or more splits (RNG), and paged cache: a range of cps
+  //    consecutive chunks.  Interleaved over many splits, each workgroup would
+  //    read 2 KB pieces far apart (every 32nd chunk on the 128K-token step,
+  //    which streams 1.2 us faster from ranges; with 2 splits interleaving is
+  //    as fast or faster); paged, each page is read by one workgroup
+  //    (interleaved, both workgroups of a page would look up its address
+  //    translation: measured 9% slower on a ragged batch)
   const int t_end = L_b;
   const int gc_end = (t_end + kChunk - 1) / kChunk;   // chunks of the sequence
   int ns_c = max(a.n_split - (a.tail_rows > 0 ? 1 : 0), 1);
   const int cps = ((a.kv_len + kChunk - 1) / kChunk + ns_c - 1) / ns_c;   // the plan's chunks per split
   if (!PAGED && a.kv_lens != nullptr) ns_c = max(min(ns_c, (gc_end + cps - 1) / cps), 1);
-  const int c_first = PAGED ? split * cps : split;
-  const int c_step = PAGED ? 1 : ns_c;
-  const int c_count = PAGED ? min(max(gc_end - c_first, 0), cps)
-                            : (split < ns_c && gc_end > split ? (gc_end - split + ns_c - 1) / ns_c : 0);
+  constexpr bool ranges = PAGED || RNG;
+  const int c_first = ranges ? split * cps : split;
+  const int c_step = ranges ? 1 : ns_c;
+  const int c_count = ranges ? min(max(gc_end - c_first, 0), cps)
+                             : (split < ns_c && gc_end > split ? (gc_end - split + ns_c - 1) / ns_c : 0);
   // splits with a chunk of this sequence: a prefix 0 .. n_used - 1
-  const int n_used = PAGED ? min((gc_end + cps - 1) / cps, ns_c) : min(ns_c, gc_end);
+  const int n_used = ranges ? min((gc_end + cps - 1) / cps, ns_c) : min(ns_c, gc_end);
   const int t_begin = c_first * kChunk;   // first row of the split's first chunk
   const int cstride = c_step * kChunk;     // rows between its chunks
   const bool nothing = c_count == 0;
@@ -1676,37 +1682,37 @@ void decode_kernel(const DecodeArgs a) {
   merge_splits();
 }
 
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0, int PKR = 0, bool APP = false>
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, int PKR = 0, bool APP = false, bool RNG = false>
 hipError_t launch_kernel2(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   // the merge buffer can pass 64 KiB (eight waves, 16 rows, D = 128): allow
   // this kernel the larger dynamic LDS once
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PKR, APP>),
+      reinterpret_cast<const void*>(&decode_kernel<D, NB, PAGED, BITS, NGA, PKR, APP, RNG>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_merge_lds_bytes<D, NB>()));
   if (attr != hipSuccess) return attr;
-  decode_kernel<D, NB, PAGED, BITS, NGA, PKR, APP><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
+  decode_kernel<D, NB, PAGED, BITS, NGA, PKR, APP, RNG><<<grid, dim3(64 * waves_for(NB)), lds, stream>>>(args);
   return hipGetLastError();
 }
 
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0, int PKR = 0>
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, int PKR = 0, bool RNG = false>
 hipError_t launch_kernel1(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   if constexpr (BITS == 4 && NGA == 0) {
-    if (args.k_new != nullptr) return launch_kernel2<D, NB, PAGED, BITS, NGA, PKR, true>(args, grid, lds, stream);
+    if (args.k_new != nullptr) return launch_kernel2<D, NB, PAGED, BITS, NGA, PKR, true, RNG>(args, grid, lds, stream);
   } else {
     if (args.k_new != nullptr) return hipErrorInvalidValue;   // the API allows append on 4-bit rows only
   }
-  return launch_kernel2<D, NB, PAGED, BITS, NGA, PKR, false>(args, grid, lds, stream);
+  return launch_kernel2<D, NB, PAGED, BITS, NGA, PKR, false, RNG>(args, grid, lds, stream);
 }
 
 // symmetric rows with at most 4 or at most 8 query rows per group: the
 // packed-softmax kernels
-template <int D, int NB, bool PAGED, int BITS, int NGA = 0>
+template <int D, int NB, bool PAGED, int BITS, int NGA = 0, bool RNG = false>
 hipError_t launch_kernel(const DecodeArgs& args, dim3 grid, size_t lds, hipStream_t stream) {
   if constexpr (NB == 1 && NGA == 0) {
-    if (args.G * args.Sq <= 4) return launch_kernel1<D, NB, PAGED, BITS, NGA, 4>(args, grid, lds, stream);
-    return launch_kernel1<D, NB, PAGED, BITS, NGA, 8>(args, grid, lds, stream);
+    if (args.G * args.Sq <= 4) return launch_kernel1<D, NB, PAGED, BITS, NGA, 4, RNG>(args, grid, lds, stream);
+    return launch_kernel1<D, NB, PAGED, BITS, NGA, 8, RNG>(args, grid, lds, stream);
   } else {
-    return launch_kernel1<D, NB, PAGED, BITS, NGA, 0>(args, grid, lds, stream);
+    return launch_kernel1<D, NB, PAGED, BITS, NGA, 0, RNG>(args, grid, lds, stream);
   }
 }
 
@@ -1725,6 +1731,8 @@ hipError_t launch_nb(const DecodeArgs& args, int B, int Hkv, int n_split, int bi
   if (bits == 2) return launch_kernel<D, NB, false, 2>(args, grid, lds, stream);
   if (bits == 3) return launch_kernel<D, NB, false, 3>(args, grid, lds, stream);
   if (args.block_table != nullptr) return launch_kernel<D, NB, true, 4>(args, grid, lds, stream);
+  if (n_split - (args.tail_rows > 0 ? 1 : 0) >= kRangeSplits)
+    return launch_kernel<D, NB, false, 4, 0, true>(args, grid, lds, stream);
   return launch_kernel<D, NB, false, 4>(args, grid, lds, stream);
 }
 

@@ -94,6 +94,8 @@ BUF_CASES = [
     (1, 4, 4, 1, 0, 8, 5, 3, 64, 0),             # no int4 rows: the buffer split alone
     (1, 4, 1, 16, 200, 256, 40, 24, 128, 0),     # 64 query rows per group, a full buffer
     (3, 12, 4, 1, 2049, 2100, 31, 2, 128, 5),
+    (1, 8, 2, 1, 3000, 3100, 17, 1, 128, 8),     # 7 cache splits (interleaved) + the buffer split
+    (1, 8, 2, 1, 3000, 3100, 17, 1, 128, 9),     # 8 cache splits (ranges) + the buffer split
 ]
 
 

@@ -37,7 +37,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-@pytest.mark.parametrize("ns", [0, 1, 3])
+@pytest.mark.parametrize("ns", [0, 1, 3, 8])
 def test_decode_matches_oracle(case, ns):
     B, Hq, Hkv, Sq, L, C, D = case
     q, kc, ks, vc, vs = random_case(sum(case), B, Hq, Hkv, Sq, L, D, C)
@@ -179,6 +179,9 @@ APPEND_CASES = [
     (2, 6, 3, 1, 1499, 1, 1600, 128, 0),    # 2 rows per group (packed softmax), D 128
     (2, 3, 1, 1, 700, 2, 720, 64, 3),       # 3 rows per group (packed softmax), D 64
     (1, 2, 2, 2, 257, 3, 300, 64, 0),       # 2 rows per group from 2 query positions
+    (1, 8, 2, 1, 2000, 1, 2100, 128, 8),    # 8 splits: each reads one range of chunks
+    (2, 16, 2, 2, 777, 2, 800, 64, 12),     # ranges of 3 chunks, the last one ragged
+    (1, 64, 8, 1, 8191, 1, 8192, 128, 32),  # 8 rows per group, 32 splits of 8 chunks
 ]
 
 
