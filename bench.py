@@ -485,7 +485,7 @@ def bench_prefill(torch, qkv, w, iters, bits=4, group=0):
 
 def bench_hbm_context(torch, iters=10):
     """Achievable-HBM context (not the headline's peak, which stays nominal):
-    the library's plain streaming-read kernel over 1 GiB (qkvb_stream_read,
+    the library's streaming-read kernel over 1 GiB (qkvb_stream_read, non-temporal loads,
     16-byte loads, four in flight per thread; best of a few grid sizes) and
     torch's 512 MiB device-to-device copy, back to back with events around
     the batch."""
