@@ -33,6 +33,7 @@ CASES = [
     (1, 8, 2, 5, 129, 129, 64),      # 20 rows per group -> two 16-row blocks
     (1, 4, 1, 16, 300, 300, 128),    # 64 rows per group -> four blocks
     (3, 12, 4, 3, 2049, 2100, 128),
+    (1, 2, 1, 1, 40000, 40000, 64),  # with 8 splits, ranges of 5024 tokens: scales not staged
 ]
 
 
