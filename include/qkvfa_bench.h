@@ -17,7 +17,8 @@ extern "C" {
 #endif
 
 /*
- * Read `bytes` bytes of device memory at `src` once, in 16-byte loads, with
+ * Read `bytes` bytes of device memory at `src` once, in 16-byte non-temporal
+ * loads (each word is read once: the policy that streams fastest), with
  * `grid` workgroups of 256 threads striding over the buffer in blocks of
  * 16 KiB (each thread keeps four loads in flight), and write one 32-bit XOR
  * of everything each workgroup read to out[blockIdx] (so the loads cannot be
