@@ -1,7 +1,7 @@
 // Streaming-read kernel of the achievable-HBM measurement (libqkvfa_bench.so).
 // Each workgroup reads 16 KiB of consecutive 16-byte words per iteration
 // (four non-temporal loads in flight per thread: each word is read once, and
-// the non-temporal policy streams a 1 GiB read at ~7.0 TB/s on MI355X against
+// the non-temporal policy streams a 1 GiB read at 6.8-7.1 TB/s on MI355X against
 // ~6.0-6.3 TB/s for the default policy) and folds them into a running XOR; it
 // writes the XOR of its threads.
 #include <hip/hip_runtime.h>
